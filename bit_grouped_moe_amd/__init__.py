@@ -1,0 +1,311 @@
+"""Python binding of libgq (grouped MoE matmul on 4-bit packed experts, MI355X).
+
+The functions below carry the names of the C entry points declared in
+``include/gq.h`` and only marshal arguments: they check tensor shapes,
+dtypes, devices and contiguity, allocate outputs with torch when the caller
+passes none, and call the library on torch's current stream.  Every step of
+the computation runs in the HIP kernels of ``libgq.so``; there is no CPU or
+PyTorch fallback.  If the library is missing, every call raises.
+
+Build the library with ``python -m bit_grouped_moe_amd.build``.
+"""
+
+import ctypes
+import os
+from collections import namedtuple
+
+import torch
+
+__all__ = [
+    "GQError", "load_library", "library_path", "EXPORTED_SYMBOLS", "TILE_M",
+    "gq_route_max_tiles", "gq_route_sort", "gq_nf4_decode", "gq_mxfp4_decode",
+    "gq_nf4_grouped_gemv", "gq_mxfp4_grouped_gemv", "gq_nf4_grouped_gemm",
+    "gq_mxfp4_grouped_gemm", "gq_nf4_grouped_dgrad", "Route",
+]
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+TILE_M = 256                       # the tile height the grouped GEMM kernels use
+
+EXPORTED_SYMBOLS = (
+    "gq_status_string", "gq_route_max_tiles", "gq_route_sort", "gq_nf4_decode",
+    "gq_mxfp4_decode", "gq_nf4_grouped_gemv", "gq_mxfp4_grouped_gemv", "gq_nf4_grouped_gemm",
+    "gq_mxfp4_grouped_gemm", "gq_nf4_grouped_dgrad",
+)
+
+_i32, _i64, _p = ctypes.c_int32, ctypes.c_int64, ctypes.c_void_p
+_SIGNATURES = {
+    "gq_status_string": (ctypes.c_char_p, [ctypes.c_int]),
+    "gq_route_max_tiles": (_i32, [_i32, _i32, _i32, _i32]),
+    "gq_route_sort": (ctypes.c_int, [_p, _i32, _i32, _i32, _i32, _p, _p, _p, _i32, _p, _p]),
+    "gq_nf4_decode": (ctypes.c_int, [_p, _p, _i64, _i32, _p, _p, _p]),
+    "gq_mxfp4_decode": (ctypes.c_int, [_p, _p, _i64, _i32, _p, _p, _p]),
+    "gq_nf4_grouped_gemv": (ctypes.c_int, [_p, _i32, _i32, _i64, _p, _p, _i32, _i32, _p, _i32,
+                                           _p, _p, _p]),
+    "gq_mxfp4_grouped_gemv": (ctypes.c_int, [_p, _i32, _i32, _i64, _p, _p, _i32, _i32, _p, _i32,
+                                             _p, _p, _p]),
+    "gq_nf4_grouped_gemm": (ctypes.c_int, [_p, _i32, _i32, _i64, _p, _p, _i32, _i32, _i32, _p,
+                                           _p, _p, _p, _p, _i32, _i32, _p, _p]),
+    "gq_mxfp4_grouped_gemm": (ctypes.c_int, [_p, _i32, _i32, _i64, _p, _p, _i32, _i32, _i32, _p,
+                                             _p, _p, _p, _p, _i32, _i32, _p, _p]),
+    "gq_nf4_grouped_dgrad": (ctypes.c_int, [_p, _i32, _i32, _i64, _p, _p, _i32, _i32, _p, _p,
+                                            _p, _p, _i32, _i32, _p, _p]),
+}
+
+_lib = None
+
+
+class GQError(RuntimeError):
+    """A libgq call returned a nonzero status, or the library is missing."""
+
+    def __init__(self, msg, status=None):
+        super().__init__(msg)
+        self.status = status
+
+
+def library_path():
+    return os.environ.get("GQ_LIBRARY", os.path.join(_HERE, "libgq.so"))
+
+
+def load_library():
+    """Load libgq.so (once) and declare its C signatures."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    path = library_path()
+    if not os.path.exists(path):
+        raise GQError(f"libgq.so not found at {path}; build it with "
+                      "`python -m bit_grouped_moe_amd.build` (no fallback exists)")
+    lib = ctypes.CDLL(path)
+    for name, (res, args) in _SIGNATURES.items():
+        fn = getattr(lib, name)
+        fn.restype = res
+        fn.argtypes = args
+    _lib = lib
+    return lib
+
+
+def _check(status, what):
+    if status != 0:
+        lib = load_library()
+        raise GQError(f"{what}: {lib.gq_status_string(status).decode()} (status {status})", status)
+
+
+def _stream(t):
+    return torch.cuda.current_stream(t.device).cuda_stream
+
+
+def _dev(t, name, dtype, ndim=None):
+    if not isinstance(t, torch.Tensor):
+        raise TypeError(f"{name} must be a torch.Tensor")
+    if t.device.type != "cuda":
+        raise ValueError(f"{name} must be a device tensor (got {t.device})")
+    if t.dtype != dtype:
+        raise ValueError(f"{name} must be {dtype} (got {t.dtype})")
+    if ndim is not None and t.dim() != ndim:
+        raise ValueError(f"{name} must have {ndim} dims (got shape {tuple(t.shape)})")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+    return t
+
+
+def _ptr(t):
+    return None if t is None else ctypes.c_void_p(t.data_ptr())
+
+
+Route = namedtuple("Route", "expert_offsets sorted_pairs tiles num_tiles max_tiles tile_m "
+                            "rows topk num_experts")
+
+
+def gq_route_max_tiles(rows, topk, num_experts, tile_m=TILE_M):
+    return int(load_library().gq_route_max_tiles(rows, topk, num_experts, tile_m))
+
+
+def gq_route_sort(topk_ids, num_experts, tile_m=TILE_M, expert_offsets=None, sorted_pairs=None,
+                  tiles=None, num_tiles=None):
+    """Group the (token, slot) pairs of ``topk_ids`` int32 [rows, topk] by expert."""
+    lib = load_library()
+    _dev(topk_ids, "topk_ids", torch.int32, 2)
+    rows, topk = topk_ids.shape
+    dev = topk_ids.device
+    max_tiles = gq_route_max_tiles(rows, topk, num_experts, tile_m)
+    if max_tiles < 0:
+        raise GQError("gq_route_max_tiles: invalid arguments", 1)
+    if expert_offsets is None:
+        expert_offsets = torch.empty(num_experts + 1, dtype=torch.int32, device=dev)
+    if sorted_pairs is None:
+        sorted_pairs = torch.empty(rows * topk, dtype=torch.int32, device=dev)
+    if tiles is None:
+        tiles = torch.empty((max_tiles, 2), dtype=torch.int32, device=dev)
+    if num_tiles is None:
+        num_tiles = torch.empty(1, dtype=torch.int32, device=dev)
+    st = lib.gq_route_sort(_ptr(topk_ids), rows, topk, num_experts, tile_m, _ptr(expert_offsets),
+                           _ptr(sorted_pairs), _ptr(tiles), tiles.shape[0], _ptr(num_tiles),
+                           _stream(topk_ids))
+    _check(st, "gq_route_sort")
+    return Route(expert_offsets, sorted_pairs, tiles, num_tiles, tiles.shape[0], tile_m, rows,
+                 topk, num_experts)
+
+
+def gq_nf4_decode(codes, absmax, out_f32=True, out_bf16=True):
+    """Decode NF4 codes uint8 [..., K/2] with absmax float32 [..., K/64]."""
+    lib = load_library()
+    _dev(codes, "codes", torch.uint8)
+    _dev(absmax, "absmax", torch.float32)
+    K = codes.shape[-1] * 2
+    n_rows = codes.numel() // (K // 2) if K else 0
+    shape = tuple(codes.shape[:-1]) + (K,)
+    f = torch.empty(shape, dtype=torch.float32, device=codes.device) if out_f32 is True else out_f32
+    b = torch.empty(shape, dtype=torch.bfloat16, device=codes.device) if out_bf16 is True else out_bf16
+    f = None if f is False else f
+    b = None if b is False else b
+    st = lib.gq_nf4_decode(_ptr(codes), _ptr(absmax), n_rows, K, _ptr(f), _ptr(b), _stream(codes))
+    _check(st, "gq_nf4_decode")
+    return f, b
+
+
+def gq_mxfp4_decode(blocks, scales, out_f32=True, out_bf16=True):
+    """Decode MXFP4 blocks uint8 [..., K/32, 16] with e8m0 scales uint8 [..., K/32]."""
+    lib = load_library()
+    _dev(blocks, "blocks", torch.uint8)
+    _dev(scales, "scales", torch.uint8)
+    K = blocks.shape[-2] * 32
+    n_rows = blocks.numel() // (K // 2) if K else 0
+    shape = tuple(blocks.shape[:-2]) + (K,)
+    f = torch.empty(shape, dtype=torch.float32, device=blocks.device) if out_f32 is True else out_f32
+    b = torch.empty(shape, dtype=torch.bfloat16, device=blocks.device) if out_bf16 is True else out_bf16
+    f = None if f is False else f
+    b = None if b is False else b
+    st = lib.gq_mxfp4_decode(_ptr(blocks), _ptr(scales), n_rows, K, _ptr(f), _ptr(b),
+                             _stream(blocks))
+    _check(st, "gq_mxfp4_decode")
+    return f, b
+
+
+def _x_args(x, name="x"):
+    if not isinstance(x, torch.Tensor) or x.device.type != "cuda" or x.dtype != torch.bfloat16:
+        raise ValueError(f"{name} must be a bf16 device tensor")
+    if x.dim() != 2 or x.stride(1) != 1:
+        raise ValueError(f"{name} must be 2-D with unit column stride")
+    return x.shape[0], x.shape[1], x.stride(0)
+
+
+def _nf4_bank(codes, absmax):
+    _dev(codes, "codes", torch.uint8, 3)
+    _dev(absmax, "absmax", torch.float32, 3)
+    E, N, half = codes.shape
+    K = half * 2
+    if tuple(absmax.shape) != (E, N, K // 64):
+        raise ValueError("absmax must be [E, N, K/64]")
+    return E, N, K
+
+
+def _mx_bank(blocks, scales):
+    _dev(blocks, "blocks", torch.uint8, 4)
+    _dev(scales, "scales", torch.uint8, 3)
+    E, N, nb, sixteen = blocks.shape
+    if sixteen != 16 or tuple(scales.shape) != (E, N, nb):
+        raise ValueError("blocks must be [E, N, K/32, 16] and scales [E, N, K/32]")
+    return E, N, nb * 32
+
+
+def _out(out, P, N, dev):
+    if out is None:
+        return torch.empty((P, N), dtype=torch.bfloat16, device=dev)
+    _dev(out, "out", torch.bfloat16)
+    if out.numel() != P * N:
+        raise ValueError("out must hold rows*topk x N elements")
+    return out
+
+
+def _scale(pair_scale, P):
+    if pair_scale is None:
+        return None
+    _dev(pair_scale, "pair_scale", torch.float32)
+    if pair_scale.numel() != P:
+        raise ValueError("pair_scale must hold one float per pair")
+    return pair_scale
+
+
+def gq_nf4_grouped_gemv(x, codes, absmax, topk_ids, pair_scale=None, out=None):
+    """Decode-time grouped GEMV (<= 256 pairs) on NF4 experts; returns bf16 [rows*topk, N]."""
+    lib = load_library()
+    rows, K, xs = _x_args(x)
+    E, N, Kw = _nf4_bank(codes, absmax)
+    if Kw != K:
+        raise ValueError("x and codes disagree on K")
+    _dev(topk_ids, "topk_ids", torch.int32, 2)
+    P = topk_ids.numel()
+    out = _out(out, P, N, x.device)
+    st = lib.gq_nf4_grouped_gemv(_ptr(x), rows, K, xs, _ptr(codes), _ptr(absmax), E, N,
+                                 _ptr(topk_ids), topk_ids.shape[1], _ptr(_scale(pair_scale, P)),
+                                 _ptr(out), _stream(x))
+    _check(st, "gq_nf4_grouped_gemv")
+    return out
+
+
+def gq_mxfp4_grouped_gemv(x, blocks, scales, topk_ids, pair_scale=None, out=None):
+    """Decode-time grouped GEMV (<= 256 pairs) on MXFP4 experts; returns bf16 [rows*topk, N]."""
+    lib = load_library()
+    rows, K, xs = _x_args(x)
+    E, N, Kw = _mx_bank(blocks, scales)
+    if Kw != K:
+        raise ValueError("x and blocks disagree on K")
+    _dev(topk_ids, "topk_ids", torch.int32, 2)
+    P = topk_ids.numel()
+    out = _out(out, P, N, x.device)
+    st = lib.gq_mxfp4_grouped_gemv(_ptr(x), rows, K, xs, _ptr(blocks), _ptr(scales), E, N,
+                                   _ptr(topk_ids), topk_ids.shape[1], _ptr(_scale(pair_scale, P)),
+                                   _ptr(out), _stream(x))
+    _check(st, "gq_mxfp4_grouped_gemv")
+    return out
+
+
+def _route_ptrs(route):
+    return (_ptr(route.expert_offsets), _ptr(route.sorted_pairs), _ptr(route.tiles),
+            _ptr(route.num_tiles), route.max_tiles, route.tile_m)
+
+
+def gq_nf4_grouped_gemm(x, codes, absmax, route, pair_scale=None, out=None):
+    """Prefill grouped GEMM on NF4 experts using a ``gq_route_sort`` result."""
+    lib = load_library()
+    rows, K, xs = _x_args(x)
+    E, N, Kw = _nf4_bank(codes, absmax)
+    if Kw != K or route.rows != rows or route.num_experts != E:
+        raise ValueError("x, codes and route disagree")
+    P = rows * route.topk
+    out = _out(out, P, N, x.device)
+    st = lib.gq_nf4_grouped_gemm(_ptr(x), rows, K, xs, _ptr(codes), _ptr(absmax), E, N,
+                                 route.topk, _ptr(_scale(pair_scale, P)), *_route_ptrs(route),
+                                 _ptr(out), _stream(x))
+    _check(st, "gq_nf4_grouped_gemm")
+    return out
+
+
+def gq_mxfp4_grouped_gemm(x, blocks, scales, route, pair_scale=None, out=None):
+    """Prefill grouped GEMM on MXFP4 experts using a ``gq_route_sort`` result."""
+    lib = load_library()
+    rows, K, xs = _x_args(x)
+    E, N, Kw = _mx_bank(blocks, scales)
+    if Kw != K or route.rows != rows or route.num_experts != E:
+        raise ValueError("x, blocks and route disagree")
+    P = rows * route.topk
+    out = _out(out, P, N, x.device)
+    st = lib.gq_mxfp4_grouped_gemm(_ptr(x), rows, K, xs, _ptr(blocks), _ptr(scales), E, N,
+                                   route.topk, _ptr(_scale(pair_scale, P)), *_route_ptrs(route),
+                                   _ptr(out), _stream(x))
+    _check(st, "gq_mxfp4_grouped_gemm")
+    return out
+
+
+def gq_nf4_grouped_dgrad(dy, codes, absmax, route, out=None):
+    """dX = dY . W per pair through NF4 experts; ``route`` from gq_route_sort(pair ids [P, 1])."""
+    lib = load_library()
+    P, N, ds = _x_args(dy, "dy")
+    E, Nw, K = _nf4_bank(codes, absmax)
+    if Nw != N or route.rows * route.topk != P or route.topk != 1 or route.num_experts != E:
+        raise ValueError("dy, codes and route disagree (route must be built with topk = 1)")
+    out = _out(out, P, K, dy.device)
+    st = lib.gq_nf4_grouped_dgrad(_ptr(dy), P, N, ds, _ptr(codes), _ptr(absmax), E, K,
+                                  *_route_ptrs(route), _ptr(out), _stream(dy))
+    _check(st, "gq_nf4_grouped_dgrad")
+    return out

@@ -1,0 +1,511 @@
+// Prefill grouped GEMM on 4-bit packed experts (NF4, MXFP4) and the NF4
+// input gradient, on gfx950 bf16 matrix cores.
+//
+// Pages: "grouped-nf4-gemm 0.43.0" -- page header (one GPU launch for the
+// active experts, no full-size bf16 weight copies) and "Which entry point?"
+// (grouped NF4 forward and backward, native MXFP4 expert math);
+// "Receipts-driven engineering" -- opening summary (the codebook is decoded
+// in registers inside the GEMM mainloop; the NF4 path is differentiable).
+// The tiling below is this library's own design for CDNA4.
+//
+// One launch covers every tile of every expert (tile list from
+// gq_route_sort).  A workgroup computes a 256 x 128 output tile:
+//  * rows = 256 routed pairs of one expert (gathered activation rows),
+//  * cols = 128 output features,
+//  * K loop in steps of 64: the B tile (128 x 64 weights) is decoded ONCE
+//    per workgroup from packed codes into bf16 in LDS (double-buffered, one
+//    barrier per step) and shared by the 4 waves; each wave streams its own
+//    activation rows straight from global memory into MFMA registers (no LDS
+//    round trip for A).
+//  * wave w owns the 32-row sub-tiles w and w+4 (interleaved so that short
+//    expert segments still spread over all four SIMDs) across all 128
+//    columns: 2 x 4 v_mfma_f32_32x32x16_bf16 per 16-wide K slice.  Sub-tiles
+//    beyond the expert's row count skip their MFMAs.
+//  * the K order inside a 64-step is permuted identically for A and B
+//    (lane half h takes k in [32h, 32h+32)), which makes every operand load
+//    a contiguous 16-byte piece.
+//  * block index -> tile is XCD-aware: the hardware deals blocks round-robin
+//    to the 8 XCDs; consecutive blocks of one XCD get all column tiles of a
+//    row tile, so the gathered activation rows are reused from that XCD's L2.
+//  * tiles past the last expert tile zero the rows of dropped pairs, in the
+//    same launch.  Every output element is written once: no atomics.
+#include <type_traits>
+
+#include "gq_device.hpp"
+#include "gq_host.hpp"
+#include "../../include/gq.h"
+
+namespace gq {
+
+constexpr int kTM = 256;          // tile rows (routed pairs)
+constexpr int kTN = 128;          // tile columns (output features)
+constexpr int kTK = 64;           // contraction per step
+constexpr int kGemmThreads = 256;
+constexpr int kBStride = 72;      // bf16 per LDS row of B (64 + 8 pad: conflict-free 16-B reads)
+constexpr int kCStride = 80;      // bytes per LDS row of raw codes (dgrad staging)
+
+enum BMode { kFwdNF4 = 0, kFwdMX = 1, kDgradNF4 = 2 };
+
+struct GemmArgs {
+  const uint16_t* x;           // activations (forward) or output gradient (dgrad)
+  int64_t x_stride;            // elements
+  const uint8_t* codes;        // [E, Nw, Kw/2]
+  const void* scl;             // NF4 absmax float [E, Nw, Kw/64] / MXFP4 e8m0 [E, Nw, Kw/32]
+  int Nw, Kw;                  // expert weight shape [Nw, Kw]
+  int Kc;                      // contraction length (Kw forward, Nw dgrad)
+  int Nout;                    // output columns (Nw forward, Kw dgrad)
+  int E, topk, P;
+  const float* pair_scale;
+  const int32_t* offsets;
+  const int32_t* sorted_pairs;
+  const int32_t* tiles;
+  const int32_t* num_tiles;
+  int n_col_tiles;             // ceil(Nout / kTN)
+  int n_logical;               // max_tiles * n_col_tiles
+  uint16_t* out;               // [P, Nout]
+};
+
+__device__ __forceinline__ bf16x8 as_bf16x8(u32x4 v) { return __builtin_bit_cast(bf16x8, v); }
+
+// ---- B producers: fill Bs[col][k] (bf16, row stride kBStride) for step ks ----
+
+// Forward: B[k][col] = W[n0 + col][ks*64 + k].  Thread t decodes 32 weights:
+// col = t % 128, half h = t / 128 (k in [32h, 32h+32)).
+struct FwdLoad {
+  u32x4 c;
+  float a;      // NF4 absmax
+  uint32_t s;   // MXFP4 scale byte
+  bool ok;
+};
+
+// Loads are unconditional, from addresses clamped into the bank; elements
+// outside the matrix are zeroed when decoded.  (A conditional load would
+// first zero its destination registers, and the hardware wait-count logic
+// then stalls on every older load in flight before that write.)
+template <int kMode>
+__device__ __forceinline__ FwdLoad fwd_load(const GemmArgs& g, int e, int n0, int ks, int tid) {
+  FwdLoad L;
+  const int col = tid & (kTN - 1), h = tid >> 7;
+  const int n = n0 + col;
+  const int k0 = ks * kTK + h * 32;
+  L.ok = n < g.Nw && k0 < g.Kw;
+  const size_t row = (size_t)e * g.Nw + min(n, g.Nw - 1);
+  const size_t kk = (size_t)min(k0, g.Kw - 32);
+  L.c = *reinterpret_cast<const u32x4*>(g.codes + row * (size_t)(g.Kw / 2) + kk / 2);
+  if constexpr (kMode == kFwdMX) {
+    L.s = (uint32_t)static_cast<const uint8_t*>(g.scl)[row * (size_t)(g.Kw / 32) + kk / 32];
+    L.a = 0.f;
+  } else {
+    L.a = static_cast<const float*>(g.scl)[row * (size_t)(g.Kw / 64) + kk / 64];
+    L.s = 0u;
+  }
+  return L;
+}
+
+template <int kMode>
+__device__ __forceinline__ void fwd_decode_store(const FwdLoad& L, const float* lut, uint16_t* Bs,
+                                                 int tid) {
+  const int col = tid & (kTN - 1), h = tid >> 7;
+  uint32_t p[16];
+  if constexpr (kMode == kFwdMX) {
+    const float sc = e8m0_to_f32(L.s);
+#pragma unroll
+    for (int w = 0; w < 4; ++w)
+#pragma unroll
+      for (int b = 0; b < 4; ++b) p[4 * w + b] = e2m1_pair_bf16_scaled(L.c[w], b, sc);
+  } else {
+#pragma unroll
+    for (int w = 0; w < 4; ++w) nf4_decode8_bf16(lut, L.c[w], L.a, &p[4 * w]);
+  }
+  if (!L.ok) {
+#pragma unroll
+    for (int i = 0; i < 16; ++i) p[i] = 0u;
+  }
+  u32x4* dst = reinterpret_cast<u32x4*>(Bs + col * kBStride + h * 32);
+#pragma unroll
+  for (int q = 0; q < 4; ++q) dst[q] = u32x4{p[4 * q], p[4 * q + 1], p[4 * q + 2], p[4 * q + 3]};
+}
+
+// Dgrad: B[k][col] = W[ks*64 + k][k0 + col], i.e. a 64 x 128 block of W
+// consumed transposed.  Raw codes (64 rows x 64 bytes) are staged in LDS,
+// then thread t decodes rows 8*(t/32) .. +8 of the column quad 4*(t%32) ..
+// +4 and writes four 16-byte runs of 8 consecutive contraction values.
+struct DgLoad {
+  u32x4 c;
+  float a;      // absmax of (row t/2, block t%2) for t < 128
+  bool ok, aok;
+};
+
+__device__ __forceinline__ DgLoad dg_load(const GemmArgs& g, int e, int k0, int ks, int tid) {
+  DgLoad L;
+  const int r = tid >> 2, q = tid & 3;                    // row in step, 16-byte quarter
+  const int n = ks * kTK + r;                             // W row (< Nw since Nw % 64 == 0)
+  const int kb = k0 + q * 32;                             // first weight of this quarter
+  L.ok = kb < g.Kw;
+  const size_t row = (size_t)e * g.Nw + n;
+  L.c = *reinterpret_cast<const u32x4*>(g.codes + row * (size_t)(g.Kw / 2) +
+                                        min(kb, g.Kw - 32) / 2);
+  // absmax of (row t/2, block t%2) for t < 128 (other threads: a harmless reload)
+  const int t = tid & (2 * kTK - 1);
+  const int ar = t >> 1, ablk = (k0 >> 6) + (t & 1);
+  L.aok = ablk < g.Kw / 64;
+  const size_t arow = (size_t)e * g.Nw + ks * kTK + ar;
+  L.a = static_cast<const float*>(g.scl)[arow * (size_t)(g.Kw / 64) + min(ablk, g.Kw / 64 - 1)];
+  return L;
+}
+
+__device__ __forceinline__ void dg_stage(const DgLoad& L, uint8_t* Cs, float* As, int tid) {
+  // Cs: 64 rows x kCStride bytes of raw codes; As: [64 rows][2 blocks] absmax
+  const int r = tid >> 2, q = tid & 3;
+  *reinterpret_cast<u32x4*>(Cs + r * kCStride + q * 16) = L.ok ? L.c : u32x4{0u, 0u, 0u, 0u};
+  if (tid < 2 * kTK) As[tid] = L.aok ? L.a : 0.f;         // As[row*2 + block]
+}
+
+__device__ __forceinline__ void dg_decode_store(const uint8_t* Cs, const float* As, const float* lut,
+                                                uint16_t* Bs, int tid) {
+  const int j4 = tid & 31, r8 = tid >> 5;                 // column quad, row octet
+  const int blk = (j4 * 4) >> 6;                          // local absmax block (0 or 1)
+  float w[4][8];                                          // [column][row]
+#pragma unroll
+  for (int i = 0; i < 8; ++i) {
+    const int r = r8 * 8 + i;
+    const uint32_t two = *reinterpret_cast<const uint16_t*>(Cs + r * kCStride + j4 * 2);
+    const float a = As[r * 2 + blk];
+    // bytes j4*2, j4*2+1 hold columns 4*j4 .. 4*j4+3 (high nibble first)
+    w[0][i] = nf4_q_hi(lut, two, 0) * a;
+    w[1][i] = nf4_q_lo(lut, two, 0) * a;
+    w[2][i] = nf4_q_hi(lut, two, 1) * a;
+    w[3][i] = nf4_q_lo(lut, two, 1) * a;
+  }
+#pragma unroll
+  for (int c = 0; c < 4; ++c) {
+    u32x4 v{pack_bf16x2(w[c][0], w[c][1]), pack_bf16x2(w[c][2], w[c][3]),
+            pack_bf16x2(w[c][4], w[c][5]), pack_bf16x2(w[c][6], w[c][7])};
+    *reinterpret_cast<u32x4*>(Bs + (j4 * 4 + c) * kBStride + r8 * 8) = v;
+  }
+}
+
+// ---- the kernel ----
+// Software pipeline, one barrier per K step.  Iteration ks:
+//   issue the global loads that step ks+1 (activations) and ks+2 (codes)
+//   need; decode step ks+1 into the LDS buffer the MFMAs are not reading;
+//   run the MFMAs of step ks from the other buffer; barrier.
+// The decode (VALU + LDS) and the matrix-core work of different steps are
+// independent inside an iteration, so they overlap.  Dgrad stages raw codes
+// through LDS first (transposed consumption), one step further ahead.
+template <int kMode>
+__device__ __forceinline__ void grouped_gemm_body(const GemmArgs& g) {
+  constexpr bool kDg = kMode == kDgradNF4;
+  __shared__ __attribute__((aligned(16))) uint16_t Bs[2][kTN * kBStride];
+  __shared__ __attribute__((aligned(16))) uint8_t Cs[kDg ? 2 : 1][kDg ? kTK * kCStride : 16];
+  __shared__ float As[kDg ? 2 : 1][kDg ? 2 * kTK : 1];
+  __shared__ int pair_s[kTM];
+  __shared__ int row_s[kTM];
+  __shared__ float lut[16];
+
+  const int tid = threadIdx.x;
+  // XCD-aware block -> logical tile mapping (see file comment).
+  const int C = g.n_col_tiles;
+  const int bid = blockIdx.x;
+  const int q = bid >> 3, xcd = bid & 7;
+  const int logical = (q / C) * (8 * C) + xcd * C + (q % C);
+  if (logical >= g.n_logical) return;
+  const int tile = logical / C;
+  const int n0 = (logical % C) * kTN;
+  const int T = *g.num_tiles;
+
+  if (tile >= T) {
+    // Zero the rows of dropped pairs (ids outside [0, E)), columns [n0, n0+128).
+    const int dstart = g.offsets[g.E] + (tile - T) * kTM;
+    if (dstart >= g.P) return;
+    if (dstart < 0) return;
+    const int dvalid = min(kTM, g.P - dstart);
+    for (int idx = tid; idx < dvalid * (kTN / 8); idx += kGemmThreads) {
+      const int r = idx / (kTN / 8), c8 = idx % (kTN / 8);
+      const int col = n0 + c8 * 8;
+      const int p = g.sorted_pairs[dstart + r];
+      if (col < g.Nout && (unsigned)p < (unsigned)g.P) {
+        *reinterpret_cast<u32x4*>(g.out + (int64_t)p * g.Nout + col) = u32x4{0u, 0u, 0u, 0u};
+      }
+    }
+    return;
+  }
+
+  const int e = g.tiles[2 * tile];
+  const int start = g.tiles[2 * tile + 1];
+  // A tile list that does not come from gq_route_sort must not make the
+  // kernel read outside its buffers: reject entries that cannot be valid.
+  if ((unsigned)e >= (unsigned)g.E || (unsigned)start >= (unsigned)g.P) return;
+  const int valid = min(kTM, min(g.offsets[e + 1], g.P) - start);
+  if (valid <= 0) return;
+  for (int r = tid; r < kTM; r += kGemmThreads) {
+    int p = g.sorted_pairs[start + min(r, valid - 1)];
+    p = ((unsigned)p < (unsigned)g.P) ? p : 0;
+    pair_s[r] = p;
+    row_s[r] = kDg ? p : p / g.topk;
+  }
+  if constexpr (kMode != kFwdMX) nf4_lut_init(lut, tid);
+  lds_barrier();
+
+  const int wave = tid >> 6, lane = tid & 63;
+  const int lr = lane & 31, lh = lane >> 5;
+  const int ms0 = wave, ms1 = wave + 4;                    // owned 32-row sub-tiles
+  const bool act0 = ms0 * 32 < valid, act1 = ms1 * 32 < valid;
+  const uint16_t* a0 = g.x + (int64_t)row_s[ms0 * 32 + lr] * g.x_stride + lh * 32;
+  const uint16_t* a1 = g.x + (int64_t)row_s[ms1 * 32 + lr] * g.x_stride + lh * 32;
+  const int nsteps = (g.Kc + kTK - 1) / kTK;
+  const bool ktail = (g.Kc % kTK) != 0;                   // MXFP4 only: last step half full
+  const int ncols = min(kTN, g.Nout - n0);                 // multiple of 32
+
+  f32x16 acc[2][4];
+#pragma unroll
+  for (int j = 0; j < 2; ++j)
+#pragma unroll
+    for (int c = 0; c < 4; ++c)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) acc[j][c][r] = 0.f;
+
+  // Activation loads are unconditional (rows of inactive sub-tiles point at a
+  // valid row; the half-step past a K tail re-reads the last valid half and
+  // is zeroed just before use), see the note at fwd_load.
+  const int a_koff_max = g.Kc - 32 - lh * 32;             // keeps k within the row
+  auto load_a = [&](int ks, u32x4 (&A)[2][4]) {
+    const int koff = min(ks * kTK, a_koff_max);
+#pragma unroll
+    for (int sl = 0; sl < 4; ++sl) {
+      A[0][sl] = *reinterpret_cast<const u32x4*>(a0 + koff + sl * 8);
+      A[1][sl] = *reinterpret_cast<const u32x4*>(a1 + koff + sl * 8);
+    }
+  };
+  auto zero_tail = [&](int ks, u32x4 (&A)[2][4]) {
+    if (ktail && ks == nsteps - 1 && lh == 1) {
+#pragma unroll
+      for (int sl = 0; sl < 4; ++sl) A[0][sl] = A[1][sl] = u32x4{0u, 0u, 0u, 0u};
+    }
+  };
+
+  // kRows = number of active 32-row sub-tiles of this wave (1 or 2) with all
+  // 128 columns valid: straight-line MFMAs, so the scheduler can interleave
+  // them with the next step's decode.  kRows == 0: generic guarded path.
+  auto mfma_step = [&](auto rows_c, const u32x4 (&A)[2][4], const uint16_t* B) {
+    constexpr int kRows = decltype(rows_c)::value;
+#pragma unroll
+    for (int sl = 0; sl < 4; ++sl) {
+      bf16x8 b[4];
+#pragma unroll
+      for (int c = 0; c < 4; ++c)
+        b[c] = as_bf16x8(
+            *reinterpret_cast<const u32x4*>(B + (c * 32 + lr) * kBStride + lh * 32 + sl * 8));
+#pragma unroll
+      for (int c = 0; c < 4; ++c) {
+        if constexpr (kRows == 0) {
+          if (c * 32 >= ncols) continue;
+          if (act0)
+            acc[0][c] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(A[0][sl]), b[c],
+                                                                acc[0][c], 0, 0, 0);
+          if (act1)
+            acc[1][c] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(A[1][sl]), b[c],
+                                                                acc[1][c], 0, 0, 0);
+        } else {
+          acc[0][c] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(A[0][sl]), b[c],
+                                                              acc[0][c], 0, 0, 0);
+          if constexpr (kRows == 2)
+            acc[1][c] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(A[1][sl]), b[c],
+                                                                acc[1][c], 0, 0, 0);
+        }
+      }
+    }
+  };
+
+  u32x4 A0[2][4], A1[2][4];
+  FwdLoad F0{}, F1{};
+  DgLoad D{};
+
+  // ---- prologue: step 0 decoded into Bs[0] ----
+  load_a(0, A0);
+  if constexpr (kDg) {
+    D = dg_load(g, e, n0, 0, tid);
+    dg_stage(D, Cs[0], As[0], tid);
+    D = dg_load(g, e, n0, min(1, nsteps - 1), tid);
+    lds_barrier();
+    dg_decode_store(Cs[0], As[0], lut, Bs[0], tid);
+    dg_stage(D, Cs[1], As[1], tid);
+    D = dg_load(g, e, n0, min(2, nsteps - 1), tid);
+  } else {
+    F0 = fwd_load<kMode>(g, e, n0, 0, tid);
+    F1 = fwd_load<kMode>(g, e, n0, min(1, nsteps - 1), tid);
+    fwd_decode_store<kMode>(F0, lut, Bs[0], tid);
+  }
+  lds_barrier();
+
+  // ---- main loop (unrolled by two so register sets swap roles, no copies) ----
+  // Prefetches and decodes run unconditionally (step indices clamped to the
+  // last step; the surplus work at the tail writes an LDS buffer nobody reads
+  // again): loads under a branch would make the compiler wait for them early.
+  auto run_loop = [&](auto rows_c) {
+    auto body = [&](int ks, u32x4 (&A_use)[2][4], u32x4 (&A_fill)[2][4], FwdLoad& F_dec,
+                    FwdLoad& F_fill) {
+      const int k1 = min(ks + 1, nsteps - 1), k2 = min(ks + 2, nsteps - 1);
+      load_a(k1, A_fill);
+      if constexpr (kDg) {
+        dg_decode_store(Cs[(ks + 1) & 1], As[(ks + 1) & 1], lut, Bs[(ks + 1) & 1], tid);
+        dg_stage(D, Cs[ks & 1], As[ks & 1], tid);
+        D = dg_load(g, e, n0, min(ks + 3, nsteps - 1), tid);
+      } else {
+        F_fill = fwd_load<kMode>(g, e, n0, k2, tid);
+        fwd_decode_store<kMode>(F_dec, lut, Bs[(ks + 1) & 1], tid);
+      }
+      zero_tail(ks, A_use);
+      mfma_step(rows_c, A_use, Bs[ks & 1]);
+      lds_barrier();
+    };
+    for (int ks = 0; ks < nsteps; ks += 2) {
+      body(ks, A0, A1, F1, F0);
+      if (ks + 1 < nsteps) body(ks + 1, A1, A0, F0, F1);
+    }
+  };
+  if (ncols == kTN && act1) run_loop(std::integral_constant<int, 2>{});
+  else if (ncols == kTN && act0) run_loop(std::integral_constant<int, 1>{});
+  else run_loop(std::integral_constant<int, 0>{});
+
+  // ---- epilogue: scale, round to bf16, scatter rows to their pairs ----
+#pragma unroll
+  for (int j = 0; j < 2; ++j) {
+    const int ms = j ? ms1 : ms0;
+    if (!(j ? act1 : act0)) continue;
+#pragma unroll
+    for (int r = 0; r < 16; ++r) {
+      const int m = ms * 32 + (r >> 2) * 8 + lh * 4 + (r & 3);
+      if (m >= valid) continue;
+      const int p = pair_s[m];
+      const float sc = g.pair_scale ? g.pair_scale[p] : 1.f;
+      uint16_t* orow = g.out + (int64_t)p * g.Nout + n0 + lr;
+#pragma unroll
+      for (int c = 0; c < 4; ++c)
+        if (c * 32 < ncols) orow[c * 32] = f32_to_bf16_bits(acc[j][c][r] * sc);
+    }
+  }
+}
+
+// Forward kernels fit 2 waves per SIMD (2 workgroups per CU) without spills;
+// the dgrad kernel needs a few more registers and runs 1 wave per SIMD.
+template <int kMode>
+__global__ __launch_bounds__(kGemmThreads, 2) void grouped_gemm_fwd_kernel(GemmArgs g) {
+  grouped_gemm_body<kMode>(g);
+}
+__global__ __launch_bounds__(kGemmThreads, 1) void grouped_dgrad_kernel(GemmArgs g) {
+  grouped_gemm_body<kDgradNF4>(g);
+}
+
+template <int kMode>
+static int launch_gemm(GemmArgs g, int32_t max_tiles, int32_t tile_m, hipStream_t stream) {
+  if (tile_m != kTM) return kNotSupported;
+  const int64_t need = (int64_t)(g.P + kTM - 1) / kTM + g.E + 1;
+  if (max_tiles < need) return kInvalid;
+  g.n_col_tiles = (g.Nout + kTN - 1) / kTN;
+  const int64_t n_logical = (int64_t)max_tiles * g.n_col_tiles;
+  const int64_t group = 8LL * g.n_col_tiles;
+  const int64_t grid = ((n_logical + group - 1) / group) * group;
+  if (grid > INT32_MAX) return kNotSupported;
+  g.n_logical = (int)n_logical;
+  if constexpr (kMode == kDgradNF4)
+    hipLaunchKernelGGL(grouped_dgrad_kernel, dim3((unsigned)grid), dim3(kGemmThreads), 0, stream,
+                       g);
+  else
+    hipLaunchKernelGGL(grouped_gemm_fwd_kernel<kMode>, dim3((unsigned)grid), dim3(kGemmThreads),
+                       0, stream, g);
+  return launch_status();
+}
+
+static int common_gemm_checks(const uint16_t* x, int64_t x_stride, int32_t Kc,
+                              const uint8_t* codes, const void* scl, const int32_t* offsets,
+                              const int32_t* sorted_pairs, const int32_t* tiles,
+                              const int32_t* num_tiles, const uint16_t* out) {
+  if (!x || !codes || !scl || !offsets || !sorted_pairs || !tiles || !num_tiles || !out)
+    return kInvalid;
+  if (x_stride < Kc || x_stride % 8) return kInvalid;
+  if (!aligned16(x) || !aligned16(codes) || !aligned16(out)) return kInvalid;
+  if (!aligned4(offsets) || !aligned4(sorted_pairs) || !aligned4(tiles) || !aligned4(num_tiles))
+    return kInvalid;
+  return kOk;
+}
+
+template <bool kMx>
+static int forward_entry(const uint16_t* x, int32_t rows, int32_t K, int64_t x_stride,
+                         const uint8_t* codes, const void* scl, int32_t E, int32_t N,
+                         int32_t topk, const float* pair_scale, const int32_t* offsets,
+                         const int32_t* sorted_pairs, const int32_t* tiles,
+                         const int32_t* num_tiles, int32_t max_tiles, int32_t tile_m,
+                         uint16_t* out, hipStream_t stream) {
+  if (rows < 0 || topk < 1 || E < 1 || N < 1 || N % 32 || K <= 0 || K % (kMx ? 32 : 64))
+    return kInvalid;
+  if (x_stride < K || x_stride % 8) return kInvalid;
+  if (tile_m != kTM) return kNotSupported;
+  const int64_t P = (int64_t)rows * topk;
+  if (P >= INT32_MAX) return kNotSupported;
+  if (P == 0) return kOk;                                  // nothing to enqueue
+  int st = common_gemm_checks(x, x_stride, K, codes, scl, offsets, sorted_pairs, tiles,
+                              num_tiles, out);
+  if (st != kOk) return st;
+  if (!kMx && !aligned4(scl)) return kInvalid;
+  if (pair_scale && !aligned4(pair_scale)) return kInvalid;
+  GemmArgs g{};
+  g.x = x; g.x_stride = x_stride; g.codes = codes; g.scl = scl;
+  g.Nw = N; g.Kw = K; g.Kc = K; g.Nout = N;
+  g.E = E; g.topk = topk; g.P = (int)P; g.pair_scale = pair_scale;
+  g.offsets = offsets; g.sorted_pairs = sorted_pairs; g.tiles = tiles; g.num_tiles = num_tiles;
+  g.out = out;
+  return launch_gemm<kMx ? kFwdMX : kFwdNF4>(g, max_tiles, tile_m, stream);
+}
+
+}  // namespace gq
+
+extern "C" int gq_nf4_grouped_gemm(const uint16_t* x, int32_t rows, int32_t K, int64_t x_stride,
+                                   const uint8_t* codes, const float* absmax, int32_t num_experts,
+                                   int32_t N, int32_t topk, const float* pair_scale,
+                                   const int32_t* expert_offsets, const int32_t* sorted_pairs,
+                                   const int32_t* tiles, const int32_t* num_tiles,
+                                   int32_t max_tiles, int32_t tile_m, uint16_t* out,
+                                   hipStream_t stream) {
+  return gq::forward_entry<false>(x, rows, K, x_stride, codes, absmax, num_experts, N, topk,
+                                  pair_scale, expert_offsets, sorted_pairs, tiles, num_tiles,
+                                  max_tiles, tile_m, out, stream);
+}
+
+extern "C" int gq_mxfp4_grouped_gemm(const uint16_t* x, int32_t rows, int32_t K,
+                                     int64_t x_stride, const uint8_t* blocks,
+                                     const uint8_t* scales, int32_t num_experts, int32_t N,
+                                     int32_t topk, const float* pair_scale,
+                                     const int32_t* expert_offsets, const int32_t* sorted_pairs,
+                                     const int32_t* tiles, const int32_t* num_tiles,
+                                     int32_t max_tiles, int32_t tile_m, uint16_t* out,
+                                     hipStream_t stream) {
+  return gq::forward_entry<true>(x, rows, K, x_stride, blocks, scales, num_experts, N, topk,
+                                 pair_scale, expert_offsets, sorted_pairs, tiles, num_tiles,
+                                 max_tiles, tile_m, out, stream);
+}
+
+extern "C" int gq_nf4_grouped_dgrad(const uint16_t* dy, int32_t P, int32_t N, int64_t dy_stride,
+                                    const uint8_t* codes, const float* absmax,
+                                    int32_t num_experts, int32_t K,
+                                    const int32_t* expert_offsets, const int32_t* sorted_pairs,
+                                    const int32_t* tiles, const int32_t* num_tiles,
+                                    int32_t max_tiles, int32_t tile_m, uint16_t* dx,
+                                    hipStream_t stream) {
+  using namespace gq;
+  if (P < 0 || num_experts < 1 || N < 1 || N % 64 || K <= 0 || K % 64) return kInvalid;
+  if (dy_stride < N || dy_stride % 8) return kInvalid;
+  if (tile_m != kTM) return kNotSupported;
+  if (P == 0) return kOk;                                  // nothing to enqueue
+  int st = common_gemm_checks(dy, dy_stride, N, codes, absmax, expert_offsets, sorted_pairs,
+                              tiles, num_tiles, dx);
+  if (st != kOk) return st;
+  if (!aligned4(absmax)) return kInvalid;
+  GemmArgs g{};
+  g.x = dy; g.x_stride = dy_stride; g.codes = codes; g.scl = absmax;
+  g.Nw = N; g.Kw = K; g.Kc = N; g.Nout = K;
+  g.E = num_experts; g.topk = 1; g.P = P; g.pair_scale = nullptr;
+  g.offsets = expert_offsets; g.sorted_pairs = sorted_pairs; g.tiles = tiles;
+  g.num_tiles = num_tiles; g.out = dx;
+  return launch_gemm<kDgradNF4>(g, max_tiles, tile_m, stream);
+}

@@ -1,0 +1,292 @@
+// Decode-time grouped GEMV on 4-bit packed experts (a few token rows: 1..8
+// tokens in gather mode, or their routed pairs in flatten mode; <= 256 pairs).
+//
+// Pages: "grouped-nf4-gemm 0.43.0" -- page header (one launch for the
+// active experts, no full-size bf16 weight copies) and "Which entry
+// point?" (the single-row decode bandwidth route); "flashrt/grouped-moe-gemv"
+// -- "Functions" (one product per routed slot, [M, top_k] routing,
+// [M, top_k, N] output).  The kernel design is this library's own.
+//
+// Design (HBM-bound: the weight bytes of the active experts are the cost):
+//  * grid (ceil(N / R), P): workgroup (x, p) owns rows [x*R, x*R + R) of the
+//    expert of pair p.  Only the FIRST pair routed to an expert does the
+//    work and it serves every pair of that expert, so each active expert's
+//    bytes cross HBM once.  No sort, no host sync: topk_ids is read here.
+//  * a thread owns one 16-byte segment (32 weights) of the rows it handles,
+//    at a fixed K offset, so the activation slice it needs sits in 32
+//    float registers; several rows per thread, all loads issued up front.
+//    Consecutive threads read consecutive 16-byte pieces of contiguous rows
+//    (fully coalesced).
+//  * NF4: codebook lookups from a 16-entry LDS table (conflict-free), the
+//    64-block absmax factored out of each 32-weight partial sum; MXFP4: the
+//    gfx950 e2m1 converter, the e8m0 factor applied to the partial sum with
+//    ldexp.  Both keep the decoded weight exact (float32).
+//  * partial sums meet in LDS and are reduced in a fixed order: no atomics,
+//    bitwise reproducible.
+#include "gq_device.hpp"
+#include "gq_host.hpp"
+#include "../../include/gq.h"
+
+namespace gq {
+
+constexpr int kGemvMaxThreads = 256;
+constexpr int kGemvMaxPairs = 256;
+constexpr int kGemvMaxK = 8192;     // 256 segments of 32 weights
+
+// NF4 codebook values of the 8 weights of one code dword, in element order.
+// Addressing costs 1.5 ops per weight: the nibbles are first spread into
+// bytes already multiplied by 4 (byte offsets into the 16-float LDS table),
+// then each lookup extracts one byte.
+__device__ __forceinline__ void nf4_lookup8(const float* lut, uint32_t d, float q[8]) {
+  const uint32_t hi4 = (d >> 2) & 0x3C3C3C3Cu;     // byte j: 4 * code of element 2j
+  const uint32_t lo4 = (d << 2) & 0x3C3C3C3Cu;     // byte j: 4 * code of element 2j+1
+  const char* base = reinterpret_cast<const char*>(lut);
+#pragma unroll
+  for (int b = 0; b < 4; ++b) {
+    q[2 * b] = *reinterpret_cast<const float*>(base + ((hi4 >> (8 * b)) & 0xFFu));
+    q[2 * b + 1] = *reinterpret_cast<const float*>(base + ((lo4 >> (8 * b)) & 0xFFu));
+  }
+}
+
+// Partial dot product of one 32-weight segment with the activation slice.
+template <bool kMx>
+__device__ __forceinline__ float segment_dot(const float* lut, u32x4 c, float am, uint32_t sb,
+                                             const float (&xf)[32]) {
+  float acc = 0.f;
+#pragma unroll
+  for (int w = 0; w < 4; ++w) {
+    uint32_t d = c[w];
+    // The decode does not depend on the pair: without this the compiler
+    // hoists every row's decoded weights out of the pair loop and needs one
+    // register per weight.  (No instruction is emitted.)
+    asm volatile("" : "+v"(d));
+    if constexpr (kMx) {
+#pragma unroll
+      for (int b = 0; b < 4; ++b) {
+        const f32x2 v = e2m1_pair_f32(d, b);        // element 2j: low nibble
+        acc = __builtin_fmaf(v.x, xf[8 * w + 2 * b], acc);
+        acc = __builtin_fmaf(v.y, xf[8 * w + 2 * b + 1], acc);
+      }
+    } else {
+      float q[8];
+      nf4_lookup8(lut, d, q);                       // element 2j: high nibble
+#pragma unroll
+      for (int j = 0; j < 8; ++j) acc = __builtin_fmaf(q[j], xf[8 * w + j], acc);
+    }
+  }
+  if constexpr (kMx) return e8m0_apply(acc, sb);
+  else return acc * am;
+}
+
+// kIter rows per thread.  Memory round trips on the critical path: (1) the
+// expert id of pair p0, the routing table and p0's activation slice, all
+// issued together; (2) the weight bytes.  Routing decisions are taken per
+// wave from ballots (no barrier).  Pairs that share p0's expert (rare at
+// decode) cost one more activation load each.
+//
+// kWaveRows: a row's S segments lie inside one wave (64 % S == 0) and are
+// summed with a butterfly of cross-lane shuffles; otherwise partial sums
+// meet in LDS.  Both orders are fixed, so results are reproducible.
+template <bool kMx, int kIter, bool kWaveRows>
+__global__ __launch_bounds__(kGemvMaxThreads) void grouped_gemv_kernel(
+    const uint16_t* __restrict__ x, int64_t x_stride, int K, const uint8_t* __restrict__ codes,
+    const void* __restrict__ scl, int N, int E, const int32_t* __restrict__ ids, int topk, int P,
+    const float* __restrict__ pair_scale, uint16_t* __restrict__ out, int S, int G, int NT) {
+  __shared__ float lut[16];
+  __shared__ float red[kWaveRows ? 1 : kIter * (kGemvMaxThreads + 32)];
+
+  const int tid = threadIdx.x;                      // NT == blockDim.x
+  const int lane = tid & (kWave - 1);
+  const int p0 = blockIdx.y;
+  const int R = G * kIter;
+  const int n0 = blockIdx.x * R;
+  const bool active = tid < S * G;
+  const int g = tid / S;
+  const int s = tid - g * S;
+
+  // ---- round trip 1: expert of p0, routing table (per wave), p0's activations ----
+  const int e = ids[p0];
+  int idl[kGemvMaxPairs / kWave];
+#pragma unroll
+  for (int c = 0; c < kGemvMaxPairs / kWave; ++c) {
+    const int q = lane + kWave * c;
+    idl[c] = (kWave * c < P && q < P) ? ids[q] : -1;
+  }
+  u32x4 xr[4];
+  {
+    const u32x4* xp =
+        reinterpret_cast<const u32x4*>(x + (int64_t)(p0 / topk) * x_stride + (active ? s : 0) * 32);
+#pragma unroll
+    for (int v = 0; v < 4; ++v) xr[v] = xp[v];
+  }
+  if ((unsigned)e >= (unsigned)E) {          // dropped pair: its slice is zero
+    for (int r = tid; r < R; r += NT)
+      if (n0 + r < N) out[(int64_t)p0 * N + n0 + r] = 0;
+    return;
+  }
+
+  // ---- round trip 2: the weight bytes of expert e ----
+  const size_t row_bytes = (size_t)K / 2;
+  u32x4 cw[kIter];
+  float am[kIter];
+  uint32_t sb[kIter];
+  // Unconditional loads from clamped addresses (rows past N and idle lanes
+  // re-read valid bytes whose results are never stored): a conditional load
+  // would zero its registers first and stall on every older load in flight.
+  const int s_cl = active ? s : 0;
+#pragma unroll
+  for (int i = 0; i < kIter; ++i) {
+    const int n = min(n0 + g + G * i, N - 1);
+    const size_t row = (size_t)e * N + n;
+    cw[i] = *reinterpret_cast<const u32x4*>(codes + row * row_bytes + (size_t)s_cl * 16);
+    if constexpr (kMx) {
+      sb[i] = (uint32_t)static_cast<const uint8_t*>(scl)[row * (size_t)(K / 32) + s_cl];
+      am[i] = 0.f;
+    } else {
+      am[i] = static_cast<const float*>(scl)[row * (size_t)(K / 64) + s_cl / 2];
+      sb[i] = 0u;
+    }
+  }
+
+  // ---- is p0 the first pair of expert e?  (same answer in every wave) ----
+  uint64_t match[kGemvMaxPairs / kWave];
+  bool dup = false;
+#pragma unroll
+  for (int c = 0; c < kGemvMaxPairs / kWave; ++c) {
+    const int q = lane + kWave * c;
+    match[c] = __ballot(idl[c] == e);
+    dup |= __ballot(idl[c] == e && q < p0) != 0ull;
+  }
+  if (dup) return;
+  if constexpr (!kMx) {
+    nf4_lut_init(lut, tid);
+    lds_barrier();
+  }
+
+  // ---- one pass per pair routed to e, ascending; p0 (the first) is peeled so
+  // that its rows are processed as their loads land (no loop-head wait) ----
+  auto process_pair = [&](int p) {
+    float xf[32];
+#pragma unroll
+    for (int v = 0; v < 4; ++v)
+#pragma unroll
+      for (int cc = 0; cc < 4; ++cc) {
+        xf[8 * v + 2 * cc] = bf16lo_to_f32(xr[v][cc]);
+        xf[8 * v + 2 * cc + 1] = bf16hi_to_f32(xr[v][cc]);
+      }
+    const float sc = pair_scale ? pair_scale[p] : 1.f;
+    if constexpr (kWaveRows) {
+#pragma unroll
+      for (int i = 0; i < kIter; ++i) {
+        float part = active ? segment_dot<kMx>(lut, cw[i], am[i], sb[i], xf) : 0.f;
+        for (int off = S >> 1; off > 0; off >>= 1) part += __shfl_xor(part, off, kWave);
+        const int n = n0 + g + G * i;
+        if (active && s == 0 && n < N) out[(int64_t)p * N + n] = f32_to_bf16_bits(part * sc);
+      }
+    } else {
+      constexpr int kStride = kGemvMaxThreads + 32;            // pad: spreads banks
+#pragma unroll
+      for (int i = 0; i < kIter; ++i)
+        red[i * kStride + tid] = active ? segment_dot<kMx>(lut, cw[i], am[i], sb[i], xf) : 0.f;
+      lds_barrier();
+      for (int r = tid; r < R; r += NT) {
+        const int gg = r % G, ii = r / G;
+        const float* src = red + ii * kStride + gg * S;
+        float s0 = 0.f, s1 = 0.f, s2 = 0.f, s3 = 0.f;          // fixed order, 4 chains
+        int j = 0;
+        for (; j + 4 <= S; j += 4) {
+          s0 += src[j];
+          s1 += src[j + 1];
+          s2 += src[j + 2];
+          s3 += src[j + 3];
+        }
+        for (; j < S; ++j) s0 += src[j];
+        const int n = n0 + r;
+        if (n < N) out[(int64_t)p * N + n] = f32_to_bf16_bits(((s0 + s1) + (s2 + s3)) * sc);
+      }
+      lds_barrier();
+    }
+  };
+
+  process_pair(p0);
+  for (int c = 0; c < kGemvMaxPairs / kWave; ++c) {
+    uint64_t m = match[c];
+    if (c == p0 / kWave) m &= ~(1ull << (p0 % kWave));
+    while (m) {
+      const int p = kWave * c + __builtin_ctzll(m);
+      m &= m - 1ull;
+      const u32x4* xp = reinterpret_cast<const u32x4*>(x + (int64_t)(p / topk) * x_stride +
+                                                        (active ? s : 0) * 32);
+#pragma unroll
+      for (int v = 0; v < 4; ++v) xr[v] = xp[v];
+      process_pair(p);
+    }
+  }
+}
+
+template <bool kMx, int kIter>
+static void launch_gemv_iter(dim3 grid, int NT, hipStream_t stream, const uint16_t* x,
+                             int64_t x_stride, int K, const uint8_t* codes, const void* scl,
+                             int N, int E, const int32_t* ids, int topk, int P,
+                             const float* pair_scale, uint16_t* out, int S, int G) {
+  if (kWave % S == 0)
+    hipLaunchKernelGGL((grouped_gemv_kernel<kMx, kIter, true>), grid, dim3(NT), 0, stream, x,
+                       x_stride, K, codes, scl, N, E, ids, topk, P, pair_scale, out, S, G, NT);
+  else
+    hipLaunchKernelGGL((grouped_gemv_kernel<kMx, kIter, false>), grid, dim3(NT), 0, stream, x,
+                       x_stride, K, codes, scl, N, E, ids, topk, P, pair_scale, out, S, G, NT);
+}
+
+template <bool kMx>
+static int launch_gemv(const uint16_t* x, int32_t rows, int32_t K, int64_t x_stride,
+                       const uint8_t* codes, const void* scl, int32_t E, int32_t N,
+                       const int32_t* ids, int32_t topk, const float* pair_scale, uint16_t* out,
+                       hipStream_t stream) {
+  if (!x || !codes || !scl || !ids || !out) return kInvalid;
+  if (rows < 1 || topk < 1 || E < 1 || N < 1 || K <= 0) return kInvalid;
+  if (K % (kMx ? 32 : 64)) return kInvalid;
+  if (x_stride < K || x_stride % 8) return kInvalid;
+  if (!aligned16(x) || !aligned16(codes) || !aligned4(ids) || !aligned4(out)) return kInvalid;
+  if (!kMx && !aligned4(scl)) return kInvalid;
+  if (pair_scale && !aligned4(pair_scale)) return kInvalid;
+  const int64_t P = (int64_t)rows * topk;
+  if (P > kGemvMaxPairs || K > kGemvMaxK || N >= (1 << 24)) return kNotSupported;
+  const int S = K / 32;
+  const int G = S >= kGemvMaxThreads ? 1 : kGemvMaxThreads / S;
+  const int NT = ((S * G + kWave - 1) / kWave) * kWave;
+  // Rows per thread: as many loads in flight per thread as possible while the
+  // grid of one pair still spreads over every CU twice.
+  const int64_t want_blocks = 512;
+  int iter = 8;
+  while (iter > 2 && (int64_t)((N + G * iter - 1) / (G * iter)) * P < want_blocks) iter >>= 1;
+  const int R = G * iter;
+  const dim3 grid((N + R - 1) / R, (unsigned)P);
+  switch (iter) {
+    case 8: launch_gemv_iter<kMx, 8>(grid, NT, stream, x, x_stride, K, codes, scl, N, E, ids,
+                                     topk, (int)P, pair_scale, out, S, G); break;
+    case 4: launch_gemv_iter<kMx, 4>(grid, NT, stream, x, x_stride, K, codes, scl, N, E, ids,
+                                     topk, (int)P, pair_scale, out, S, G); break;
+    default: launch_gemv_iter<kMx, 2>(grid, NT, stream, x, x_stride, K, codes, scl, N, E, ids,
+                                      topk, (int)P, pair_scale, out, S, G); break;
+  }
+  return launch_status();
+}
+
+}  // namespace gq
+
+extern "C" int gq_nf4_grouped_gemv(const uint16_t* x, int32_t rows, int32_t K, int64_t x_stride,
+                                   const uint8_t* codes, const float* absmax, int32_t num_experts,
+                                   int32_t N, const int32_t* topk_ids, int32_t topk,
+                                   const float* pair_scale, uint16_t* out, hipStream_t stream) {
+  return gq::launch_gemv<false>(x, rows, K, x_stride, codes, absmax, num_experts, N, topk_ids,
+                                topk, pair_scale, out, stream);
+}
+
+extern "C" int gq_mxfp4_grouped_gemv(const uint16_t* x, int32_t rows, int32_t K, int64_t x_stride,
+                                     const uint8_t* blocks, const uint8_t* scales,
+                                     int32_t num_experts, int32_t N, const int32_t* topk_ids,
+                                     int32_t topk, const float* pair_scale, uint16_t* out,
+                                     hipStream_t stream) {
+  return gq::launch_gemv<true>(x, rows, K, x_stride, blocks, scales, num_experts, N, topk_ids,
+                               topk, pair_scale, out, stream);
+}

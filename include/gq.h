@@ -1,0 +1,212 @@
+/*
+ * gq.h -- C ABI of libgq: grouped mixture-of-experts matmul on 4-bit packed
+ * expert weights (NF4 and MXFP4) for AMD MI355X (gfx950).
+ *
+ * What the library computes follows these web pages:
+ *   [P1] "grouped-nf4-gemm 0.43.0" (PyPI project page): section "Which
+ *        entry point?" (grouped NF4 forward and backward, the single-row
+ *        decode bandwidth route, native MXFP4 expert math) and the page
+ *        header (one GPU launch for the active experts, no full-size bf16
+ *        weight copies); section "Try the packers and byte checks on CPU"
+ *        (packed shapes).
+ *   [P2] "Receipts-driven engineering": opening summary (codebook decoded
+ *        in registers inside the GEMM mainloop; NF4 in the bitsandbytes
+ *        packed layout; MXFP4 as OCP e2m1 on released bytes; the NF4 path
+ *        is differentiable).
+ *   [P4] "flashrt/grouped-moe-gemv": section "Functions" (routing tensor
+ *        [M, top_k] of expert ids, output [M, top_k, N], flatten to
+ *        M = routed pairs and top_k = 1 when each pair has its own input;
+ *        no atomics, no host synchronisation, caller-owned buffers).
+ *   [P5] GPTQModel wiki "NF12": malformed arguments to native C-ABI calls
+ *        return hipErrorInvalidValue; launches beyond supported limits
+ *        return hipErrorNotSupported before launch.
+ *
+ * Conventions shared by every entry point
+ * ---------------------------------------
+ * - Every buffer pointer is DEVICE memory on the current HIP device and is
+ *   owned by the caller; the library never allocates, frees or keeps a
+ *   pointer after the call returns.
+ * - Work is enqueued asynchronously on `stream` (NULL = default stream);
+ *   nothing synchronises the host.  Results are ready when the stream is.
+ * - bf16 values travel as raw uint16_t bit patterns.
+ * - Packed weights (all experts stacked, contiguous):
+ *     NF4   codes  uint8 [E, N, K/2]  element 2j of a row in the HIGH nibble
+ *                                     of byte j (bitsandbytes layout)
+ *           absmax float [E, N, K/64] one scale per 64 consecutive k
+ *           weight = float32(nf4_codebook[code] * absmax)
+ *     MXFP4 blocks uint8 [E, N, K/32, 16] element 2j of a 32-block in the LOW
+ *                                     nibble of byte j (released gpt-oss layout)
+ *           scales uint8 [E, N, K/32] e8m0: factor 2^(s-127); 255 = NaN
+ *           weight = e2m1(code) * 2^(s-127)
+ * - Routing: topk_ids int32 [rows, topk], pair index p = t*topk + s.  A pair
+ *   routed to an id outside [0, E) is dropped and its output row is zeros.
+ *   Gather mode (topk > 1): pair p reads activation row p / topk.  Flatten
+ *   mode (per-pair inputs, e.g. a down projection): pass rows = pairs and
+ *   topk = 1.
+ * - Outputs are bf16, rounded to nearest even from an fp32 accumulator,
+ *   optionally multiplied by pair_scale[p] (fp32, one per pair; NULL = 1).
+ *   No atomics: each output element is written by exactly one thread, so
+ *   results are bitwise reproducible run to run.
+ * - Return value: 0 on success; hipErrorInvalidValue (1) for a malformed
+ *   argument (checked on the host before anything is enqueued; nothing is
+ *   truncated or clamped); hipErrorNotSupported (801) for a well-formed
+ *   request outside what the kernels support (stated per function);
+ *   otherwise the HIP error reported by the launch.
+ * - Expert ids are data on the device; the kernels treat any id outside
+ *   [0, E) as dropped, so no id can make a kernel read outside the banks.
+ */
+#ifndef GQ_H
+#define GQ_H
+
+#include <stdint.h>
+#include <hip/hip_runtime_api.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+/* Name of a status code returned by this library (static string). */
+const char* gq_status_string(int status);
+
+/* ------------------------------------------------------------------------
+ * Token-to-expert grouping.  [P1] header and [P2] summary: all active
+ * experts run in one launch, which needs the pairs grouped by expert on the
+ * device without a host round trip ([P4] "Functions": no host sync).
+ *
+ * Upper bound on the number of tiles gq_route_sort can emit, including the
+ * tiles the grouped GEMM uses to clear dropped rows:
+ *     ceil(rows*topk / tile_m) + E + 1.
+ * Returns -1 if an argument is negative, tile_m < 1 or E < 1.
+ */
+int32_t gq_route_max_tiles(int32_t rows, int32_t topk, int32_t num_experts, int32_t tile_m);
+
+/*
+ * Stable counting sort of the rows*topk (token, slot) pairs by expert.
+ *   topk_ids       int32 [rows, topk]       in
+ *   expert_offsets int32 [E + 1]            out: offsets[e] = #valid pairs with
+ *                                                expert < e; offsets[E] = #valid pairs
+ *   sorted_pairs   int32 [rows*topk]        out: expert by expert, ascending pair
+ *                                                index within an expert; dropped
+ *                                                pairs last, ascending
+ *   tiles          int32 [max_tiles, 2]     out: (expert, start in sorted_pairs) of
+ *                                                every tile_m-row slice of each
+ *                                                expert's segment, experts
+ *                                                ascending; unused entries = -1
+ *   num_tiles      int32 [1]                out: number of valid tiles
+ * Deterministic: the output is the unique answer to the definition above.
+ * InvalidValue: null pointer, rows/topk < 0, E < 1, tile_m < 1,
+ *               max_tiles < gq_route_max_tiles(...).
+ * NotSupported: E > 1024, rows*topk >= 2^31.
+ * rows*topk == 0 is valid (offsets all 0, num_tiles 0, tiles all -1).
+ */
+int gq_route_sort(const int32_t* topk_ids, int32_t rows, int32_t topk, int32_t num_experts,
+                  int32_t tile_m, int32_t* expert_offsets, int32_t* sorted_pairs,
+                  int32_t* tiles, int32_t max_tiles, int32_t* num_tiles, hipStream_t stream);
+
+/* ------------------------------------------------------------------------
+ * Decode probes.  [P1] "Try the packers and byte checks on CPU" (packed
+ * shapes) and [P2] summary (codes decoded in registers).  They write the
+ * decoded weights with the same device decode routines the matmul kernels
+ * use, so decoding can be compared bit for bit.  Not on the hot path.
+ *   NF4:   codes [n_rows, K/2], absmax [n_rows, K/64]; K % 64 == 0
+ *   MXFP4: blocks [n_rows, K/32, 16], scales [n_rows, K/32]; K % 32 == 0
+ *   out_f32 float [n_rows, K] (may be NULL), out_bf16 uint16 [n_rows, K]
+ *   (may be NULL; bf16 = RNE of the float32 weight).  At least one output.
+ * InvalidValue: null inputs, both outputs NULL, n_rows < 0, K <= 0 or not a
+ * multiple of the block.
+ */
+int gq_nf4_decode(const uint8_t* codes, const float* absmax, int64_t n_rows, int32_t K,
+                  float* out_f32, uint16_t* out_bf16, hipStream_t stream);
+int gq_mxfp4_decode(const uint8_t* blocks, const uint8_t* scales, int64_t n_rows, int32_t K,
+                    float* out_f32, uint16_t* out_bf16, hipStream_t stream);
+
+/* ------------------------------------------------------------------------
+ * Decode-time GEMV: 1..8 tokens in gather mode, or their routed pairs in
+ * flatten mode (at most 256 pairs).  [P1] header, "Which entry point?"
+ * (single-row decode bandwidth route), [P4] "Functions" (one product per
+ * routed slot, [M, top_k] -> [M, top_k, N]).
+ *
+ *   out[p, n] = bf16( pair_scale[p] * sum_k x[p/topk, k] * W_{ids[p]}[n, k] )
+ *
+ *   x          uint16 bf16 [rows, K] with row stride x_stride elements
+ *              (x_stride >= K, x_stride % 8 == 0, x 16-byte aligned)
+ *   codes/absmax (NF4) or blocks/scales (MXFP4) for E experts of shape [N, K]
+ *   topk_ids   int32 [rows, topk]; pair_scale float [rows*topk] or NULL
+ *   out        uint16 bf16 [rows*topk, N]
+ * Each distinct active expert's bytes are read once, whichever tokens use
+ * it; no sort is needed (the kernel reads topk_ids directly).  Arithmetic:
+ * exact float32 decode, float32 products and sums.
+ * InvalidValue: null pointer (pair_scale may be NULL), rows < 1,
+ *   topk < 1, E < 1, N < 1, K not a positive multiple of 64 (NF4) / 32
+ *   (MXFP4), bad stride or alignment.
+ * NotSupported: rows*topk > 256, K > 8192, N >= 2^24.
+ */
+int gq_nf4_grouped_gemv(const uint16_t* x, int32_t rows, int32_t K, int64_t x_stride,
+                        const uint8_t* codes, const float* absmax, int32_t num_experts,
+                        int32_t N, const int32_t* topk_ids, int32_t topk,
+                        const float* pair_scale, uint16_t* out, hipStream_t stream);
+int gq_mxfp4_grouped_gemv(const uint16_t* x, int32_t rows, int32_t K, int64_t x_stride,
+                          const uint8_t* blocks, const uint8_t* scales, int32_t num_experts,
+                          int32_t N, const int32_t* topk_ids, int32_t topk,
+                          const float* pair_scale, uint16_t* out, hipStream_t stream);
+
+/* ------------------------------------------------------------------------
+ * Prefill grouped GEMM.  [P1] "Which entry point?" (grouped NF4 forward,
+ * native MXFP4 expert math) and header (one launch for the active experts,
+ * no full-size bf16 weight copies); [P2] summary (codebook decoded in
+ * registers inside the mainloop).
+ *
+ *   out[p, n] = bf16( pair_scale[p] * sum_k x[p/topk, k] * W_{ids[p]}[n, k] )
+ *
+ * Same x / weights / pair_scale / out conventions as the GEMV.  The
+ * grouping comes from gq_route_sort(topk_ids, rows, topk, E, tile_m, ...)
+ * called with the same tile_m: expert_offsets, sorted_pairs, tiles,
+ * num_tiles and max_tiles are passed through unchanged.  Dropped pairs'
+ * rows are written as zeros by the same launch.  Arithmetic: decoded weight
+ * rounded to bf16 (NF4: RNE of the float32 weight; MXFP4: exact), bf16
+ * matrix-core products, float32 accumulation.
+ * InvalidValue: null pointer (pair_scale may be NULL), rows < 0, topk < 1,
+ *   E < 1, N < 1 or N % 32, K not a positive multiple of 64 (NF4) / 32
+ *   (MXFP4), bad stride or alignment, max_tiles below the bound.
+ * NotSupported: tile_m != 256, rows*topk >= 2^31, grid beyond 2^31 blocks.
+ * rows == 0 enqueues nothing.
+ */
+int gq_nf4_grouped_gemm(const uint16_t* x, int32_t rows, int32_t K, int64_t x_stride,
+                        const uint8_t* codes, const float* absmax, int32_t num_experts,
+                        int32_t N, int32_t topk, const float* pair_scale,
+                        const int32_t* expert_offsets, const int32_t* sorted_pairs,
+                        const int32_t* tiles, const int32_t* num_tiles, int32_t max_tiles,
+                        int32_t tile_m, uint16_t* out, hipStream_t stream);
+int gq_mxfp4_grouped_gemm(const uint16_t* x, int32_t rows, int32_t K, int64_t x_stride,
+                          const uint8_t* blocks, const uint8_t* scales, int32_t num_experts,
+                          int32_t N, int32_t topk, const float* pair_scale,
+                          const int32_t* expert_offsets, const int32_t* sorted_pairs,
+                          const int32_t* tiles, const int32_t* num_tiles, int32_t max_tiles,
+                          int32_t tile_m, uint16_t* out, hipStream_t stream);
+
+/* ------------------------------------------------------------------------
+ * NF4 input gradient.  [P1] "Which entry point?" (grouped NF4 backward);
+ * [P2] summary (the NF4 path is differentiable, fine-tuning stays packed).
+ *
+ *   dx[p, k] = bf16( sum_n dy[p, n] * W_{e(p)}[n, k] )
+ *
+ *   dy   uint16 bf16 [P, N] with row stride dy_stride elements (per pair)
+ *   dx   uint16 bf16 [P, K]
+ * The grouping comes from gq_route_sort(pair_expert, P, 1, E, tile_m, ...);
+ * pairs with an expert outside [0, E) get dx rows of zeros.  Same decode
+ * and arithmetic as the NF4 GEMM, contraction over N.
+ * InvalidValue: null pointer, P < 0, E < 1, N < 1 or N % 64, K not a
+ *   positive multiple of 64, bad stride or alignment, max_tiles too small.
+ * NotSupported: tile_m != 256, grid beyond 2^31 blocks.
+ */
+int gq_nf4_grouped_dgrad(const uint16_t* dy, int32_t P, int32_t N, int64_t dy_stride,
+                         const uint8_t* codes, const float* absmax, int32_t num_experts,
+                         int32_t K, const int32_t* expert_offsets, const int32_t* sorted_pairs,
+                         const int32_t* tiles, const int32_t* num_tiles, int32_t max_tiles,
+                         int32_t tile_m, uint16_t* dx, hipStream_t stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* GQ_H */

@@ -1,0 +1,147 @@
+"""CPU checks of the C ABI: the library loads, exports every entry point that
+include/gq.h declares, and rejects malformed arguments on the host before
+anything is enqueued (no compute call is made here; no GPU is needed)."""
+
+import ctypes
+import os
+import re
+
+import pytest
+
+import bit_grouped_moe_amd as gq
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+INVALID, NOT_SUPPORTED = 1, 801
+
+
+def _declared():
+    text = open(os.path.join(ROOT, "include", "gq.h")).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(gq_[a-z0-9_]+)\s*\(", text)))
+
+
+@pytest.fixture(scope="module")
+def lib():
+    return gq.load_library()
+
+
+def test_every_declared_symbol_is_exported(lib):
+    names = _declared()
+    assert len(names) >= 10
+    for n in names:
+        assert hasattr(lib, n), n
+    assert sorted(gq.EXPORTED_SYMBOLS) == names
+
+
+def test_status_strings(lib):
+    assert b"success" in lib.gq_status_string(0)
+    assert b"InvalidValue" in lib.gq_status_string(INVALID)
+    assert b"NotSupported" in lib.gq_status_string(NOT_SUPPORTED)
+
+
+def test_route_max_tiles(lib):
+    assert lib.gq_route_max_tiles(4096, 8, 128, 256) == 128 + 128 + 1
+    assert lib.gq_route_max_tiles(16, 2, 4, 256) == 1 + 4 + 1
+    assert lib.gq_route_max_tiles(0, 8, 128, 256) == 129
+    assert lib.gq_route_max_tiles(-1, 8, 128, 256) == -1
+    assert lib.gq_route_max_tiles(1, 8, 0, 256) == -1
+    assert lib.gq_route_max_tiles(1, 8, 4, 0) == -1
+
+
+F = ctypes.c_void_p(0x1000)          # a fake, aligned, never-dereferenced pointer
+F2 = ctypes.c_void_p(0x1002)         # misaligned
+NULL = None
+
+
+def test_route_sort_rejects(lib):
+    ok = dict(ids=F, rows=4, topk=2, E=8, tm=256, off=F, sp=F, tl=F, mt=11, nt=F)
+
+    def call(**kw):
+        a = {**ok, **kw}
+        return lib.gq_route_sort(a["ids"], a["rows"], a["topk"], a["E"], a["tm"], a["off"],
+                                 a["sp"], a["tl"], a["mt"], a["nt"], None)
+    assert call(ids=NULL) == INVALID
+    assert call(off=NULL) == INVALID
+    assert call(rows=-1) == INVALID
+    assert call(E=0) == INVALID
+    assert call(tm=0) == INVALID
+    assert call(mt=lib.gq_route_max_tiles(4, 2, 8, 256) - 1) == INVALID
+    assert call(E=1025, mt=2000) == NOT_SUPPORTED
+
+
+def test_decode_rejects(lib):
+    assert lib.gq_nf4_decode(NULL, F, 4, 64, F, F, None) == INVALID
+    assert lib.gq_nf4_decode(F, F, 4, 64, NULL, NULL, None) == INVALID
+    assert lib.gq_nf4_decode(F, F, 4, 96, F, F, None) == INVALID
+    assert lib.gq_nf4_decode(F, F, -1, 64, F, F, None) == INVALID
+    assert lib.gq_nf4_decode(F, F, 4, 64, F2, NULL, None) == INVALID
+    assert lib.gq_mxfp4_decode(F, F, 4, 48, F, F, None) == INVALID
+    assert lib.gq_mxfp4_decode(F, NULL, 4, 32, F, F, None) == INVALID
+
+
+def _gemv(lib, fn, **kw):
+    a = dict(x=F, rows=1, K=2048, xs=2048, c=F, s=F, E=128, N=1536, ids=F, topk=8, ps=NULL,
+             out=F)
+    a.update(kw)
+    return getattr(lib, fn)(a["x"], a["rows"], a["K"], a["xs"], a["c"], a["s"], a["E"], a["N"],
+                            a["ids"], a["topk"], a["ps"], a["out"], None)
+
+
+@pytest.mark.parametrize("fn", ["gq_nf4_grouped_gemv", "gq_mxfp4_grouped_gemv"])
+def test_gemv_rejects(lib, fn):
+    assert _gemv(lib, fn, x=NULL) == INVALID
+    assert _gemv(lib, fn, ids=NULL) == INVALID
+    assert _gemv(lib, fn, rows=0) == INVALID
+    assert _gemv(lib, fn, rows=33) == NOT_SUPPORTED              # 33*8 pairs > 256
+    assert _gemv(lib, fn, topk=0) == INVALID
+    assert _gemv(lib, fn, K=2050, xs=2050) == INVALID
+    assert _gemv(lib, fn, xs=2047) == INVALID
+    assert _gemv(lib, fn, xs=2052) == INVALID
+    assert _gemv(lib, fn, x=F2) == INVALID
+    assert _gemv(lib, fn, rows=8, topk=33) == NOT_SUPPORTED
+    assert _gemv(lib, fn, K=16384, xs=16384) == NOT_SUPPORTED
+    if fn == "gq_nf4_grouped_gemv":
+        assert _gemv(lib, fn, K=2080, xs=2080) == INVALID      # K % 64
+
+
+def _gemm(lib, fn, **kw):
+    a = dict(x=F, rows=4096, K=2048, xs=2048, c=F, s=F, E=128, N=1536, topk=8, ps=NULL,
+             off=F, sp=F, tl=F, nt=F, mt=257, tm=256, out=F)
+    a.update(kw)
+    return getattr(lib, fn)(a["x"], a["rows"], a["K"], a["xs"], a["c"], a["s"], a["E"], a["N"],
+                            a["topk"], a["ps"], a["off"], a["sp"], a["tl"], a["nt"], a["mt"],
+                            a["tm"], a["out"], None)
+
+
+@pytest.mark.parametrize("fn", ["gq_nf4_grouped_gemm", "gq_mxfp4_grouped_gemm"])
+def test_gemm_rejects(lib, fn):
+    assert _gemm(lib, fn, tl=NULL) == INVALID
+    assert _gemm(lib, fn, rows=-1) == INVALID
+    assert _gemm(lib, fn, N=1552) == INVALID                   # N % 32
+    assert _gemm(lib, fn, mt=256) == INVALID                   # below the tile bound
+    assert _gemm(lib, fn, out=F2) == INVALID
+    assert _gemm(lib, fn, tm=128) == NOT_SUPPORTED
+    assert _gemm(lib, fn, rows=0) == 0                         # nothing enqueued
+
+
+def test_dgrad_rejects(lib):
+    def call(**kw):
+        a = dict(dy=F, P=16384, N=1536, ds=1536, c=F, s=F, E=128, K=2048, off=F, sp=F, tl=F,
+                 nt=F, mt=193, tm=256, dx=F)
+        a.update(kw)
+        return lib.gq_nf4_grouped_dgrad(a["dy"], a["P"], a["N"], a["ds"], a["c"], a["s"],
+                                        a["E"], a["K"], a["off"], a["sp"], a["tl"], a["nt"],
+                                        a["mt"], a["tm"], a["dx"], None)
+    assert call(dy=NULL) == INVALID
+    assert call(N=1568, ds=1568) == INVALID                    # N % 64
+    assert call(K=2080) == INVALID
+    assert call(mt=100) == INVALID
+    assert call(tm=64) == NOT_SUPPORTED
+    assert call(P=0) == 0
+
+
+def test_missing_library_raises(monkeypatch, tmp_path):
+    monkeypatch.setattr(gq, "_lib", None)
+    monkeypatch.setenv("GQ_LIBRARY", str(tmp_path / "nope.so"))
+    with pytest.raises(gq.GQError):
+        gq.load_library()

@@ -89,9 +89,11 @@ def router_weights(g, M, k):
 
 
 def _max_abs_normal(u, n):
-    """Inverse CDF of max of n iid |N(0,1)| at uniform u (torch tensors)."""
+    """Inverse CDF of max of n iid |N(0,1)| at uniform u (torch tensors),
+    evaluated in float64 so that u**(1/n) stays below 1."""
     import torch
-    return torch.erfinv(u.pow(1.0 / n)) * (2.0 ** 0.5)
+    v = u.to(torch.float64).clamp(1e-12, 1.0 - 1e-12).pow(1.0 / n)
+    return torch.erfinv(v) * (2.0 ** 0.5)
 
 
 def random_nf4_bank(E, N, K, device, seed, std=0.02):
@@ -104,7 +106,6 @@ def random_nf4_bank(E, N, K, device, seed, std=0.02):
     gen.manual_seed(int(seed))
     codes = torch.randint(0, 256, (E, N, K // 2), dtype=torch.uint8, device=device, generator=gen)
     u = torch.rand((E, N, K // 64), device=device, generator=gen, dtype=torch.float32)
-    u = u.clamp(1e-6, 1 - 1e-7)
     absmax = (_max_abs_normal(u, 64) * std).to(torch.float32)
     return codes, absmax
 
