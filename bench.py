@@ -6,27 +6,33 @@ Headline workload (one JSON line on stdout): Qwen3-30B-A3B-shaped NF4
 decode at M = 1 token, top-8 of E = 128 experts.  One step is one decode
 token through both expert projections: the gate_up GEMV (W [1536, 2048])
 and the down GEMV (W [2048, 768], one input row per routed pair).  Every
-step draws a fresh routing and rotates through 16 independent copies of
-each expert bank, so the active experts' bytes come from HBM and not from
-the 256 MB last-level cache.  ``value`` is algorithmic bytes per second:
-packed codes + absmax of the distinct active experts, activations read
-once, outputs written once.
+step has its own routing and reads one of 16 independent copies of each
+expert bank in turn, so the active experts' bytes come from HBM and not
+from the 256 MB last-level cache.  The K timed steps are captured once in a
+HIP graph and replayed (a decode loop's launch pattern), bracketed by
+device synchronisation.  ``value`` is algorithmic bytes per second: packed
+codes + absmax of the distinct active experts, activations read once,
+outputs written once.
 
 The same line carries
-  * ``roofline``: the gate_up GEMV kernel's algorithmic bytes per launch
-    over its average launch time (HIP events on the launch stream) against
-    the 8 TB/s HBM peak;
-  * ``cpu_baseline``: the CPU oracle (decode + float64 grouped matmul)
-    timed on a bounded sample of the same decode steps;
-  * ``prefill``: the Qwen3 NF4 prefill (M = 4096, Zipf(1.1) top-8, router
-    weights) -- route sort + gate_up GEMM + down GEMM -- in TFLOP/s
-    against the bf16 MFMA peak;
+  * ``roofline``: the gate_up GEMV kernel's algorithmic bytes per launch over
+    its average device time per launch, from HIP events around a replayed
+    graph of K gate_up launches on the launch stream, against the 8 TB/s HBM
+    peak; plus same-run controls: the empty-launch floor and a plain
+    streaming read of the same byte count from cold memory;
+  * ``cpu_baseline``: the CPU oracle (decode + float64 grouped matmul) on a
+    bounded sample of the same decode steps;
+  * ``prefill``: Qwen3 NF4 prefill (M = 4096, Zipf(1.1) top-8, router
+    weights) -- route sort + gate_up GEMM + down GEMM -- in TFLOP/s against
+    the dense bf16 MFMA peak;
   * ``extra``: MXFP4 gpt-oss-20b decode (M = 1) and prefill (M = 2048), NF4
-    dgrad (M = 2048, top-8), and the M = 4 decode.
+    dgrad (M = 2048, top-8) and the NF4 M = 4 decode.
 All inputs are synthetic and resident in HBM before timing starts.
 """
 
 import argparse
+import ctypes
+import hashlib
 import json
 import os
 import sys
@@ -45,6 +51,7 @@ HBM_PEAK_GBS = 8000.0            # MI355X HBM3E
 BF16_PEAK_TFLOPS = 2516.6        # MI355X dense bf16 MFMA
 FP4_PEAK_TFLOPS = 10066.0        # MI355X dense fp4 MFMA
 COPIES = 16                      # independent bank copies rotated per step
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic_counters.json")
 
 
 def log(*a):
@@ -59,8 +66,37 @@ def mx_expert_bytes(N, K):
     return N * K // 2 + N * (K // 32)
 
 
+def bf16_dev(bits, dev):
+    return torch.from_numpy(np.ascontiguousarray(bits).view(np.int16)).view(torch.bfloat16).to(dev)
+
+
+def capture(fn, n):
+    """HIP graph of fn(0) .. fn(n-1) captured on a side stream."""
+    g = torch.cuda.CUDAGraph()
+    s = torch.cuda.Stream()
+    s.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.graph(g, stream=s):
+        for i in range(n):
+            fn(i)
+    torch.cuda.current_stream().wait_stream(s)
+    return g
+
+
+def event_ms(fn):
+    """Device time of fn() from HIP events on the current stream."""
+    e0 = torch.cuda.Event(enable_timing=True)
+    e1 = torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    e0.record()
+    fn()
+    e1.record()
+    torch.cuda.synchronize()
+    return e0.elapsed_time(e1)
+
+
 class Timer:
-    """Per-launch HIP event pairs on torch's current stream."""
+    """Event pairs around individual launches (long kernels only: the queue
+    stays busy, so host launch latency does not leak into the pair)."""
 
     def __init__(self):
         self.pairs = []
@@ -79,20 +115,15 @@ class Timer:
         return 1e3 * float(np.mean([a.elapsed_time(b) for a, b in self.pairs]))
 
 
-def bf16_dev(bits, dev):
-    return torch.from_numpy(np.ascontiguousarray(bits).view(np.int16)).view(torch.bfloat16).to(dev)
-
-
 # --------------------------------------------------------------------------
 def decode_nf4(dev, steps, warmup, M=1):
-    """Qwen3 NF4 decode: gate_up GEMV + down GEMV per step."""
+    """Qwen3 NF4 decode: gate_up GEMV + down GEMV per step (graph replay)."""
     E, topk = wl.QWEN["E"], wl.QWEN["topk"]
     (Ng, Kg), (Nd, Kd) = wl.QWEN["gate_up"], wl.QWEN["down"]
     banks_g = [wl.random_nf4_bank(E, Ng, Kg, dev, seed=10 + c) for c in range(COPIES)]
     banks_d = [wl.random_nf4_bank(E, Nd, Kd, dev, seed=100 + c) for c in range(COPIES)]
-    n = steps + warmup
     g = wl.rng(wl.CFG_QWEN_DECODE, wl.S_ROUTE)
-    ids = [wl.route_uniform(g, M, E, topk) for _ in range(n)]
+    ids = [wl.route_uniform(g, M, E, topk) for _ in range(steps + warmup)]
     ids_g = [torch.from_numpy(i).to(dev) for i in ids]
     ids_d = [torch.from_numpy(i.reshape(-1, 1).copy()).to(dev) for i in ids]
     x = bf16_dev(wl.draw_bf16(wl.rng(wl.CFG_QWEN_DECODE, wl.S_X), (M, Kg)), dev)
@@ -100,38 +131,43 @@ def decode_nf4(dev, steps, warmup, M=1):
     out_g = torch.empty((M * topk, Ng), dtype=torch.bfloat16, device=dev)
     out_d = torch.empty((M * topk, Nd), dtype=torch.bfloat16, device=dev)
 
+    def gate(i):
+        c, a = banks_g[i % COPIES]
+        gq.gq_nf4_grouped_gemv(x, c, a, ids_g[i], out=out_g)
+
+    def down(i):
+        c, a = banks_d[i % COPIES]
+        gq.gq_nf4_grouped_gemv(xd, c, a, ids_d[i], out=out_d)
+
+    def step(i):
+        gate(i)
+        down(i)
+
+    for i in range(steps, steps + warmup):            # untimed warmup steps (eager)
+        step(i)
+    g_steps = capture(step, steps)
+    g_gate = capture(gate, steps)
+    g_steps.replay()                                   # first replay uploads the graph
+    g_gate.replay()
+    torch.cuda.synchronize()
+
+    t0 = time.perf_counter()
+    g_steps.replay()
+    torch.cuda.synchronize()
+    dt = time.perf_counter() - t0
+    gate_ms = event_ms(g_gate.replay)
+
     def step_bytes(i):
         d = len(set(ids[i].reshape(-1).tolist()))
         bg = d * nf4_expert_bytes(Ng, Kg) + M * Kg * 2 + M * topk * Ng * 2
         bd = d * nf4_expert_bytes(Nd, Kd) + M * topk * Kd * 2 + M * topk * Nd * 2
         return bg, bd
 
-    tg = Timer()
-
-    def run(i, timed):
-        cg, ag = banks_g[i % COPIES]
-        cd, ad = banks_d[i % COPIES]
-        ev = tg.start() if timed else None
-        gq.gq_nf4_grouped_gemv(x, cg, ag, ids_g[i], out=out_g)
-        if timed:
-            tg.stop(ev)
-        gq.gq_nf4_grouped_gemv(xd, cd, ad, ids_d[i], out=out_d)
-
-    for i in range(warmup):
-        run(i, False)
-    torch.cuda.synchronize()
-    t0 = time.perf_counter()
-    for i in range(warmup, n):
-        run(i, True)
-    torch.cuda.synchronize()
-    dt = time.perf_counter() - t0
-    byts = [step_bytes(i) for i in range(warmup, n)]
+    byts = [step_bytes(i) for i in range(steps)]
     total = sum(a + b for a, b in byts)
     gate_bytes = float(np.mean([a for a, _ in byts]))
-    gate_us = tg.avg_us()
-    # one host copy of the active experts of the first timed steps, for the oracle
-    sample = {"ids": ids[warmup:], "banks_g": banks_g, "banks_d": banks_d,
-              "x": x, "xd": xd, "warmup": warmup}
+    gate_us = 1e3 * gate_ms / steps
+    sample = {"ids": ids[:steps], "banks_g": banks_g, "banks_d": banks_d, "x": x, "xd": xd}
     return {
         "ms_per_step": 1e3 * dt / steps,
         "gbs": total / dt / 1e9,
@@ -142,41 +178,72 @@ def decode_nf4(dev, steps, warmup, M=1):
     }, sample
 
 
+def controls(dev, nbytes, n=64):
+    """Empty-launch floor and a cold streaming read of nbytes, graph-replayed."""
+    lib = ctypes.CDLL(os.path.join(ROOT, "bit_grouped_moe_amd", "libgq_probes.so"))
+    lib.gq_probe_empty.argtypes = [ctypes.c_void_p]
+    lib.gq_probe_stream_read.argtypes = [ctypes.c_void_p, ctypes.c_int64, ctypes.c_void_p,
+                                         ctypes.c_void_p]
+    nb = (nbytes + 15) // 16 * 16
+    nbuf = 40                                          # 40 x 14 MB >> the 256 MB cache
+    bufs = [torch.randint(0, 255, (nb,), dtype=torch.uint8, device=dev) for _ in range(nbuf)]
+    sink = torch.zeros(4, dtype=torch.int32, device=dev)
+
+    def stream(i):
+        st = lib.gq_probe_stream_read(ctypes.c_void_p(bufs[i % nbuf].data_ptr()), nb,
+                                      ctypes.c_void_p(sink.data_ptr()),
+                                      ctypes.c_void_p(torch.cuda.current_stream().cuda_stream))
+        assert st == 0
+
+    def empty(i):
+        assert lib.gq_probe_empty(ctypes.c_void_p(torch.cuda.current_stream().cuda_stream)) == 0
+
+    gs, ge = capture(stream, n), capture(empty, n)
+    gs.replay()
+    ge.replay()
+    us_stream = 1e3 * event_ms(gs.replay) / n
+    us_empty = 1e3 * event_ms(ge.replay) / n
+    return {"empty_launch_us": us_empty, "stream_read_us": us_stream,
+            "stream_read_gbs": nb / (us_stream * 1e-6) / 1e9, "stream_read_bytes": nb}
+
+
 def decode_mx(dev, steps, warmup):
     E, topk = wl.GPTOSS["E"], wl.GPTOSS["topk"]
     (Ng, Kg), (Nd, Kd) = wl.GPTOSS["gate_up"], wl.GPTOSS["down"]
     copies = 8
     banks_g = [wl.random_mxfp4_bank(E, Ng, Kg, dev, seed=20 + c) for c in range(copies)]
     banks_d = [wl.random_mxfp4_bank(E, Nd, Kd, dev, seed=200 + c) for c in range(copies)]
-    n = steps + warmup
     g = wl.rng(wl.CFG_GPTOSS, wl.S_ROUTE)
-    ids = [wl.route_uniform(g, 1, E, topk) for _ in range(n)]
+    ids = [wl.route_uniform(g, 1, E, topk) for _ in range(steps + warmup)]
     ids_g = [torch.from_numpy(i).to(dev) for i in ids]
     ids_d = [torch.from_numpy(i.reshape(-1, 1).copy()).to(dev) for i in ids]
     x = bf16_dev(wl.draw_bf16(wl.rng(wl.CFG_GPTOSS, wl.S_X), (1, Kg)), dev)
     xd = bf16_dev(wl.draw_bf16(wl.rng(wl.CFG_GPTOSS, wl.S_DOWN_IN), (topk, Kd)), dev)
-    tg = Timer()
+    out_g = torch.empty((topk, Ng), dtype=torch.bfloat16, device=dev)
+    out_d = torch.empty((topk, Nd), dtype=torch.bfloat16, device=dev)
 
-    def run(i, timed):
-        bg, sg = banks_g[i % copies]
-        bd, sd = banks_d[i % copies]
-        ev = tg.start() if timed else None
-        gq.gq_mxfp4_grouped_gemv(x, bg, sg, ids_g[i])
-        if timed:
-            tg.stop(ev)
-        gq.gq_mxfp4_grouped_gemv(xd, bd, sd, ids_d[i])
+    def gate(i):
+        b, s = banks_g[i % copies]
+        gq.gq_mxfp4_grouped_gemv(x, b, s, ids_g[i], out=out_g)
 
-    for i in range(warmup):
-        run(i, False)
+    def step(i):
+        gate(i)
+        b, s = banks_d[i % copies]
+        gq.gq_mxfp4_grouped_gemv(xd, b, s, ids_d[i], out=out_d)
+
+    for i in range(steps, steps + warmup):
+        step(i)
+    g_steps, g_gate = capture(step, steps), capture(gate, steps)
+    g_steps.replay()
+    g_gate.replay()
     torch.cuda.synchronize()
     t0 = time.perf_counter()
-    for i in range(warmup, n):
-        run(i, True)
+    g_steps.replay()
     torch.cuda.synchronize()
     dt = time.perf_counter() - t0
+    us = 1e3 * event_ms(g_gate.replay) / steps
     bg = topk * mx_expert_bytes(Ng, Kg) + Kg * 2 + topk * Ng * 2
     bd = topk * mx_expert_bytes(Nd, Kd) + topk * Kd * 2 + topk * Nd * 2
-    us = tg.avg_us()
     return {"workload": "gpt-oss-20b mxfp4 decode gemv M=1 (gate_up [5760,2880] + down "
                         "[2880,2880], E=32, top-4)",
             "ms_per_step": 1e3 * dt / steps, "gbs": (bg + bd) * steps / dt / 1e9,
@@ -186,7 +253,7 @@ def decode_mx(dev, steps, warmup):
 
 def prefill(dev, steps, warmup, fmt):
     """NF4 Qwen3 (M=4096 Zipf top-8) or MXFP4 gpt-oss (M=2048 uniform top-4):
-    route sort + gate_up GEMM + down GEMM per step."""
+    route sort + gate_up GEMM + down GEMM per step (eager; kernels are long)."""
     if fmt == "nf4":
         cfgd, M, cfg = wl.QWEN, 4096, wl.CFG_QWEN_PREFILL
         route = wl.route_zipf(wl.rng(cfg, wl.S_ROUTE), M, cfgd["E"], cfgd["topk"])
@@ -203,7 +270,6 @@ def prefill(dev, steps, warmup, fmt):
     a_g, b_g = bank(E, Ng, Kg, dev, seed=30)
     a_d, b_d = bank(E, Nd, Kd, dev, seed=300)
     ids = torch.from_numpy(route).to(dev)
-    ids_d = ids.reshape(-1, 1).contiguous()
     sc = torch.from_numpy(wl.router_weights(wl.rng(cfg, wl.S_LOGITS), M, topk)).to(dev)
     x = bf16_dev(wl.draw_bf16(wl.rng(cfg, wl.S_X), (M, Kg)), dev)
     xd = bf16_dev(wl.draw_bf16(wl.rng(cfg, wl.S_DOWN_IN), (P, Kd)), dev)
@@ -243,7 +309,6 @@ def prefill(dev, steps, warmup, fmt):
         "gate_up_us": ug, "down_us": ud, "route_sort_us": us,
         "gate_up_tflops": fg / (ug * 1e-6) / 1e12,
         "down_tflops": fd / (ud * 1e-6) / 1e12,
-        "gate_up_flops": fg, "down_flops": fd,
         "expert_rows_max_median_min": [int(counts.max()), float(np.median(counts)),
                                        int(counts.min())],
     }
@@ -309,9 +374,8 @@ def cpu_baseline(sample, budget_s):
     done, total_bytes, elapsed = 0, 0, 0.0
     try:
         for i, ids in enumerate(sample["ids"]):
-            j = i + sample["warmup"]
-            cg, ag = sample["banks_g"][j % COPIES]
-            cd, ad = sample["banks_d"][j % COPIES]
+            cg, ag = sample["banks_g"][i % COPIES]
+            cd, ad = sample["banks_d"][i % COPIES]
             active = sorted(set(ids.reshape(-1).tolist()))
             host = {e: (cg[e].cpu().numpy(), ag[e].cpu().numpy(), cd[e].cpu().numpy(),
                         ad[e].cpu().numpy()) for e in active}          # untimed host copy
@@ -333,7 +397,27 @@ def cpu_baseline(sample, budget_s):
     return {"value": total_bytes / elapsed / 1e9, "unit": "GB/s", "cores": 1, "kind": "oracle",
             "sample": f"{done} of the timed decode steps (M=1, gate_up + down, 8 experts each): "
                       f"NumPy NF4 decode of the active experts + float64 grouped matmul, "
-                      f"{elapsed:.1f} s, BLAS limited to 1 thread"}
+                      f"{elapsed:.1f} s on 1 core (BLAS limited to 1 thread)"}
+
+
+def measured_traffic(kernel_key, bytes_per_launch):
+    """HBM bytes per launch from committed rocprofv3 counter runs, if they were
+    taken on the current kernel source (else None)."""
+    try:
+        with open(TRAFFIC_FILE) as f:
+            rec = json.load(f)[kernel_key]
+    except (OSError, KeyError, ValueError):
+        return None
+    src = os.path.join(ROOT, "bit_grouped_moe_amd", "csrc", rec["source"])
+    digest = hashlib.sha256(open(src, "rb").read()).hexdigest()
+    if digest != rec["source_sha256"]:
+        return None
+    return {"bytes_per_launch": rec["hbm_bytes_per_launch"],
+            "ratio_to_algorithmic": rec["hbm_bytes_per_launch"] / bytes_per_launch}
+
+
+def r4(d):
+    return {k: (round(v, 4) if isinstance(v, float) else v) for k, v in d.items()}
 
 
 def main():
@@ -358,10 +442,12 @@ def main():
 
     log("[bench] nf4 decode M=1")
     dec, sample = decode_nf4(dev, args.steps, args.warmup, M=1)
-    log("[bench]", dec)
+    log("[bench]", r4(dec))
+    ctl = controls(dev, int(dec["gate_up_bytes_per_launch"]))
+    log("[bench] controls", r4(ctl))
     log("[bench] nf4 prefill M=4096")
     pre = prefill(dev, args.prefill_steps, 2, "nf4")
-    log("[bench]", pre)
+    log("[bench]", r4(pre))
     extra = {}
     if not args.quick:
         log("[bench] nf4 decode M=4")
@@ -378,8 +464,7 @@ def main():
         extra["mxfp4_prefill_m2048"] = mp
         log("[bench] nf4 dgrad")
         extra["nf4_dgrad_m2048"] = dgrad(dev, args.prefill_steps, 2)
-    del_extra = {k: {kk: (round(vv, 4) if isinstance(vv, float) else vv) for kk, vv in v.items()}
-                 for k, v in extra.items()}
+    extra = {k: r4(v) for k, v in extra.items()}
 
     log("[bench] cpu baseline (oracle)")
     cpu = cpu_baseline(sample, 3.0 if args.quick else args.cpu_budget)
@@ -398,17 +483,20 @@ def main():
         "dtype": "f32",
         "data": "synthetic",
         "config": {"workload": "qwen3-30b-a3b-shaped nf4 decode gemv, M=1 token, top-8 of "
-                               "E=128, gate_up W[1536,2048] + down W[2048,768], fresh routing "
-                               "and cold bank copy per step",
+                               "E=128, gate_up W[1536,2048] + down W[2048,768], own routing "
+                               "and cold bank copy per step, graph-replayed",
                    "bytes_per_step": round(dec["bytes_per_step"]),
                    "frac_hbm_peak": round(dec["gbs"] / HBM_PEAK_GBS, 4)},
         "roofline": {"bound": "hbm", "achieved": round(dec["gate_up_gbs"], 2),
                      "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                     "frac": round(dec["gate_up_gbs"] / HBM_PEAK_GBS, 4), "traffic": None,
-                     "kernel": "grouped_gemv_kernel<nf4> (gate_up)",
+                     "frac": round(dec["gate_up_gbs"] / HBM_PEAK_GBS, 4),
+                     "traffic": measured_traffic("gemv_nf4_gate_up_m1",
+                                                 dec["gate_up_bytes_per_launch"]),
+                     "kernel": "grouped_gemv_kernel (NF4, gate_up, M=1)",
                      "bytes_per_launch": round(dec["gate_up_bytes_per_launch"]),
-                     "avg_launch_us": round(dec["gate_up_us"], 3)},
-        "cpu_baseline": {k: (round(v, 4) if isinstance(v, float) else v) for k, v in cpu.items()},
+                     "avg_launch_us": round(dec["gate_up_us"], 3),
+                     "controls": r4(ctl)},
+        "cpu_baseline": r4(cpu),
         "prefill": {"workload": "qwen3-30b-a3b-shaped nf4 prefill, M=4096 tokens, top-8 Zipf(1.1) "
                                 "of E=128, router-weight scales: route sort + gate_up GEMM + "
                                 "down GEMM",
@@ -418,13 +506,13 @@ def main():
                                  "peak": BF16_PEAK_TFLOPS, "unit": "TFLOP/s",
                                  "frac": round(pre["gate_up_tflops"] / BF16_PEAK_TFLOPS, 4),
                                  "traffic": None,
-                                 "kernel": "grouped_gemm_kernel<nf4> (gate_up)",
+                                 "kernel": "grouped_gemm_fwd_kernel (NF4, gate_up)",
                                  "avg_launch_us": round(pre["gate_up_us"], 2)},
                     "down_tflops": round(pre["down_tflops"], 2),
                     "down_us": round(pre["down_us"], 2),
                     "route_sort_us": round(pre["route_sort_us"], 2),
                     "expert_rows_max_median_min": pre["expert_rows_max_median_min"]},
-        "extra": del_extra,
+        "extra": extra,
     }
     print(json.dumps(line), flush=True)
 

@@ -1,4 +1,5 @@
-"""Build libgq.so (HIP kernels + C ABI) in-tree for gfx950.
+"""Build libgq.so (HIP kernels + C ABI) and libgq_probes.so (benchmark
+controls) in-tree for gfx950.
 
     python -m bit_grouped_moe_amd.build        # or __graft_entry__.build()
 
@@ -15,6 +16,8 @@ HERE = os.path.dirname(os.path.abspath(__file__))
 CSRC = os.path.join(HERE, "csrc")
 BUILD = os.path.join(HERE, "_build")
 LIB = os.path.join(HERE, "libgq.so")
+PROBE_LIB = os.path.join(HERE, "libgq_probes.so")
+PROBE_SRC = os.path.join(CSRC, "probes", "probes.hip")
 ARCH = "gfx950"
 
 CFLAGS = [
@@ -57,13 +60,18 @@ def build(verbose=False, jobs=8):
 
     with ThreadPoolExecutor(max_workers=jobs) as ex:
         objs = list(ex.map(compile_one, srcs))
-    tmp = LIB + ".tmp"
+    link(hipcc, objs, LIB)
+    link(hipcc, [compile_one(PROBE_SRC)], PROBE_LIB)
+    return LIB
+
+
+def link(hipcc, objs, lib):
+    tmp = lib + ".tmp"
     cmd = [hipcc, "-shared", "-fPIC", f"--offload-arch={ARCH}", *objs, "-o", tmp]
     r = subprocess.run(cmd, capture_output=True, text=True)
     if r.returncode != 0:
         raise RuntimeError(f"link failed:\n{r.stdout}{r.stderr}")
-    os.replace(tmp, LIB)
-    return LIB
+    os.replace(tmp, lib)
 
 
 if __name__ == "__main__":

@@ -102,28 +102,22 @@ __device__ __forceinline__ FwdLoad fwd_load(const GemmArgs& g, int e, int n0, in
   return L;
 }
 
+// Decode one code dword (8 weights, chunk q of the thread's 32) of a forward
+// B tile into Bs[col][h*32 + 8q .. +8].
 template <int kMode>
-__device__ __forceinline__ void fwd_decode_store(const FwdLoad& L, const float* lut, uint16_t* Bs,
-                                                 int tid) {
+__device__ __forceinline__ void fwd_decode_chunk(const FwdLoad& L, int q, const float* lut,
+                                                 uint16_t* Bs, int tid) {
   const int col = tid & (kTN - 1), h = tid >> 7;
-  uint32_t p[16];
+  uint32_t p[4];
   if constexpr (kMode == kFwdMX) {
     const float sc = e8m0_to_f32(L.s);
 #pragma unroll
-    for (int w = 0; w < 4; ++w)
-#pragma unroll
-      for (int b = 0; b < 4; ++b) p[4 * w + b] = e2m1_pair_bf16_scaled(L.c[w], b, sc);
+    for (int b = 0; b < 4; ++b) p[b] = e2m1_pair_bf16_scaled(L.c[q], b, sc);
   } else {
-#pragma unroll
-    for (int w = 0; w < 4; ++w) nf4_decode8_bf16(lut, L.c[w], L.a, &p[4 * w]);
+    nf4_decode8_bf16(lut, L.c[q], L.a, p);
   }
-  if (!L.ok) {
-#pragma unroll
-    for (int i = 0; i < 16; ++i) p[i] = 0u;
-  }
-  u32x4* dst = reinterpret_cast<u32x4*>(Bs + col * kBStride + h * 32);
-#pragma unroll
-  for (int q = 0; q < 4; ++q) dst[q] = u32x4{p[4 * q], p[4 * q + 1], p[4 * q + 2], p[4 * q + 3]};
+  const u32x4 v = L.ok ? u32x4{p[0], p[1], p[2], p[3]} : u32x4{0u, 0u, 0u, 0u};
+  *reinterpret_cast<u32x4*>(Bs + col * kBStride + h * 32 + 8 * q) = v;
 }
 
 // Dgrad: B[k][col] = W[ks*64 + k][k0 + col], i.e. a 64 x 128 block of W
@@ -161,28 +155,39 @@ __device__ __forceinline__ void dg_stage(const DgLoad& L, uint8_t* Cs, float* As
   if (tid < 2 * kTK) As[tid] = L.aok ? L.a : 0.f;         // As[row*2 + block]
 }
 
-__device__ __forceinline__ void dg_decode_store(const uint8_t* Cs, const float* As, const float* lut,
-                                                uint16_t* Bs, int tid) {
-  const int j4 = tid & 31, r8 = tid >> 5;                 // column quad, row octet
-  const int blk = (j4 * 4) >> 6;                          // local absmax block (0 or 1)
-  float w[4][8];                                          // [column][row]
+// Dgrad decode, in four chunks: chunk c writes column 4*j4 + c of the
+// thread's column quad (8 consecutive contraction values, 16 bytes).  The
+// thread's raw codes and absmax are read from LDS once, by chunk 0.
+struct DgCodes {
+  uint32_t two[8];   // bytes j4*2, j4*2+1 of rows r8*8 .. +8
+  float a[8];
+};
+
+__device__ __forceinline__ void dg_read_codes(const uint8_t* Cs, const float* As, int tid,
+                                              DgCodes& R) {
+  const int j4 = tid & 31, r8 = tid >> 5;
+  const int blk = (j4 * 4) >> 6;
 #pragma unroll
   for (int i = 0; i < 8; ++i) {
     const int r = r8 * 8 + i;
-    const uint32_t two = *reinterpret_cast<const uint16_t*>(Cs + r * kCStride + j4 * 2);
-    const float a = As[r * 2 + blk];
-    // bytes j4*2, j4*2+1 hold columns 4*j4 .. 4*j4+3 (high nibble first)
-    w[0][i] = nf4_q_hi(lut, two, 0) * a;
-    w[1][i] = nf4_q_lo(lut, two, 0) * a;
-    w[2][i] = nf4_q_hi(lut, two, 1) * a;
-    w[3][i] = nf4_q_lo(lut, two, 1) * a;
+    R.two[i] = *reinterpret_cast<const uint16_t*>(Cs + r * kCStride + j4 * 2);
+    R.a[i] = As[r * 2 + blk];
   }
+}
+
+__device__ __forceinline__ void dg_decode_chunk(const DgCodes& R, int c, const float* lut,
+                                                uint16_t* Bs, int tid) {
+  const int j4 = tid & 31, r8 = tid >> 5;
+  float w[8];
+  // bytes j4*2, j4*2+1 hold columns 4*j4 .. 4*j4+3 (high nibble first)
 #pragma unroll
-  for (int c = 0; c < 4; ++c) {
-    u32x4 v{pack_bf16x2(w[c][0], w[c][1]), pack_bf16x2(w[c][2], w[c][3]),
-            pack_bf16x2(w[c][4], w[c][5]), pack_bf16x2(w[c][6], w[c][7])};
-    *reinterpret_cast<u32x4*>(Bs + (j4 * 4 + c) * kBStride + r8 * 8) = v;
+  for (int i = 0; i < 8; ++i) {
+    const float qv = (c & 1) ? nf4_q_lo(lut, R.two[i], c >> 1) : nf4_q_hi(lut, R.two[i], c >> 1);
+    w[i] = qv * R.a[i];
   }
+  const u32x4 v{pack_bf16x2(w[0], w[1]), pack_bf16x2(w[2], w[3]), pack_bf16x2(w[4], w[5]),
+                pack_bf16x2(w[6], w[7])};
+  *reinterpret_cast<u32x4*>(Bs + (j4 * 4 + c) * kBStride + r8 * 8) = v;
 }
 
 // ---- the kernel ----
@@ -269,120 +274,148 @@ __device__ __forceinline__ void grouped_gemm_body(const GemmArgs& g) {
   // valid row; the half-step past a K tail re-reads the last valid half and
   // is zeroed just before use), see the note at fwd_load.
   const int a_koff_max = g.Kc - 32 - lh * 32;             // keeps k within the row
-  auto load_a = [&](int ks, u32x4 (&A)[2][4]) {
+  auto load_a_slice = [&](int ks, int sl, u32x4 (&A)[2][4]) {
     const int koff = min(ks * kTK, a_koff_max);
-#pragma unroll
-    for (int sl = 0; sl < 4; ++sl) {
-      A[0][sl] = *reinterpret_cast<const u32x4*>(a0 + koff + sl * 8);
-      A[1][sl] = *reinterpret_cast<const u32x4*>(a1 + koff + sl * 8);
-    }
+    A[0][sl] = *reinterpret_cast<const u32x4*>(a0 + koff + sl * 8);
+    A[1][sl] = *reinterpret_cast<const u32x4*>(a1 + koff + sl * 8);
   };
-  auto zero_tail = [&](int ks, u32x4 (&A)[2][4]) {
-    if (ktail && ks == nsteps - 1 && lh == 1) {
+  auto load_b_slice = [&](const uint16_t* B, int sl, bf16x8 (&b)[4]) {
 #pragma unroll
-      for (int sl = 0; sl < 4; ++sl) A[0][sl] = A[1][sl] = u32x4{0u, 0u, 0u, 0u};
-    }
+    for (int c = 0; c < 4; ++c)
+      b[c] = as_bf16x8(
+          *reinterpret_cast<const u32x4*>(B + (c * 32 + lr) * kBStride + lh * 32 + sl * 8));
   };
-
   // kRows = number of active 32-row sub-tiles of this wave (1 or 2) with all
-  // 128 columns valid: straight-line MFMAs, so the scheduler can interleave
-  // them with the next step's decode.  kRows == 0: generic guarded path.
-  auto mfma_step = [&](auto rows_c, const u32x4 (&A)[2][4], const uint16_t* B) {
+  // 128 columns valid: unguarded MFMAs.  kRows == 0: generic guarded path.
+  auto mfma_slice = [&](auto rows_c, const u32x4 (&A)[2][4], int sl, const bf16x8 (&b)[4]) {
     constexpr int kRows = decltype(rows_c)::value;
 #pragma unroll
-    for (int sl = 0; sl < 4; ++sl) {
-      bf16x8 b[4];
-#pragma unroll
-      for (int c = 0; c < 4; ++c)
-        b[c] = as_bf16x8(
-            *reinterpret_cast<const u32x4*>(B + (c * 32 + lr) * kBStride + lh * 32 + sl * 8));
-#pragma unroll
-      for (int c = 0; c < 4; ++c) {
-        if constexpr (kRows == 0) {
-          if (c * 32 >= ncols) continue;
-          if (act0)
-            acc[0][c] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(A[0][sl]), b[c],
-                                                                acc[0][c], 0, 0, 0);
-          if (act1)
-            acc[1][c] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(A[1][sl]), b[c],
-                                                                acc[1][c], 0, 0, 0);
-        } else {
+    for (int c = 0; c < 4; ++c) {
+      if constexpr (kRows == 0) {
+        if (c * 32 >= ncols) continue;
+        if (act0)
           acc[0][c] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(A[0][sl]), b[c],
                                                               acc[0][c], 0, 0, 0);
-          if constexpr (kRows == 2)
-            acc[1][c] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(A[1][sl]), b[c],
-                                                                acc[1][c], 0, 0, 0);
-        }
+        if (act1)
+          acc[1][c] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(A[1][sl]), b[c],
+                                                              acc[1][c], 0, 0, 0);
+      } else {
+        acc[0][c] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(A[0][sl]), b[c],
+                                                            acc[0][c], 0, 0, 0);
+        if constexpr (kRows == 2)
+          acc[1][c] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(A[1][sl]), b[c],
+                                                              acc[1][c], 0, 0, 0);
       }
     }
   };
 
-  u32x4 A0[2][4], A1[2][4];
+  u32x4 A[2][4];
   FwdLoad F0{}, F1{};
   DgLoad D{};
+  DgCodes R{};
 
-  // ---- prologue: step 0 decoded into Bs[0] ----
-  load_a(0, A0);
+  // ---- prologue: step 0 decoded into Bs[0]; step 1's codes in flight ----
+#pragma unroll
+  for (int sl = 0; sl < 4; ++sl) load_a_slice(0, sl, A);
   if constexpr (kDg) {
     D = dg_load(g, e, n0, 0, tid);
     dg_stage(D, Cs[0], As[0], tid);
     D = dg_load(g, e, n0, min(1, nsteps - 1), tid);
     lds_barrier();
-    dg_decode_store(Cs[0], As[0], lut, Bs[0], tid);
+    dg_read_codes(Cs[0], As[0], tid, R);
+#pragma unroll
+    for (int c = 0; c < 4; ++c) dg_decode_chunk(R, c, lut, Bs[0], tid);
     dg_stage(D, Cs[1], As[1], tid);
     D = dg_load(g, e, n0, min(2, nsteps - 1), tid);
   } else {
     F0 = fwd_load<kMode>(g, e, n0, 0, tid);
     F1 = fwd_load<kMode>(g, e, n0, min(1, nsteps - 1), tid);
-    fwd_decode_store<kMode>(F0, lut, Bs[0], tid);
+#pragma unroll
+    for (int q = 0; q < 4; ++q) fwd_decode_chunk<kMode>(F0, q, lut, Bs[0], tid);
   }
   lds_barrier();
 
-  // ---- main loop (unrolled by two so register sets swap roles, no copies) ----
-  // Prefetches and decodes run unconditionally (step indices clamped to the
-  // last step; the surplus work at the tail writes an LDS buffer nobody reads
-  // again): loads under a branch would make the compiler wait for them early.
+  // ---- main loop: step ks runs its MFMAs slice by slice; between them it
+  // decodes a quarter of step ks+1 into the other LDS buffer and refills the
+  // consumed activation registers with step ks+1.  All prefetches and decodes
+  // are unconditional (indices clamped to the last step): loads under a branch
+  // make the compiler wait for them early.  Unrolled by two so the two code
+  // register sets swap roles without copies. ----
   auto run_loop = [&](auto rows_c) {
-    auto body = [&](int ks, u32x4 (&A_use)[2][4], u32x4 (&A_fill)[2][4], FwdLoad& F_dec,
-                    FwdLoad& F_fill) {
-      const int k1 = min(ks + 1, nsteps - 1), k2 = min(ks + 2, nsteps - 1);
-      load_a(k1, A_fill);
-      if constexpr (kDg) {
-        dg_decode_store(Cs[(ks + 1) & 1], As[(ks + 1) & 1], lut, Bs[(ks + 1) & 1], tid);
-        dg_stage(D, Cs[ks & 1], As[ks & 1], tid);
-        D = dg_load(g, e, n0, min(ks + 3, nsteps - 1), tid);
-      } else {
-        F_fill = fwd_load<kMode>(g, e, n0, k2, tid);
-        fwd_decode_store<kMode>(F_dec, lut, Bs[(ks + 1) & 1], tid);
+    auto step = [&](int ks, FwdLoad& F_dec, FwdLoad& F_fill) {
+      const int k1 = min(ks + 1, nsteps - 1);
+      const uint16_t* B = Bs[ks & 1];
+      uint16_t* Bn = Bs[(ks + 1) & 1];
+      if constexpr (!kDg) F_fill = fwd_load<kMode>(g, e, n0, min(ks + 2, nsteps - 1), tid);
+      if constexpr (kMode == kFwdMX) {                     // K tail: zero the missing half
+        if (ktail && ks == nsteps - 1 && lh == 1) {
+#pragma unroll
+          for (int sl = 0; sl < 4; ++sl) A[0][sl] = A[1][sl] = u32x4{0u, 0u, 0u, 0u};
+        }
       }
-      zero_tail(ks, A_use);
-      mfma_step(rows_c, A_use, Bs[ks & 1]);
+      bf16x8 b_cur[4], b_nxt[4];
+      load_b_slice(B, 0, b_cur);
+#pragma unroll
+      for (int sl = 0; sl < 4; ++sl) {
+        if (sl < 3) load_b_slice(B, sl + 1, b_nxt);
+        if constexpr (kDg) {
+          if (sl == 0) dg_read_codes(Cs[(ks + 1) & 1], As[(ks + 1) & 1], tid, R);
+          dg_decode_chunk(R, sl, lut, Bn, tid);
+          if (sl == 3) {                                   // codes of step ks+2, then ks+3
+            dg_stage(D, Cs[ks & 1], As[ks & 1], tid);
+            D = dg_load(g, e, n0, min(ks + 3, nsteps - 1), tid);
+          }
+        } else {
+          fwd_decode_chunk<kMode>(F_dec, sl, lut, Bn, tid);
+        }
+        mfma_slice(rows_c, A, sl, b_cur);
+        load_a_slice(k1, sl, A);
+        if (sl < 3) {
+#pragma unroll
+          for (int c = 0; c < 4; ++c) b_cur[c] = b_nxt[c];
+        }
+      }
       lds_barrier();
     };
     for (int ks = 0; ks < nsteps; ks += 2) {
-      body(ks, A0, A1, F1, F0);
-      if (ks + 1 < nsteps) body(ks + 1, A1, A0, F0, F1);
+      step(ks, F1, F0);
+      if (ks + 1 < nsteps) step(ks + 1, F0, F1);
     }
   };
   if (ncols == kTN && act1) run_loop(std::integral_constant<int, 2>{});
   else if (ncols == kTN && act0) run_loop(std::integral_constant<int, 1>{});
   else run_loop(std::integral_constant<int, 0>{});
 
-  // ---- epilogue: scale, round to bf16, scatter rows to their pairs ----
+  // ---- epilogue: scale, round to bf16, stage each 32-row sub-tile in LDS
+  // (the B buffers are free now), then write whole output rows with 16-byte
+  // stores instead of scattered 2-byte ones. ----
+  constexpr int kOStride = kTN + 8;                         // padded row: conflict-free
+  static_assert(4 * 32 * kOStride <= 2 * kTN * kBStride, "staging must fit in Bs");
+  lds_barrier();
+  uint16_t* stage = &Bs[0][0] + wave * (32 * kOStride);
 #pragma unroll
   for (int j = 0; j < 2; ++j) {
     const int ms = j ? ms1 : ms0;
     if (!(j ? act1 : act0)) continue;
 #pragma unroll
     for (int r = 0; r < 16; ++r) {
-      const int m = ms * 32 + (r >> 2) * 8 + lh * 4 + (r & 3);
-      if (m >= valid) continue;
-      const int p = pair_s[m];
-      const float sc = g.pair_scale ? g.pair_scale[p] : 1.f;
-      uint16_t* orow = g.out + (int64_t)p * g.Nout + n0 + lr;
+      const int rr = (r >> 2) * 8 + lh * 4 + (r & 3);
+      const int m = ms * 32 + rr;
+      const float sc = (g.pair_scale && m < valid) ? g.pair_scale[pair_s[m]] : 1.f;
 #pragma unroll
       for (int c = 0; c < 4; ++c)
-        if (c * 32 < ncols) orow[c * 32] = f32_to_bf16_bits(acc[j][c][r] * sc);
+        stage[rr * kOStride + c * 32 + lr] = f32_to_bf16_bits(acc[j][c][r] * sc);
+    }
+    // a wave's LDS operations complete in order: no barrier needed to read back
+#pragma unroll
+    for (int it = 0; it < 8; ++it) {
+      const int chunk = it * 64 + lane;                   // 32 rows x 16 chunks of 8 bf16
+      const int rr = chunk >> 4, c8 = chunk & 15;
+      const int m = ms * 32 + rr;
+      if (m < valid && c8 * 8 < ncols) {
+        const u32x4 v = *reinterpret_cast<const u32x4*>(stage + rr * kOStride + c8 * 8);
+        *reinterpret_cast<u32x4*>(g.out + (int64_t)pair_s[m] * g.Nout + n0 + c8 * 8) = v;
+      }
     }
   }
 }

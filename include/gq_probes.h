@@ -1,0 +1,37 @@
+/*
+ * gq_probes.h -- measurement controls for the benchmark (libgq_probes.so).
+ * Not part of the matmul path.  They give the same-run reference points a
+ * kernel's time is read against: the device duration of an empty launch
+ * (the per-launch floor) and a plain coalesced streaming read of a given
+ * byte count (the achievable HBM rate at that size).  The pages recommend
+ * pairing every measurement with controls taken on the same instance
+ * ("Receipts-driven engineering", "What the discipline caught": baselines
+ * differ between hosts, so ratios are taken on one machine).
+ *
+ * Pointers are device memory owned by the caller; work is enqueued on
+ * `stream`.  Return 0, hipErrorInvalidValue for bad arguments, or the launch
+ * error.
+ */
+#ifndef GQ_PROBES_H
+#define GQ_PROBES_H
+
+#include <stdint.h>
+#include <hip/hip_runtime_api.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+/* One workgroup that does nothing. */
+int gq_probe_empty(hipStream_t stream);
+
+/* Reads `bytes` bytes (a multiple of 16, buffer 16-byte aligned) once with
+ * 16-byte coalesced loads, 16 per thread, all issued before use; writes
+ * nothing unless the xor of everything read equals 0x9E3779B9, in which
+ * case one word goes to sink[0] (sink: >= 4 bytes). */
+int gq_probe_stream_read(const void* buf, int64_t bytes, uint32_t* sink, hipStream_t stream);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* GQ_PROBES_H */
