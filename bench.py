@@ -32,7 +32,6 @@ All inputs are synthetic and resident in HBM before timing starts.
 
 import argparse
 import ctypes
-import hashlib
 import json
 import os
 import sys
@@ -184,6 +183,8 @@ def controls(dev, nbytes, n=64):
     lib.gq_probe_empty.argtypes = [ctypes.c_void_p]
     lib.gq_probe_stream_read.argtypes = [ctypes.c_void_p, ctypes.c_int64, ctypes.c_void_p,
                                          ctypes.c_void_p]
+    lib.gq_probe_copy.argtypes = [ctypes.c_void_p, ctypes.c_void_p, ctypes.c_int64,
+                                  ctypes.c_void_p]
     nb = (nbytes + 15) // 16 * 16
     nbuf = 40                                          # 40 x 14 MB >> the 256 MB cache
     bufs = [torch.randint(0, 255, (nb,), dtype=torch.uint8, device=dev) for _ in range(nbuf)]
@@ -198,13 +199,24 @@ def controls(dev, nbytes, n=64):
     def empty(i):
         assert lib.gq_probe_empty(ctypes.c_void_p(torch.cuda.current_stream().cuda_stream)) == 0
 
-    gs, ge = capture(stream, n), capture(empty, n)
+    dst = torch.empty(nb, dtype=torch.uint8, device=dev)
+
+    def copy(i):
+        st = lib.gq_probe_copy(ctypes.c_void_p(bufs[i % nbuf].data_ptr()),
+                               ctypes.c_void_p(dst.data_ptr()), nb,
+                               ctypes.c_void_p(torch.cuda.current_stream().cuda_stream))
+        assert st == 0
+
+    gs, ge, gc = capture(stream, n), capture(empty, n), capture(copy, n)
     gs.replay()
     ge.replay()
+    gc.replay()
     us_stream = 1e3 * event_ms(gs.replay) / n
     us_empty = 1e3 * event_ms(ge.replay) / n
+    us_copy = 1e3 * event_ms(gc.replay) / n
     return {"empty_launch_us": us_empty, "stream_read_us": us_stream,
-            "stream_read_gbs": nb / (us_stream * 1e-6) / 1e9, "stream_read_bytes": nb}
+            "stream_read_gbs": nb / (us_stream * 1e-6) / 1e9, "stream_read_bytes": nb,
+            "copy_us": us_copy, "copy_gbs": 2 * nb / (us_copy * 1e-6) / 1e9}
 
 
 def decode_mx(dev, steps, warmup):
@@ -303,7 +315,9 @@ def prefill(dev, steps, warmup, fmt):
     fg, fd = 2.0 * P * Ng * Kg, 2.0 * P * Nd * Kd
     ug, ud, us = tg.avg_us(), td.avg_us(), ts.avg_us()
     counts = np.bincount(route.reshape(-1), minlength=E)
+    eb = nf4_expert_bytes(Ng, Kg) if fmt == "nf4" else mx_expert_bytes(Ng, Kg)
     return {
+        "gate_up_bytes": int((counts > 0).sum()) * eb + M * Kg * 2 + P * Ng * 2,
         "ms_per_step": 1e3 * dt / steps,
         "tflops": (fg + fd) * steps / dt / 1e12,
         "gate_up_us": ug, "down_us": ud, "route_sort_us": us,
@@ -400,20 +414,24 @@ def cpu_baseline(sample, budget_s):
                       f"{elapsed:.1f} s on 1 core (BLAS limited to 1 thread)"}
 
 
-def measured_traffic(kernel_key, bytes_per_launch):
+def measured_traffic(kernel_key, algorithmic):
     """HBM bytes per launch from committed rocprofv3 counter runs, if they were
-    taken on the current kernel source (else None)."""
+    taken on the current kernel sources (else None)."""
+    from bit_grouped_moe_amd.profile_summary import sources_sha
     try:
         with open(TRAFFIC_FILE) as f:
             rec = json.load(f)[kernel_key]
     except (OSError, KeyError, ValueError):
         return None
-    src = os.path.join(ROOT, "bit_grouped_moe_amd", "csrc", rec["source"])
-    digest = hashlib.sha256(open(src, "rb").read()).hexdigest()
-    if digest != rec["source_sha256"]:
+    if sources_sha(kernel_key) != rec["source_sha256"]:
         return None
-    return {"bytes_per_launch": rec["hbm_bytes_per_launch"],
-            "ratio_to_algorithmic": rec["hbm_bytes_per_launch"] / bytes_per_launch}
+    return {"bytes_per_launch": round(rec["hbm_bytes_per_launch"]),
+            "read_bytes": round(rec["fetch_bytes"]), "written_bytes": round(rec["write_bytes"]),
+            "ratio_to_algorithmic": round(rec["hbm_bytes_per_launch"] / algorithmic, 4)}
+
+
+def traffic_bytes(t):
+    return None if t is None else t["bytes_per_launch"]
 
 
 def r4(d):
@@ -469,6 +487,8 @@ def main():
     log("[bench] cpu baseline (oracle)")
     cpu = cpu_baseline(sample, 3.0 if args.quick else args.cpu_budget)
 
+    gemv_traffic = measured_traffic("gemv_nf4_gate_up_m1", dec["gate_up_bytes_per_launch"])
+    gemm_traffic = measured_traffic("gemm_nf4_gate_up_prefill", pre["gate_up_bytes"])
     line = {
         "metric": "decode GB/s (% HBM peak) @1 tok; prefill TFLOP/s (% MFMA peak) @4096 tok",
         "value": round(dec["gbs"], 2),
@@ -490,8 +510,8 @@ def main():
         "roofline": {"bound": "hbm", "achieved": round(dec["gate_up_gbs"], 2),
                      "peak": HBM_PEAK_GBS, "unit": "GB/s",
                      "frac": round(dec["gate_up_gbs"] / HBM_PEAK_GBS, 4),
-                     "traffic": measured_traffic("gemv_nf4_gate_up_m1",
-                                                 dec["gate_up_bytes_per_launch"]),
+                     "traffic": traffic_bytes(gemv_traffic),
+                     "traffic_detail": gemv_traffic,
                      "kernel": "grouped_gemv_kernel (NF4, gate_up, M=1)",
                      "bytes_per_launch": round(dec["gate_up_bytes_per_launch"]),
                      "avg_launch_us": round(dec["gate_up_us"], 3),
@@ -505,7 +525,8 @@ def main():
                     "roofline": {"bound": "mfma", "achieved": round(pre["gate_up_tflops"], 2),
                                  "peak": BF16_PEAK_TFLOPS, "unit": "TFLOP/s",
                                  "frac": round(pre["gate_up_tflops"] / BF16_PEAK_TFLOPS, 4),
-                                 "traffic": None,
+                                 "traffic": traffic_bytes(gemm_traffic),
+                                 "traffic_detail": gemm_traffic,
                                  "kernel": "grouped_gemm_fwd_kernel (NF4, gate_up)",
                                  "avg_launch_us": round(pre["gate_up_us"], 2)},
                     "down_tflops": round(pre["down_tflops"], 2),

@@ -30,7 +30,25 @@ __global__ __launch_bounds__(kThreads) void stream_read_kernel(const u32x4* __re
   if (r == 0x9E3779B9u) sink[0] = r;
 }
 
+__global__ __launch_bounds__(kThreads) void copy_kernel(const u32x4* __restrict__ src,
+                                                        u32x4* __restrict__ dst, int64_t n16) {
+  const int64_t i = (int64_t)blockIdx.x * kThreads + threadIdx.x;
+  if (i < n16) dst[i] = src[i];
+}
+
 }  // namespace
+
+extern "C" int gq_probe_copy(const void* src, void* dst, int64_t bytes, hipStream_t stream) {
+  if (!src || !dst || bytes <= 0 || bytes % 16 || (reinterpret_cast<uintptr_t>(src) & 15u) ||
+      (reinterpret_cast<uintptr_t>(dst) & 15u))
+    return (int)hipErrorInvalidValue;
+  const int64_t n16 = bytes / 16;
+  const int64_t blocks = (n16 + kThreads - 1) / kThreads;
+  if (blocks > INT32_MAX) return (int)hipErrorInvalidValue;
+  hipLaunchKernelGGL(copy_kernel, dim3((unsigned)blocks), dim3(kThreads), 0, stream,
+                     static_cast<const u32x4*>(src), static_cast<u32x4*>(dst), n16);
+  return (int)hipGetLastError();
+}
 
 extern "C" int gq_probe_empty(hipStream_t stream) {
   hipLaunchKernelGGL(empty_kernel, dim3(1), dim3(64), 0, stream);

@@ -31,6 +31,11 @@ int gq_probe_empty(hipStream_t stream);
  * case one word goes to sink[0] (sink: >= 4 bytes). */
 int gq_probe_stream_read(const void* buf, int64_t bytes, uint32_t* sink, hipStream_t stream);
 
+/* Copies `bytes` bytes (a multiple of 16, both buffers 16-byte aligned, not
+ * overlapping) with 16-byte coalesced loads and stores: a kernel of known
+ * read and write size, the reference that scales HBM byte counters. */
+int gq_probe_copy(const void* src, void* dst, int64_t bytes, hipStream_t stream);
+
 #ifdef __cplusplus
 }
 #endif

@@ -145,3 +145,24 @@ def test_missing_library_raises(monkeypatch, tmp_path):
     monkeypatch.setenv("GQ_LIBRARY", str(tmp_path / "nope.so"))
     with pytest.raises(gq.GQError):
         gq.load_library()
+
+
+def test_probe_library_exports_its_header():
+    """libgq_probes.so (the bench's control kernels) exports what
+    include/gq_probes.h declares and rejects bad copy arguments on the host."""
+    path = os.path.join(ROOT, "bit_grouped_moe_amd", "libgq_probes.so")
+    if not os.path.exists(path):
+        pytest.fail("libgq_probes.so is not built")
+    text = open(os.path.join(ROOT, "include", "gq_probes.h")).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    names = sorted(set(re.findall(r"\b(gq_probe_[a-z0-9_]+)\s*\(", text)))
+    plib = ctypes.CDLL(path)
+    assert names == ["gq_probe_copy", "gq_probe_empty", "gq_probe_stream_read"]
+    for n in names:
+        assert hasattr(plib, n), n
+    plib.gq_probe_copy.argtypes = [ctypes.c_void_p, ctypes.c_void_p, ctypes.c_int64,
+                                   ctypes.c_void_p]
+    assert plib.gq_probe_copy(F, F, 24, None) == INVALID          # not a multiple of 16
+    assert plib.gq_probe_copy(F2, F, 16, None) == INVALID         # misaligned source
+    assert plib.gq_probe_copy(NULL, F, 16, None) == INVALID
+    assert plib.gq_probe_copy(F, F, 0, None) == INVALID
