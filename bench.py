@@ -25,8 +25,8 @@ The same line carries
   * ``prefill``: Qwen3 NF4 prefill (M = 4096, Zipf(1.1) top-8, router
     weights) -- route sort + gate_up GEMM + down GEMM -- in TFLOP/s against
     the dense bf16 MFMA peak;
-  * ``extra``: MXFP4 gpt-oss-20b decode (M = 1) and prefill (M = 2048), NF4
-    dgrad (M = 2048, top-8) and the NF4 M = 4 decode.
+  * ``extra``: MXFP4 gpt-oss-20b decode (M = 1), prefill (M = 2048) and dgrad
+    (M = 2048, top-4), NF4 dgrad (M = 2048, top-8) and the NF4 M = 4 decode.
 All inputs are synthetic and resident in HBM before timing starts.
 """
 
@@ -328,27 +328,33 @@ def prefill(dev, steps, warmup, fmt):
     }
 
 
-def dgrad(dev, steps, warmup):
-    E, topk = wl.QWEN["E"], wl.QWEN["topk"]
-    (Ng, Kg), (Nd, Kd) = wl.QWEN["gate_up"], wl.QWEN["down"]
+def dgrad(dev, steps, warmup, fmt="nf4"):
+    """Input gradient of both projections: Qwen3 NF4 (M=2048 top-8) or
+    gpt-oss MXFP4 (M=2048 top-4), eager with per-launch events."""
+    if fmt == "nf4":
+        cfgd, cfg, bank, fn = wl.QWEN, wl.CFG_QWEN_DGRAD, wl.random_nf4_bank, gq.gq_nf4_grouped_dgrad
+    else:
+        cfgd, cfg, bank, fn = wl.GPTOSS, wl.CFG_GPTOSS, wl.random_mxfp4_bank, gq.gq_mxfp4_grouped_dgrad
+    E, topk = cfgd["E"], cfgd["topk"]
+    (Ng, Kg), (Nd, Kd) = cfgd["gate_up"], cfgd["down"]
     M = 2048
     P = M * topk
-    pe = wl.route_uniform(wl.rng(wl.CFG_QWEN_DGRAD, wl.S_ROUTE), M, E, topk).reshape(-1, 1)
+    pe = wl.route_uniform(wl.rng(cfg, wl.S_ROUTE), M, E, topk).reshape(-1, 1)
     ids = torch.from_numpy(pe.copy()).to(dev)
-    cg, ag = wl.random_nf4_bank(E, Ng, Kg, dev, seed=40)
-    cd, ad = wl.random_nf4_bank(E, Nd, Kd, dev, seed=400)
-    dyg = bf16_dev(wl.draw_bf16(wl.rng(wl.CFG_QWEN_DGRAD, wl.S_DOWN_IN), (P, Ng)), dev)
-    dyd = bf16_dev(wl.draw_bf16(wl.rng(wl.CFG_QWEN_DGRAD, wl.S_X), (P, Nd)), dev)
+    cg, ag = bank(E, Ng, Kg, dev, seed=40)
+    cd, ad = bank(E, Nd, Kd, dev, seed=400)
+    dyg = bf16_dev(wl.draw_bf16(wl.rng(cfg, wl.S_DOWN_IN), (P, Ng)), dev)
+    dyd = bf16_dev(wl.draw_bf16(wl.rng(cfg, wl.S_X), (P, Nd)), dev)
     tg, td = Timer(), Timer()
 
     def run(timed):
         r = gq.gq_route_sort(ids, E)
         ev = tg.start() if timed else None
-        gq.gq_nf4_grouped_dgrad(dyg, cg, ag, r)
+        fn(dyg, cg, ag, r)
         if timed:
             tg.stop(ev)
             ev = td.start()
-        gq.gq_nf4_grouped_dgrad(dyd, cd, ad, r)
+        fn(dyd, cd, ad, r)
         if timed:
             td.stop(ev)
 
@@ -362,7 +368,9 @@ def dgrad(dev, steps, warmup):
     dt = time.perf_counter() - t0
     fg, fd = 2.0 * P * Ng * Kg, 2.0 * P * Nd * Kd
     ug, ud = tg.avg_us(), td.avg_us()
-    return {"workload": "qwen3-30b-a3b nf4 dgrad M=2048 top-8 (16384 pairs)",
+    name = ("qwen3-30b-a3b nf4 dgrad M=2048 top-8 (16384 pairs)" if fmt == "nf4" else
+            "gpt-oss-20b mxfp4 dgrad M=2048 top-4 (8192 pairs)")
+    return {"workload": name,
             "ms_per_step": 1e3 * dt / steps, "tflops": (fg + fd) * steps / dt / 1e12,
             "gate_up_us": ug, "down_us": ud,
             "gate_up_tflops": fg / (ug * 1e-6) / 1e12, "down_tflops": fd / (ud * 1e-6) / 1e12}
@@ -482,6 +490,8 @@ def main():
         extra["mxfp4_prefill_m2048"] = mp
         log("[bench] nf4 dgrad")
         extra["nf4_dgrad_m2048"] = dgrad(dev, args.prefill_steps, 2)
+        log("[bench] mxfp4 dgrad")
+        extra["mxfp4_dgrad_m2048"] = dgrad(dev, args.prefill_steps, 2, "mx")
     extra = {k: r4(v) for k, v in extra.items()}
 
     log("[bench] cpu baseline (oracle)")

@@ -20,7 +20,7 @@ __all__ = [
     "GQError", "load_library", "library_path", "EXPORTED_SYMBOLS", "TILE_M",
     "gq_route_max_tiles", "gq_route_sort", "gq_nf4_decode", "gq_mxfp4_decode",
     "gq_nf4_grouped_gemv", "gq_mxfp4_grouped_gemv", "gq_nf4_grouped_gemm",
-    "gq_mxfp4_grouped_gemm", "gq_nf4_grouped_dgrad", "Route",
+    "gq_mxfp4_grouped_gemm", "gq_nf4_grouped_dgrad", "gq_mxfp4_grouped_dgrad", "Route",
 ]
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
@@ -29,7 +29,7 @@ TILE_M = 256                       # the tile height the grouped GEMM kernels us
 EXPORTED_SYMBOLS = (
     "gq_status_string", "gq_route_max_tiles", "gq_route_sort", "gq_nf4_decode",
     "gq_mxfp4_decode", "gq_nf4_grouped_gemv", "gq_mxfp4_grouped_gemv", "gq_nf4_grouped_gemm",
-    "gq_mxfp4_grouped_gemm", "gq_nf4_grouped_dgrad",
+    "gq_mxfp4_grouped_gemm", "gq_nf4_grouped_dgrad", "gq_mxfp4_grouped_dgrad",
 )
 
 _i32, _i64, _p = ctypes.c_int32, ctypes.c_int64, ctypes.c_void_p
@@ -49,6 +49,8 @@ _SIGNATURES = {
                                              _p, _p, _p, _p, _i32, _i32, _p, _p]),
     "gq_nf4_grouped_dgrad": (ctypes.c_int, [_p, _i32, _i32, _i64, _p, _p, _i32, _i32, _p, _p,
                                             _p, _p, _i32, _i32, _p, _p]),
+    "gq_mxfp4_grouped_dgrad": (ctypes.c_int, [_p, _i32, _i32, _i64, _p, _p, _i32, _i32, _p, _p,
+                                              _p, _p, _i32, _i32, _p, _p]),
 }
 
 _lib = None
@@ -308,4 +310,18 @@ def gq_nf4_grouped_dgrad(dy, codes, absmax, route, out=None):
     st = lib.gq_nf4_grouped_dgrad(_ptr(dy), P, N, ds, _ptr(codes), _ptr(absmax), E, K,
                                   *_route_ptrs(route), _ptr(out), _stream(dy))
     _check(st, "gq_nf4_grouped_dgrad")
+    return out
+
+
+def gq_mxfp4_grouped_dgrad(dy, blocks, scales, route, out=None):
+    """dX = dY . W per pair through MXFP4 experts; ``route`` from gq_route_sort(pair ids [P, 1])."""
+    lib = load_library()
+    P, N, ds = _x_args(dy, "dy")
+    E, Nw, K = _mx_bank(blocks, scales)
+    if Nw != N or route.rows * route.topk != P or route.topk != 1 or route.num_experts != E:
+        raise ValueError("dy, blocks and route disagree (route must be built with topk = 1)")
+    out = _out(out, P, K, dy.device)
+    st = lib.gq_mxfp4_grouped_dgrad(_ptr(dy), P, N, ds, _ptr(blocks), _ptr(scales), E, K,
+                                    *_route_ptrs(route), _ptr(out), _stream(dy))
+    _check(st, "gq_mxfp4_grouped_dgrad")
     return out

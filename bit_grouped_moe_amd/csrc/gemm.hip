@@ -1,5 +1,5 @@
-// Prefill grouped GEMM on 4-bit packed experts (NF4, MXFP4) and the NF4
-// input gradient, on gfx950 bf16 matrix cores.
+// Prefill grouped GEMM on 4-bit packed experts (NF4, MXFP4) and their
+// input gradients, on gfx950 bf16 matrix cores.
 //
 // Pages: "grouped-nf4-gemm 0.43.0" -- page header (one GPU launch for the
 // active experts, no full-size bf16 weight copies) and "Which entry point?"
@@ -44,7 +44,7 @@ constexpr int kGemmThreads = 256;
 constexpr int kBStride = 72;      // bf16 per LDS row of B (64 + 8 pad: conflict-free 16-B reads)
 constexpr int kCStride = 80;      // bytes per LDS row of raw codes (dgrad staging)
 
-enum BMode { kFwdNF4 = 0, kFwdMX = 1, kDgradNF4 = 2 };
+enum BMode { kFwdNF4 = 0, kFwdMX = 1, kDgradNF4 = 2, kDgradMX = 3 };
 
 struct GemmArgs {
   const uint16_t* x;           // activations (forward) or output gradient (dgrad)
@@ -124,13 +124,25 @@ __device__ __forceinline__ void fwd_decode_chunk(const FwdLoad& L, int q, const 
 // consumed transposed.  Raw codes (64 rows x 64 bytes) are staged in LDS,
 // then thread t decodes rows 8*(t/32) .. +8 of the column quad 4*(t%32) ..
 // +4 and writes four 16-byte runs of 8 consecutive contraction values.
+// The 128 columns span 2 NF4 absmax blocks or 4 MXFP4 scale blocks per row;
+// their factors are staged as float ([64 rows][kBlk]).
+template <int kMode>
+struct DgFmt {
+  static constexpr bool kMx = kMode == kDgradMX;
+  static constexpr int kBlkK = kMx ? 32 : 64;             // weights per scale block
+  static constexpr int kBlk = kTN / kBlkK;                 // scale blocks per tile row
+};
+
 struct DgLoad {
   u32x4 c;
-  float a;      // absmax of (row t/2, block t%2) for t < 128
+  float a;      // NF4 absmax of (row t/kBlk, block t%kBlk), t < 64*kBlk
+  uint32_t s;   // MXFP4 scale byte of the same
   bool ok, aok;
 };
 
+template <int kMode>
 __device__ __forceinline__ DgLoad dg_load(const GemmArgs& g, int e, int k0, int ks, int tid) {
+  using F = DgFmt<kMode>;
   DgLoad L;
   const int r = tid >> 2, q = tid & 3;                    // row in step, 16-byte quarter
   const int n = ks * kTK + r;                             // W row (< Nw since Nw % 64 == 0)
@@ -139,20 +151,34 @@ __device__ __forceinline__ DgLoad dg_load(const GemmArgs& g, int e, int k0, int 
   const size_t row = (size_t)e * g.Nw + n;
   L.c = *reinterpret_cast<const u32x4*>(g.codes + row * (size_t)(g.Kw / 2) +
                                         min(kb, g.Kw - 32) / 2);
-  // absmax of (row t/2, block t%2) for t < 128 (other threads: a harmless reload)
-  const int t = tid & (2 * kTK - 1);
-  const int ar = t >> 1, ablk = (k0 >> 6) + (t & 1);
-  L.aok = ablk < g.Kw / 64;
-  const size_t arow = (size_t)e * g.Nw + ks * kTK + ar;
-  L.a = static_cast<const float*>(g.scl)[arow * (size_t)(g.Kw / 64) + min(ablk, g.Kw / 64 - 1)];
+  // scale of (row t/kBlk, block t%kBlk); threads past 64*kBlk reload a valid one
+  const int t = tid & (F::kBlk * kTK - 1);
+  const int ar = t / F::kBlk, ablk = k0 / F::kBlkK + t % F::kBlk;
+  const int nblk = g.Kw / F::kBlkK;
+  L.aok = ablk < nblk;
+  const size_t aidx = ((size_t)e * g.Nw + ks * kTK + ar) * (size_t)nblk + min(ablk, nblk - 1);
+  if constexpr (F::kMx) {
+    L.s = (uint32_t)static_cast<const uint8_t*>(g.scl)[aidx];
+    L.a = 0.f;
+  } else {
+    L.a = static_cast<const float*>(g.scl)[aidx];
+    L.s = 0u;
+  }
   return L;
 }
 
+template <int kMode>
 __device__ __forceinline__ void dg_stage(const DgLoad& L, uint8_t* Cs, float* As, int tid) {
-  // Cs: 64 rows x kCStride bytes of raw codes; As: [64 rows][2 blocks] absmax
+  using F = DgFmt<kMode>;
+  // Cs: 64 rows x kCStride bytes of raw codes; As: [64 rows][kBlk] factors
   const int r = tid >> 2, q = tid & 3;
   *reinterpret_cast<u32x4*>(Cs + r * kCStride + q * 16) = L.ok ? L.c : u32x4{0u, 0u, 0u, 0u};
-  if (tid < 2 * kTK) As[tid] = L.aok ? L.a : 0.f;         // As[row*2 + block]
+  if (tid < F::kBlk * kTK) {
+    float f;
+    if constexpr (F::kMx) f = e8m0_to_f32(L.s);
+    else f = L.a;
+    As[tid] = L.aok ? f : 0.f;
+  }
 }
 
 // Dgrad decode, in four chunks: chunk c writes column 4*j4 + c of the
@@ -163,26 +189,34 @@ struct DgCodes {
   float a[8];
 };
 
+template <int kMode>
 __device__ __forceinline__ void dg_read_codes(const uint8_t* Cs, const float* As, int tid,
                                               DgCodes& R) {
+  using F = DgFmt<kMode>;
   const int j4 = tid & 31, r8 = tid >> 5;
-  const int blk = (j4 * 4) >> 6;
+  const int blk = (j4 * 4) / F::kBlkK;
 #pragma unroll
   for (int i = 0; i < 8; ++i) {
     const int r = r8 * 8 + i;
     R.two[i] = *reinterpret_cast<const uint16_t*>(Cs + r * kCStride + j4 * 2);
-    R.a[i] = As[r * 2 + blk];
+    R.a[i] = As[r * F::kBlk + blk];
   }
 }
 
+// The LUT holds the NF4 codebook or the e2m1 values; weight = value * factor
+// in float32 (exact for e2m1 times a power of two), then bf16 RNE.
+template <int kMode>
 __device__ __forceinline__ void dg_decode_chunk(const DgCodes& R, int c, const float* lut,
                                                 uint16_t* Bs, int tid) {
   const int j4 = tid & 31, r8 = tid >> 5;
   float w[8];
-  // bytes j4*2, j4*2+1 hold columns 4*j4 .. 4*j4+3 (high nibble first)
+  // bytes j4*2, j4*2+1 hold columns 4*j4 .. 4*j4+3; element 2j sits in the
+  // high nibble (NF4) or the low nibble (MXFP4) of byte j
+  constexpr bool kLowFirst = DgFmt<kMode>::kMx;
 #pragma unroll
   for (int i = 0; i < 8; ++i) {
-    const float qv = (c & 1) ? nf4_q_lo(lut, R.two[i], c >> 1) : nf4_q_hi(lut, R.two[i], c >> 1);
+    const bool lo = ((c & 1) != 0) != kLowFirst;
+    const float qv = lo ? nf4_q_lo(lut, R.two[i], c >> 1) : nf4_q_hi(lut, R.two[i], c >> 1);
     w[i] = qv * R.a[i];
   }
   const u32x4 v{pack_bf16x2(w[0], w[1]), pack_bf16x2(w[2], w[3]), pack_bf16x2(w[4], w[5]),
@@ -200,10 +234,10 @@ __device__ __forceinline__ void dg_decode_chunk(const DgCodes& R, int c, const f
 // through LDS first (transposed consumption), one step further ahead.
 template <int kMode>
 __device__ __forceinline__ void grouped_gemm_body(const GemmArgs& g) {
-  constexpr bool kDg = kMode == kDgradNF4;
+  constexpr bool kDg = kMode == kDgradNF4 || kMode == kDgradMX;
   __shared__ __attribute__((aligned(16))) uint16_t Bs[2][kTN * kBStride];
   __shared__ __attribute__((aligned(16))) uint8_t Cs[kDg ? 2 : 1][kDg ? kTK * kCStride : 16];
-  __shared__ float As[kDg ? 2 : 1][kDg ? 2 * kTK : 1];
+  __shared__ float As[kDg ? 2 : 1][kDg ? DgFmt<kMode>::kBlk * kTK : 1];
   __shared__ int pair_s[kTM];
   __shared__ int row_s[kTM];
   __shared__ float lut[16];
@@ -249,7 +283,8 @@ __device__ __forceinline__ void grouped_gemm_body(const GemmArgs& g) {
     pair_s[r] = p;
     row_s[r] = kDg ? p : p / g.topk;
   }
-  if constexpr (kMode != kFwdMX) nf4_lut_init(lut, tid);
+  if constexpr (kMode == kDgradMX) e2m1_lut_init(lut, tid);
+  else if constexpr (kMode != kFwdMX) nf4_lut_init(lut, tid);
   lds_barrier();
 
   const int wave = tid >> 6, lane = tid & 63;
@@ -318,15 +353,15 @@ __device__ __forceinline__ void grouped_gemm_body(const GemmArgs& g) {
 #pragma unroll
   for (int sl = 0; sl < 4; ++sl) load_a_slice(0, sl, A);
   if constexpr (kDg) {
-    D = dg_load(g, e, n0, 0, tid);
-    dg_stage(D, Cs[0], As[0], tid);
-    D = dg_load(g, e, n0, min(1, nsteps - 1), tid);
+    D = dg_load<kMode>(g, e, n0, 0, tid);
+    dg_stage<kMode>(D, Cs[0], As[0], tid);
+    D = dg_load<kMode>(g, e, n0, min(1, nsteps - 1), tid);
     lds_barrier();
-    dg_read_codes(Cs[0], As[0], tid, R);
+    dg_read_codes<kMode>(Cs[0], As[0], tid, R);
 #pragma unroll
-    for (int c = 0; c < 4; ++c) dg_decode_chunk(R, c, lut, Bs[0], tid);
-    dg_stage(D, Cs[1], As[1], tid);
-    D = dg_load(g, e, n0, min(2, nsteps - 1), tid);
+    for (int c = 0; c < 4; ++c) dg_decode_chunk<kMode>(R, c, lut, Bs[0], tid);
+    dg_stage<kMode>(D, Cs[1], As[1], tid);
+    D = dg_load<kMode>(g, e, n0, min(2, nsteps - 1), tid);
   } else {
     F0 = fwd_load<kMode>(g, e, n0, 0, tid);
     F1 = fwd_load<kMode>(g, e, n0, min(1, nsteps - 1), tid);
@@ -359,11 +394,11 @@ __device__ __forceinline__ void grouped_gemm_body(const GemmArgs& g) {
       for (int sl = 0; sl < 4; ++sl) {
         if (sl < 3) load_b_slice(B, sl + 1, b_nxt);
         if constexpr (kDg) {
-          if (sl == 0) dg_read_codes(Cs[(ks + 1) & 1], As[(ks + 1) & 1], tid, R);
-          dg_decode_chunk(R, sl, lut, Bn, tid);
+          if (sl == 0) dg_read_codes<kMode>(Cs[(ks + 1) & 1], As[(ks + 1) & 1], tid, R);
+          dg_decode_chunk<kMode>(R, sl, lut, Bn, tid);
           if (sl == 3) {                                   // codes of step ks+2, then ks+3
-            dg_stage(D, Cs[ks & 1], As[ks & 1], tid);
-            D = dg_load(g, e, n0, min(ks + 3, nsteps - 1), tid);
+            dg_stage<kMode>(D, Cs[ks & 1], As[ks & 1], tid);
+            D = dg_load<kMode>(g, e, n0, min(ks + 3, nsteps - 1), tid);
           }
         } else {
           fwd_decode_chunk<kMode>(F_dec, sl, lut, Bn, tid);
@@ -426,8 +461,9 @@ template <int kMode>
 __global__ __launch_bounds__(kGemmThreads, 2) void grouped_gemm_fwd_kernel(GemmArgs g) {
   grouped_gemm_body<kMode>(g);
 }
+template <int kMode>
 __global__ __launch_bounds__(kGemmThreads, 1) void grouped_dgrad_kernel(GemmArgs g) {
-  grouped_gemm_body<kDgradNF4>(g);
+  grouped_gemm_body<kMode>(g);
 }
 
 template <int kMode>
@@ -441,9 +477,9 @@ static int launch_gemm(GemmArgs g, int32_t max_tiles, int32_t tile_m, hipStream_
   const int64_t grid = ((n_logical + group - 1) / group) * group;
   if (grid > INT32_MAX) return kNotSupported;
   g.n_logical = (int)n_logical;
-  if constexpr (kMode == kDgradNF4)
-    hipLaunchKernelGGL(grouped_dgrad_kernel, dim3((unsigned)grid), dim3(kGemmThreads), 0, stream,
-                       g);
+  if constexpr (kMode == kDgradNF4 || kMode == kDgradMX)
+    hipLaunchKernelGGL(grouped_dgrad_kernel<kMode>, dim3((unsigned)grid), dim3(kGemmThreads), 0,
+                       stream, g);
   else
     hipLaunchKernelGGL(grouped_gemm_fwd_kernel<kMode>, dim3((unsigned)grid), dim3(kGemmThreads),
                        0, stream, g);
@@ -518,6 +554,33 @@ extern "C" int gq_mxfp4_grouped_gemm(const uint16_t* x, int32_t rows, int32_t K,
                                  max_tiles, tile_m, out, stream);
 }
 
+namespace gq {
+
+template <bool kMx>
+static int dgrad_entry(const uint16_t* dy, int32_t P, int32_t N, int64_t dy_stride,
+                       const uint8_t* codes, const void* scl, int32_t E, int32_t K,
+                       const int32_t* offsets, const int32_t* sorted_pairs, const int32_t* tiles,
+                       const int32_t* num_tiles, int32_t max_tiles, int32_t tile_m, uint16_t* dx,
+                       hipStream_t stream) {
+  if (P < 0 || E < 1 || N < 1 || N % 64 || K <= 0 || K % (kMx ? 32 : 64)) return kInvalid;
+  if (dy_stride < N || dy_stride % 8) return kInvalid;
+  if (tile_m != kTM) return kNotSupported;
+  if (P == 0) return kOk;                                  // nothing to enqueue
+  int st = common_gemm_checks(dy, dy_stride, N, codes, scl, offsets, sorted_pairs, tiles,
+                              num_tiles, dx);
+  if (st != kOk) return st;
+  if (!kMx && !aligned4(scl)) return kInvalid;
+  GemmArgs g{};
+  g.x = dy; g.x_stride = dy_stride; g.codes = codes; g.scl = scl;
+  g.Nw = N; g.Kw = K; g.Kc = N; g.Nout = K;
+  g.E = E; g.topk = 1; g.P = P; g.pair_scale = nullptr;
+  g.offsets = offsets; g.sorted_pairs = sorted_pairs; g.tiles = tiles;
+  g.num_tiles = num_tiles; g.out = dx;
+  return launch_gemm<kMx ? kDgradMX : kDgradNF4>(g, max_tiles, tile_m, stream);
+}
+
+}  // namespace gq
+
 extern "C" int gq_nf4_grouped_dgrad(const uint16_t* dy, int32_t P, int32_t N, int64_t dy_stride,
                                     const uint8_t* codes, const float* absmax,
                                     int32_t num_experts, int32_t K,
@@ -525,20 +588,19 @@ extern "C" int gq_nf4_grouped_dgrad(const uint16_t* dy, int32_t P, int32_t N, in
                                     const int32_t* tiles, const int32_t* num_tiles,
                                     int32_t max_tiles, int32_t tile_m, uint16_t* dx,
                                     hipStream_t stream) {
-  using namespace gq;
-  if (P < 0 || num_experts < 1 || N < 1 || N % 64 || K <= 0 || K % 64) return kInvalid;
-  if (dy_stride < N || dy_stride % 8) return kInvalid;
-  if (tile_m != kTM) return kNotSupported;
-  if (P == 0) return kOk;                                  // nothing to enqueue
-  int st = common_gemm_checks(dy, dy_stride, N, codes, absmax, expert_offsets, sorted_pairs,
-                              tiles, num_tiles, dx);
-  if (st != kOk) return st;
-  if (!aligned4(absmax)) return kInvalid;
-  GemmArgs g{};
-  g.x = dy; g.x_stride = dy_stride; g.codes = codes; g.scl = absmax;
-  g.Nw = N; g.Kw = K; g.Kc = N; g.Nout = K;
-  g.E = num_experts; g.topk = 1; g.P = P; g.pair_scale = nullptr;
-  g.offsets = expert_offsets; g.sorted_pairs = sorted_pairs; g.tiles = tiles;
-  g.num_tiles = num_tiles; g.out = dx;
-  return launch_gemm<kDgradNF4>(g, max_tiles, tile_m, stream);
+  return gq::dgrad_entry<false>(dy, P, N, dy_stride, codes, absmax, num_experts, K,
+                                expert_offsets, sorted_pairs, tiles, num_tiles, max_tiles, tile_m,
+                                dx, stream);
+}
+
+extern "C" int gq_mxfp4_grouped_dgrad(const uint16_t* dy, int32_t P, int32_t N, int64_t dy_stride,
+                                      const uint8_t* blocks, const uint8_t* scales,
+                                      int32_t num_experts, int32_t K,
+                                      const int32_t* expert_offsets, const int32_t* sorted_pairs,
+                                      const int32_t* tiles, const int32_t* num_tiles,
+                                      int32_t max_tiles, int32_t tile_m, uint16_t* dx,
+                                      hipStream_t stream) {
+  return gq::dgrad_entry<true>(dy, P, N, dy_stride, blocks, scales, num_experts, K,
+                               expert_offsets, sorted_pairs, tiles, num_tiles, max_tiles, tile_m,
+                               dx, stream);
 }

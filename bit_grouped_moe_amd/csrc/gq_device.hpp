@@ -44,6 +44,21 @@ __device__ __forceinline__ void nf4_lut_init(float* lut, int tid) {
   if (tid < 16) lut[tid] = __uint_as_float(v);
 }
 
+// OCP e2m1 magnitudes (codes 0..7) as float32 bit patterns; bit 3 of a code
+// is the sign.
+__device__ constexpr uint32_t kE2M1Bits[8] = {0x00000000u, 0x3F000000u, 0x3F800000u,
+                                              0x3FC00000u, 0x40000000u, 0x40400000u,
+                                              0x40800000u, 0x40C00000u};
+
+// Fill a 16-entry float LUT in LDS with the e2m1 values (threads 0..15),
+// selected from immediates like nf4_lut_init.  Code 8 is -0.
+__device__ __forceinline__ void e2m1_lut_init(float* lut, int tid) {
+  uint32_t v = 0u;
+#pragma unroll
+  for (int i = 0; i < 8; ++i) v = ((tid & 7) == i) ? kE2M1Bits[i] : v;
+  if (tid < 16) lut[tid] = __uint_as_float(v | ((tid & 8) ? 0x80000000u : 0u));
+}
+
 // bf16 bit pattern of x, round to nearest even (v_cvt_pk_bf16_f32).
 __device__ __forceinline__ uint16_t f32_to_bf16_bits(float x) {
   __bf16 b = (__bf16)x;

@@ -205,6 +205,27 @@ int gq_nf4_grouped_dgrad(const uint16_t* dy, int32_t P, int32_t N, int64_t dy_st
                          const int32_t* tiles, const int32_t* num_tiles, int32_t max_tiles,
                          int32_t tile_m, uint16_t* dx, hipStream_t stream);
 
+/* ------------------------------------------------------------------------
+ * MXFP4 input gradient.  [P1] "Which entry point?" (native MXFP4 expert
+ * math next to the grouped NF4 backward).  The pages name no MXFP4
+ * backward entry point; this is the NF4 one with the MXFP4 decode:
+ *
+ *   dx[p, k] = bf16( sum_n dy[p, n] * W_{e(p)}[n, k] )
+ *
+ *   blocks  uint8 [E, N, K/32, 16] e2m1 codes (element 2j: low nibble)
+ *   scales  uint8 [E, N, K/32] e8m0 (255 = NaN)
+ * Decoded weights are exact in bf16; bf16 matrix-core products, float32
+ * accumulation.  dy, dx and the grouping as for gq_nf4_grouped_dgrad.
+ * InvalidValue: null pointer, P < 0, E < 1, N < 1 or N % 64, K not a
+ *   positive multiple of 32, bad stride or alignment, max_tiles too small.
+ * NotSupported: tile_m != 256, grid beyond 2^31 blocks.
+ */
+int gq_mxfp4_grouped_dgrad(const uint16_t* dy, int32_t P, int32_t N, int64_t dy_stride,
+                           const uint8_t* blocks, const uint8_t* scales, int32_t num_experts,
+                           int32_t K, const int32_t* expert_offsets, const int32_t* sorted_pairs,
+                           const int32_t* tiles, const int32_t* num_tiles, int32_t max_tiles,
+                           int32_t tile_m, uint16_t* dx, hipStream_t stream);
+
 #ifdef __cplusplus
 }
 #endif

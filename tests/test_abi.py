@@ -140,6 +140,23 @@ def test_dgrad_rejects(lib):
     assert call(P=0) == 0
 
 
+def test_mxfp4_dgrad_rejects(lib):
+    def call(**kw):
+        a = dict(dy=F, P=8192, N=5760, ds=5760, c=F, s=F, E=32, K=2880, off=F, sp=F, tl=F,
+                 nt=F, mt=65, tm=256, dx=F)
+        a.update(kw)
+        return lib.gq_mxfp4_grouped_dgrad(a["dy"], a["P"], a["N"], a["ds"], a["c"], a["s"],
+                                          a["E"], a["K"], a["off"], a["sp"], a["tl"], a["nt"],
+                                          a["mt"], a["tm"], a["dx"], None)
+    assert call(s=NULL) == INVALID
+    assert call(N=5792, ds=5792) == INVALID                    # N % 64
+    assert call(K=2896) == INVALID                             # K % 32
+    assert call(ds=5761) == INVALID                            # stride % 8
+    assert call(mt=40) == INVALID
+    assert call(tm=128) == NOT_SUPPORTED
+    assert call(P=0) == 0
+
+
 def test_missing_library_raises(monkeypatch, tmp_path):
     monkeypatch.setattr(gq, "_lib", None)
     monkeypatch.setenv("GQ_LIBRARY", str(tmp_path / "nope.so"))

@@ -10,7 +10,7 @@ import torch
 import bit_grouped_moe_amd as gq
 import oracle
 import workloads as wl
-from tests.gpu_common import (LazyDecoded, plus_zero,
+from tests.gpu_common import (LazyDecoded, plus_zero, packed_mx_bank,
                               assert_slices, bf16_bits, bf16_to_host_f32, device,
                               packed_nf4_bank, say, to_dev, to_dev_bf16)
 
@@ -90,4 +90,84 @@ def test_deterministic():
     say("dgrad determinism")
     a = _dgrad(dy, to_dev(codes, dev), to_dev(absmax, dev), pe, E, dev)
     b = _dgrad(dy, to_dev(codes, dev), to_dev(absmax, dev), pe, E, dev)
+    assert torch.equal(a.view(torch.int16), b.view(torch.int16))
+
+
+# ---- MXFP4 -----------------------------------------------------------------
+def _dgrad_mx(dy_bits, blocks, scales, pe, E, dev):
+    dy = to_dev_bf16(dy_bits, dev)
+    route = gq.gq_route_sort(to_dev(pe.astype(np.int32).reshape(-1, 1), dev), E)
+    out = gq.gq_mxfp4_grouped_dgrad(dy, blocks, scales, route)
+    torch.cuda.synchronize()
+    return out
+
+
+@pytest.mark.parametrize("E,N,K,P", [(4, 128, 256, 64), (5, 192, 352, 700), (3, 320, 2880, 300)])
+def test_mx_small_and_ragged(E, N, K, P):
+    """K = 352 and 2880 leave a partial 128-column tile (K % 64 == 32 for 352)."""
+    dev = device()
+    g = np.random.default_rng(N + 3 * K)
+    blocks, scales = packed_mx_bank(g, E, N, K)
+    W = LazyDecoded("mx", blocks, scales)
+    pe = wl.route_zipf(g, P, E, 1, s=2.0).reshape(-1)
+    pe[g.random(P) < 0.03] = -1
+    dy = wl.draw_bf16(g, (P, N))
+    say("mx dgrad", E, N, K, P)
+    out = _dgrad_mx(dy, to_dev(blocks, dev), to_dev(scales, dev), pe, E, dev)
+    ref = oracle.grouped_dgrad(dy, W, pe, E)
+    assert_slices(bf16_to_host_f32(out), ref, pe, E)
+    dropped = pe < 0
+    assert not bf16_bits(out)[dropped].any() or not dropped.any()
+
+
+def test_mx_one_hot_probe_is_bit_exact():
+    """dY = e_n makes dX row p the decoded MXFP4 weight row W[n, :] (exact in bf16)."""
+    dev = device()
+    g = np.random.default_rng(16)
+    E, N, K = 2, 128, 224
+    blocks, scales = packed_mx_bank(g, E, N, K)
+    W = LazyDecoded("mx", blocks, scales)
+    ns = np.array([0, 1, 63, 64, 127])
+    dy = np.zeros((2 * len(ns), N), dtype=np.uint16)
+    pe = np.zeros(2 * len(ns), dtype=np.int32)
+    for i, n in enumerate(ns):
+        dy[2 * i, n] = dy[2 * i + 1, n] = 0x3F80
+        pe[2 * i + 1] = 1
+    say("mx dgrad one-hot")
+    out = bf16_bits(_dgrad_mx(dy, to_dev(blocks, dev), to_dev(scales, dev), pe, E, dev))
+    for i, n in enumerate(ns):
+        for s in range(2):
+            want = oracle.f32_to_bf16_rne(W(s)[n])
+            assert np.array_equal(plus_zero(out[2 * i + s]), plus_zero(want)), (n, s)
+
+
+@pytest.mark.parametrize("proj", ["gate_up", "down"])
+def test_gptoss_mx_dgrad_full_shapes(proj):
+    """gpt-oss-20b shapes, 2048 tokens x top-4 = 8192 pairs over 32 experts.
+    Checked on three experts, every row."""
+    dev = device()
+    E, topk = wl.GPTOSS["E"], wl.GPTOSS["topk"]
+    N, K = wl.GPTOSS[proj]
+    blocks, scales = wl.random_mxfp4_bank(E, N, K, dev, seed=6000 + N)
+    pe = wl.route_uniform(wl.rng(wl.CFG_GPTOSS, wl.S_ROUTE), 2048, E, topk).reshape(-1)
+    dy = wl.draw_bf16(wl.rng(wl.CFG_GPTOSS, wl.S_DOWN_IN), (pe.size, N))
+    say("mx dgrad gpt-oss", proj)
+    out = _dgrad_mx(dy, blocks, scales, pe, E, dev)
+    W = LazyDecoded("mx", blocks.cpu().numpy(), scales.cpu().numpy())
+    check = [0, 17, 31]
+    ref = oracle.grouped_dgrad(dy, lambda e: W(e) if e in check else np.zeros((N, K), np.float32),
+                               pe, E)
+    assert_slices(bf16_to_host_f32(out), ref, pe, E, experts=check)
+
+
+def test_mx_deterministic():
+    dev = device()
+    g = np.random.default_rng(13)
+    E, N, K, P = 8, 256, 416, 1000
+    blocks, scales = packed_mx_bank(g, E, N, K)
+    pe = g.integers(0, E, P)
+    dy = wl.draw_bf16(g, (P, N))
+    say("mx dgrad determinism")
+    a = _dgrad_mx(dy, to_dev(blocks, dev), to_dev(scales, dev), pe, E, dev)
+    b = _dgrad_mx(dy, to_dev(blocks, dev), to_dev(scales, dev), pe, E, dev)
     assert torch.equal(a.view(torch.int16), b.view(torch.int16))
