@@ -21,8 +21,8 @@
 //    64-block absmax factored out of each 32-weight partial sum; MXFP4: the
 //    gfx950 e2m1 converter, the e8m0 factor applied to the partial sum with
 //    ldexp.  Both keep the decoded weight exact (float32).
-//  * partial sums meet in LDS and are reduced in a fixed order: no atomics,
-//    bitwise reproducible.
+//  * partial sums are reduced in a fixed order (DPP lane moves inside a wave,
+//    LDS across waves): no atomics, bitwise reproducible.
 #include "gq_device.hpp"
 #include "gq_host.hpp"
 #include "../../include/gq.h"
@@ -79,19 +79,21 @@ __device__ __forceinline__ float segment_dot(const float* lut, u32x4 c, float am
 }
 
 // kIter rows per thread.  Memory round trips on the critical path: (1) the
-// expert id of pair p0, the routing table and p0's activation slice, all
-// issued together; (2) the weight bytes.  Routing decisions are taken per
-// wave from ballots (no barrier).  Pairs that share p0's expert (rare at
-// decode) cost one more activation load each.
+// expert id of pair p0 (a scalar load), issued together with the routing
+// table and p0's activation slice; (2) the weight bytes.  Routing decisions
+// are taken per wave from ballots (no barrier), after p0's rows are
+// computed.  Pairs that share p0's expert (rare at decode) cost one more
+// activation load each.
 //
 // kWaveRows: a row's S segments lie inside one wave (64 % S == 0) and are
-// summed with a butterfly of cross-lane shuffles; otherwise partial sums
-// meet in LDS.  Both orders are fixed, so results are reproducible.
+// summed with DPP lane moves; otherwise partial sums meet in LDS.  Both
+// orders are fixed, so results are reproducible.
 template <bool kMx, int kIter, bool kWaveRows>
 __global__ __launch_bounds__(kGemvMaxThreads) void grouped_gemv_kernel(
     const uint16_t* __restrict__ x, int64_t x_stride, int K, const uint8_t* __restrict__ codes,
     const void* __restrict__ scl, int N, int E, const int32_t* __restrict__ ids, int topk, int P,
-    const float* __restrict__ pair_scale, uint16_t* __restrict__ out, int S, int G, int NT) {
+    const float* __restrict__ pair_scale, uint16_t* __restrict__ out, int S, int W, int G,
+    int NT) {
   __shared__ float lut[16];
   __shared__ float red[kWaveRows ? 1 : kIter * (kGemvMaxThreads + 32)];
 
@@ -100,9 +102,9 @@ __global__ __launch_bounds__(kGemvMaxThreads) void grouped_gemv_kernel(
   const int p0 = blockIdx.y;
   const int R = G * kIter;
   const int n0 = blockIdx.x * R;
-  const bool active = tid < S * G;
-  const int g = tid / S;
-  const int s = tid - g * S;
+  const int g = tid / W;                            // row slot
+  const int s = tid - g * W;                        // segment
+  const bool active = kWaveRows ? s < S : tid < S * G;
 
   // ---- round trip 1: expert of p0, routing table (per wave), p0's activations ----
   const int e = ids[p0];
@@ -148,6 +150,79 @@ __global__ __launch_bounds__(kGemvMaxThreads) void grouped_gemv_kernel(
     }
   }
 
+  if constexpr (!kMx) {
+    nf4_lut_init(lut, tid);
+    lds_barrier();
+  }
+
+  // ---- the rows of one pair: kWaveRows -> row i's total on the last lane of
+  // its segment group; otherwise vals[j] of thread t holds row t + j*NT's total ----
+  float vals[kIter];
+  auto compute_pair = [&]() {
+    float xf[32];
+#pragma unroll
+    for (int v = 0; v < 4; ++v)
+#pragma unroll
+      for (int cc = 0; cc < 4; ++cc) {
+        xf[8 * v + 2 * cc] = bf16lo_to_f32(xr[v][cc]);
+        xf[8 * v + 2 * cc + 1] = bf16hi_to_f32(xr[v][cc]);
+      }
+    if constexpr (kWaveRows) {
+#pragma unroll
+      for (int i = 0; i < kIter; ++i) {
+        const float part = active ? segment_dot<kMx>(lut, cw[i], am[i], sb[i], xf) : 0.f;
+        vals[i] = group_sum_last(part, W);                     // total on lane s == W-1
+      }
+    } else {
+      constexpr int kStride = kGemvMaxThreads + 32;            // pad: spreads banks
+#pragma unroll
+      for (int i = 0; i < kIter; ++i)
+        red[i * kStride + tid] = active ? segment_dot<kMx>(lut, cw[i], am[i], sb[i], xf) : 0.f;
+      lds_barrier();
+#pragma unroll
+      for (int jr = 0; jr < kIter; ++jr) {                     // R <= kIter * NT
+        const int r = tid + jr * NT;
+        vals[jr] = 0.f;
+        if (r < R) {
+          const int gg = r % G, ii = r / G;
+          const float* src = red + ii * kStride + gg * S;
+          float s0 = 0.f, s1 = 0.f, s2 = 0.f, s3 = 0.f;        // fixed order, 4 chains
+          int j = 0;
+          for (; j + 4 <= S; j += 4) {
+            s0 += src[j];
+            s1 += src[j + 1];
+            s2 += src[j + 2];
+            s3 += src[j + 3];
+          }
+          for (; j < S; ++j) s0 += src[j];
+          vals[jr] = (s0 + s1) + (s2 + s3);
+        }
+      }
+      lds_barrier();
+    }
+  };
+  auto store_pair = [&](int p) {
+    const float sc = pair_scale ? pair_scale[p] : 1.f;
+    if constexpr (kWaveRows) {
+#pragma unroll
+      for (int i = 0; i < kIter; ++i) {
+        const int n = n0 + g + G * i;
+        if (s == W - 1 && n < N) out[(int64_t)p * N + n] = f32_to_bf16_bits(vals[i] * sc);
+      }
+    } else {
+#pragma unroll
+      for (int jr = 0; jr < kIter; ++jr) {
+        const int r = tid + jr * NT, n = n0 + r;
+        if (r < R && n < N) out[(int64_t)p * N + n] = f32_to_bf16_bits(vals[jr] * sc);
+      }
+    }
+  };
+
+  // ---- p0's rows are computed before the routing table is inspected: with
+  // the decision first, the compiler holds the weight loads back until the
+  // table has arrived (a full extra memory round trip) ----
+  compute_pair();
+
   // ---- is p0 the first pair of expert e?  (same answer in every wave) ----
   uint64_t match[kGemvMaxPairs / kWave];
   bool dup = false;
@@ -157,58 +232,10 @@ __global__ __launch_bounds__(kGemvMaxThreads) void grouped_gemv_kernel(
     match[c] = __ballot(idl[c] == e);
     dup |= __ballot(idl[c] == e && q < p0) != 0ull;
   }
-  if (dup) return;
-  if constexpr (!kMx) {
-    nf4_lut_init(lut, tid);
-    lds_barrier();
-  }
+  if (dup) return;                           // an earlier pair's workgroup serves p0
+  store_pair(p0);
 
-  // ---- one pass per pair routed to e, ascending; p0 (the first) is peeled so
-  // that its rows are processed as their loads land (no loop-head wait) ----
-  auto process_pair = [&](int p) {
-    float xf[32];
-#pragma unroll
-    for (int v = 0; v < 4; ++v)
-#pragma unroll
-      for (int cc = 0; cc < 4; ++cc) {
-        xf[8 * v + 2 * cc] = bf16lo_to_f32(xr[v][cc]);
-        xf[8 * v + 2 * cc + 1] = bf16hi_to_f32(xr[v][cc]);
-      }
-    const float sc = pair_scale ? pair_scale[p] : 1.f;
-    if constexpr (kWaveRows) {
-#pragma unroll
-      for (int i = 0; i < kIter; ++i) {
-        float part = active ? segment_dot<kMx>(lut, cw[i], am[i], sb[i], xf) : 0.f;
-        for (int off = S >> 1; off > 0; off >>= 1) part += __shfl_xor(part, off, kWave);
-        const int n = n0 + g + G * i;
-        if (active && s == 0 && n < N) out[(int64_t)p * N + n] = f32_to_bf16_bits(part * sc);
-      }
-    } else {
-      constexpr int kStride = kGemvMaxThreads + 32;            // pad: spreads banks
-#pragma unroll
-      for (int i = 0; i < kIter; ++i)
-        red[i * kStride + tid] = active ? segment_dot<kMx>(lut, cw[i], am[i], sb[i], xf) : 0.f;
-      lds_barrier();
-      for (int r = tid; r < R; r += NT) {
-        const int gg = r % G, ii = r / G;
-        const float* src = red + ii * kStride + gg * S;
-        float s0 = 0.f, s1 = 0.f, s2 = 0.f, s3 = 0.f;          // fixed order, 4 chains
-        int j = 0;
-        for (; j + 4 <= S; j += 4) {
-          s0 += src[j];
-          s1 += src[j + 1];
-          s2 += src[j + 2];
-          s3 += src[j + 3];
-        }
-        for (; j < S; ++j) s0 += src[j];
-        const int n = n0 + r;
-        if (n < N) out[(int64_t)p * N + n] = f32_to_bf16_bits(((s0 + s1) + (s2 + s3)) * sc);
-      }
-      lds_barrier();
-    }
-  };
-
-  process_pair(p0);
+  // ---- then every later pair routed to e, ascending ----
   for (int c = 0; c < kGemvMaxPairs / kWave; ++c) {
     uint64_t m = match[c];
     if (c == p0 / kWave) m &= ~(1ull << (p0 % kWave));
@@ -219,7 +246,8 @@ __global__ __launch_bounds__(kGemvMaxThreads) void grouped_gemv_kernel(
                                                         (active ? s : 0) * 32);
 #pragma unroll
       for (int v = 0; v < 4; ++v) xr[v] = xp[v];
-      process_pair(p);
+      compute_pair();
+      store_pair(p);
     }
   }
 }
@@ -228,13 +256,13 @@ template <bool kMx, int kIter>
 static void launch_gemv_iter(dim3 grid, int NT, hipStream_t stream, const uint16_t* x,
                              int64_t x_stride, int K, const uint8_t* codes, const void* scl,
                              int N, int E, const int32_t* ids, int topk, int P,
-                             const float* pair_scale, uint16_t* out, int S, int G) {
-  if (kWave % S == 0)
+                             const float* pair_scale, uint16_t* out, int S, int W, int G) {
+  if (S <= kWave)
     hipLaunchKernelGGL((grouped_gemv_kernel<kMx, kIter, true>), grid, dim3(NT), 0, stream, x,
-                       x_stride, K, codes, scl, N, E, ids, topk, P, pair_scale, out, S, G, NT);
+                       x_stride, K, codes, scl, N, E, ids, topk, P, pair_scale, out, S, W, G, NT);
   else
     hipLaunchKernelGGL((grouped_gemv_kernel<kMx, kIter, false>), grid, dim3(NT), 0, stream, x,
-                       x_stride, K, codes, scl, N, E, ids, topk, P, pair_scale, out, S, G, NT);
+                       x_stride, K, codes, scl, N, E, ids, topk, P, pair_scale, out, S, W, G, NT);
 }
 
 template <bool kMx>
@@ -251,9 +279,15 @@ static int launch_gemv(const uint16_t* x, int32_t rows, int32_t K, int64_t x_str
   if (pair_scale && !aligned4(pair_scale)) return kInvalid;
   const int64_t P = (int64_t)rows * topk;
   if (P > kGemvMaxPairs || K > kGemvMaxK || N >= (1 << 24)) return kNotSupported;
+  // S segments of 32 weights per row.  S <= 64: a row's segments go to a
+  // group of W = S rounded up to a power of two lanes inside one wave (lanes
+  // s >= S idle); longer rows: S consecutive threads, reduced through LDS.
   const int S = K / 32;
-  const int G = S >= kGemvMaxThreads ? 1 : kGemvMaxThreads / S;
-  const int NT = ((S * G + kWave - 1) / kWave) * kWave;
+  int W = S;
+  if (S <= kWave)
+    while (W & (W - 1)) W += W & -W;
+  const int G = S > kWave ? (S >= kGemvMaxThreads ? 1 : kGemvMaxThreads / S) : kGemvMaxThreads / W;
+  const int NT = S > kWave ? ((S * G + kWave - 1) / kWave) * kWave : kGemvMaxThreads;
   // Rows per thread: as many loads in flight per thread as possible while the
   // grid of one pair still spreads over every CU twice.
   const int64_t want_blocks = 512;
@@ -263,11 +297,11 @@ static int launch_gemv(const uint16_t* x, int32_t rows, int32_t K, int64_t x_str
   const dim3 grid((N + R - 1) / R, (unsigned)P);
   switch (iter) {
     case 8: launch_gemv_iter<kMx, 8>(grid, NT, stream, x, x_stride, K, codes, scl, N, E, ids,
-                                     topk, (int)P, pair_scale, out, S, G); break;
+                                     topk, (int)P, pair_scale, out, S, W, G); break;
     case 4: launch_gemv_iter<kMx, 4>(grid, NT, stream, x, x_stride, K, codes, scl, N, E, ids,
-                                     topk, (int)P, pair_scale, out, S, G); break;
+                                     topk, (int)P, pair_scale, out, S, W, G); break;
     default: launch_gemv_iter<kMx, 2>(grid, NT, stream, x, x_stride, K, codes, scl, N, E, ids,
-                                      topk, (int)P, pair_scale, out, S, G); break;
+                                      topk, (int)P, pair_scale, out, S, W, G); break;
   }
   return launch_status();
 }

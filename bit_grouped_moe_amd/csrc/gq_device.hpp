@@ -151,6 +151,30 @@ __device__ __forceinline__ void lds_barrier() {
   __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup", "local");
 }
 
+// v from lane (lane pattern kCtrl) through a DPP move; rows (16 lanes) not in
+// kRowMask read 0.
+template <int kCtrl, int kRowMask = 0xF>
+__device__ __forceinline__ float dpp_f32(float v) {
+  return __int_as_float(
+      __builtin_amdgcn_update_dpp(0, __float_as_int(v), kCtrl, kRowMask, 0xF, false));
+}
+
+// Sum over aligned groups of `width` lanes (a power of two, 1..64) with DPP
+// lane moves only (no LDS traffic, no waits), in a fixed order.  The last
+// lane of each group receives the group total (width <= 16: every lane).
+//   quad_perm [1,0,3,2], [2,3,0,1]: pairs, then quads
+//   row_half_mirror, row_mirror: 8 and 16 lanes
+//   row_bcast:15 into rows 1 and 3, row_bcast:31 into row 3: 32 and 64 lanes
+__device__ __forceinline__ float group_sum_last(float v, int width) {
+  if (width >= 2) v += dpp_f32<0xB1>(v);
+  if (width >= 4) v += dpp_f32<0x4E>(v);
+  if (width >= 8) v += dpp_f32<0x141>(v);
+  if (width >= 16) v += dpp_f32<0x140>(v);
+  if (width >= 32) v += dpp_f32<0x142, 0xA>(v);
+  if (width >= 64) v += dpp_f32<0x143, 0x8>(v);
+  return v;
+}
+
 __device__ __forceinline__ int wave_inclusive_scan(int v) {
   const int lane = threadIdx.x & (kWave - 1);
 #pragma unroll

@@ -47,6 +47,27 @@ def test_tiny_gather(fmt, rows):
 
 
 @pytest.mark.parametrize("fmt", ["nf4", "mx"])
+@pytest.mark.parametrize("K", [64, 128, 256, 1024, 4096, 192, 96])
+def test_k_sweep(fmt, K):
+    """Every in-wave reduction width (K/32 segments = 2 .. 64 lanes), the
+    cross-wave path (K = 4096), and segment counts that do not divide a wave
+    (K = 96, 192: several rows per thread in the cross-wave reduction)."""
+    if fmt == "nf4" and K % 64:
+        pytest.skip("NF4 needs K % 64 == 0")
+    dev = device()
+    g = wl.rng(wl.CFG_TINY, 300 + K)
+    E, N, topk, rows = 3, 160, 2, 2
+    bank = packed_nf4_bank(g, E, N, K) if fmt == "nf4" else packed_mx_bank(g, E, N, K)
+    x = wl.draw_bf16(g, (rows, K))
+    ids = wl.route_uniform(g, rows, E, topk)
+    W = LazyDecoded(fmt, *bank)
+    say("gemv k sweep", fmt, K)
+    out = _run(fmt, x, bank, ids, dev, None)
+    ref = oracle.grouped_gemm(x, W, ids, E)
+    assert_slices(bf16_to_host_f32(out), ref, ids, E)
+
+
+@pytest.mark.parametrize("fmt", ["nf4", "mx"])
 def test_shared_experts_dropped_and_flatten(fmt):
     dev = device()
     g = np.random.default_rng(7)
