@@ -288,9 +288,12 @@ static int launch_gemv(const uint16_t* x, int32_t rows, int32_t K, int64_t x_str
     while (W & (W - 1)) W += W & -W;
   const int G = S > kWave ? (S >= kGemvMaxThreads ? 1 : kGemvMaxThreads / S) : kGemvMaxThreads / W;
   const int NT = S > kWave ? ((S * G + kWave - 1) / kWave) * kWave : kGemvMaxThreads;
-  // Rows per thread: as many loads in flight per thread as possible while the
-  // grid of one pair still spreads over every CU twice.
-  const int64_t want_blocks = 512;
+  // Rows per thread: the largest count (8, 4, 2) that still gives enough
+  // workgroups.  With in-wave reductions many small workgroups stream better
+  // (about eight per CU: on the one-token gate_up GEMV 1536 workgroups of 2
+  // rows per thread beat 768 of 4 by 8%); the LDS-reduced long rows prefer
+  // more rows per thread (two workgroups per CU).
+  const int64_t want_blocks = S <= kWave ? 2048 : 512;
   int iter = 8;
   while (iter > 2 && (int64_t)((N + G * iter - 1) / (G * iter)) * P < want_blocks) iter >>= 1;
   const int R = G * iter;
