@@ -109,15 +109,16 @@ __device__ __forceinline__ void fwd_decode_chunk(const FwdLoad& L, int q, const 
                                                  uint16_t* Bs, int tid) {
   const int col = tid & (kTN - 1), h = tid >> 7;
   uint32_t p[4];
+  // Elements outside the matrix get a zero factor (their codes are a clamped
+  // re-read): one select per chunk instead of one per output dword.
   if constexpr (kMode == kFwdMX) {
-    const float sc = e8m0_to_f32(L.s);
+    const float sc = L.ok ? e8m0_to_f32(L.s) : 0.f;
 #pragma unroll
     for (int b = 0; b < 4; ++b) p[b] = e2m1_pair_bf16_scaled(L.c[q], b, sc);
   } else {
-    nf4_decode8_bf16(lut, L.c[q], L.a, p);
+    nf4_decode8_bf16(lut, L.c[q], L.ok ? L.a : 0.f, p);
   }
-  const u32x4 v = L.ok ? u32x4{p[0], p[1], p[2], p[3]} : u32x4{0u, 0u, 0u, 0u};
-  *reinterpret_cast<u32x4*>(Bs + col * kBStride + h * 32 + 8 * q) = v;
+  *reinterpret_cast<u32x4*>(Bs + col * kBStride + h * 32 + 8 * q) = u32x4{p[0], p[1], p[2], p[3]};
 }
 
 // Dgrad: B[k][col] = W[ks*64 + k][k0 + col], i.e. a 64 x 128 block of W
@@ -388,11 +389,11 @@ __device__ __forceinline__ void grouped_gemm_body(const GemmArgs& g) {
           for (int sl = 0; sl < 4; ++sl) A[0][sl] = A[1][sl] = u32x4{0u, 0u, 0u, 0u};
         }
       }
-      bf16x8 b_cur[4], b_nxt[4];
-      load_b_slice(B, 0, b_cur);
-#pragma unroll
-      for (int sl = 0; sl < 4; ++sl) {
-        if (sl < 3) load_b_slice(B, sl + 1, b_nxt);
+      // B fragments ping-pong between two register sets (no copies): slice
+      // sl's MFMAs read one set while slice sl+1's fragments load into the other.
+      bf16x8 b0[4], b1[4];
+      auto slice = [&](int sl, const bf16x8 (&bc)[4], bf16x8 (&bn)[4]) {
+        if (sl < 3) load_b_slice(B, sl + 1, bn);
         if constexpr (kDg) {
           if (sl == 0) dg_read_codes<kMode>(Cs[(ks + 1) & 1], As[(ks + 1) & 1], tid, R);
           dg_decode_chunk<kMode>(R, sl, lut, Bn, tid);
@@ -403,13 +404,14 @@ __device__ __forceinline__ void grouped_gemm_body(const GemmArgs& g) {
         } else {
           fwd_decode_chunk<kMode>(F_dec, sl, lut, Bn, tid);
         }
-        mfma_slice(rows_c, A, sl, b_cur);
+        mfma_slice(rows_c, A, sl, bc);
         load_a_slice(k1, sl, A);
-        if (sl < 3) {
-#pragma unroll
-          for (int c = 0; c < 4; ++c) b_cur[c] = b_nxt[c];
-        }
-      }
+      };
+      load_b_slice(B, 0, b0);
+      slice(0, b0, b1);
+      slice(1, b1, b0);
+      slice(2, b0, b1);
+      slice(3, b1, b0);
       lds_barrier();
     };
     for (int ks = 0; ks < nsteps; ks += 2) {

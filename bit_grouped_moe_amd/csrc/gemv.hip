@@ -33,21 +33,6 @@ constexpr int kGemvMaxThreads = 256;
 constexpr int kGemvMaxPairs = 256;
 constexpr int kGemvMaxK = 8192;     // 256 segments of 32 weights
 
-// NF4 codebook values of the 8 weights of one code dword, in element order.
-// Addressing costs 1.5 ops per weight: the nibbles are first spread into
-// bytes already multiplied by 4 (byte offsets into the 16-float LDS table),
-// then each lookup extracts one byte.
-__device__ __forceinline__ void nf4_lookup8(const float* lut, uint32_t d, float q[8]) {
-  const uint32_t hi4 = (d >> 2) & 0x3C3C3C3Cu;     // byte j: 4 * code of element 2j
-  const uint32_t lo4 = (d << 2) & 0x3C3C3C3Cu;     // byte j: 4 * code of element 2j+1
-  const char* base = reinterpret_cast<const char*>(lut);
-#pragma unroll
-  for (int b = 0; b < 4; ++b) {
-    q[2 * b] = *reinterpret_cast<const float*>(base + ((hi4 >> (8 * b)) & 0xFFu));
-    q[2 * b + 1] = *reinterpret_cast<const float*>(base + ((lo4 >> (8 * b)) & 0xFFu));
-  }
-}
-
 // Partial dot product of one 32-weight segment with the activation slice.
 template <bool kMx>
 __device__ __forceinline__ float segment_dot(const float* lut, u32x4 c, float am, uint32_t sb,

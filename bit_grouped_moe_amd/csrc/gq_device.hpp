@@ -88,17 +88,33 @@ __device__ __forceinline__ float nf4_q_lo(const float* lut, uint32_t d, int byte
   return lut[(d >> (8 * byte_idx)) & 15u];
 }
 
+// NF4 codebook values of the 8 weights of one code dword, in element order.
+// Addressing costs 1.25 ops per weight: the nibbles are first spread into
+// bytes already multiplied by 4 (byte offsets into the 16-float LDS table),
+// then each lookup extracts one byte.
+__device__ __forceinline__ void nf4_lookup8(const float* lut, uint32_t d, float q[8]) {
+  uint32_t hi4 = (d >> 2) & 0x3C3C3C3Cu;           // byte j: 4 * code of element 2j
+  uint32_t lo4 = (d << 2) & 0x3C3C3C3Cu;           // byte j: 4 * code of element 2j+1
+  // Opaque to the optimizer: otherwise it folds the spread back into a shift
+  // and a mask per lookup (two ops) instead of one byte extract.
+  asm("" : "+v"(hi4), "+v"(lo4));
+  const char* base = reinterpret_cast<const char*>(lut);
+#pragma unroll
+  for (int b = 0; b < 4; ++b) {
+    q[2 * b] = *reinterpret_cast<const float*>(base + __builtin_amdgcn_ubfe(hi4, 8 * b, 8));
+    q[2 * b + 1] = *reinterpret_cast<const float*>(base + __builtin_amdgcn_ubfe(lo4, 8 * b, 8));
+  }
+}
+
 // Decode the 8 weights of one dword of NF4 codes to bf16 pairs (element
 // order preserved: out[i] holds elements 2i (low half) and 2i+1 (high half)).
 // weight = float32(q * absmax), then bf16 RNE.
 __device__ __forceinline__ void nf4_decode8_bf16(const float* lut, uint32_t d, float absmax,
                                                  uint32_t out[4]) {
+  float q[8];
+  nf4_lookup8(lut, d, q);
 #pragma unroll
-  for (int b = 0; b < 4; ++b) {
-    float w0 = nf4_q_hi(lut, d, b) * absmax;
-    float w1 = nf4_q_lo(lut, d, b) * absmax;
-    out[b] = pack_bf16x2(w0, w1);
-  }
+  for (int b = 0; b < 4; ++b) out[b] = pack_bf16x2(q[2 * b] * absmax, q[2 * b + 1] * absmax);
 }
 
 // ---- MXFP4 ---------------------------------------------------------------
