@@ -451,7 +451,9 @@ def main():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=200)
     ap.add_argument("--warmup", type=int, default=20)
-    ap.add_argument("--prefill-steps", type=int, default=10)
+    ap.add_argument("--prefill-steps", type=int, default=30)
+    ap.add_argument("--prefill-warmup", type=int, default=30,
+                    help="untimed prefill/dgrad steps first (long kernels: lets the clocks settle)")
     ap.add_argument("--cpu-budget", type=float, default=12.0)
     ap.add_argument("--quick", action="store_true", help="headline + prefill only, short CPU leg")
     args = ap.parse_args()
@@ -472,7 +474,7 @@ def main():
     ctl = controls(dev, int(dec["gate_up_bytes_per_launch"]))
     log("[bench] controls", r4(ctl))
     log("[bench] nf4 prefill M=4096")
-    pre = prefill(dev, args.prefill_steps, 2, "nf4")
+    pre = prefill(dev, args.prefill_steps, args.prefill_warmup, "nf4")
     log("[bench]", r4(pre))
     extra = {}
     if not args.quick:
@@ -483,15 +485,15 @@ def main():
         log("[bench] mxfp4 decode M=1")
         extra["mxfp4_decode_m1"] = decode_mx(dev, args.steps, args.warmup)
         log("[bench] mxfp4 prefill M=2048")
-        mp = prefill(dev, args.prefill_steps, 2, "mx")
+        mp = prefill(dev, args.prefill_steps, args.prefill_warmup, "mx")
         mp["workload"] = "gpt-oss-20b mxfp4 prefill M=2048 top-4 (bf16 MFMA on exact decode)"
         mp["gate_up_frac_bf16_peak"] = mp["gate_up_tflops"] / BF16_PEAK_TFLOPS
         mp["gate_up_frac_fp4_peak"] = mp["gate_up_tflops"] / FP4_PEAK_TFLOPS
         extra["mxfp4_prefill_m2048"] = mp
         log("[bench] nf4 dgrad")
-        extra["nf4_dgrad_m2048"] = dgrad(dev, args.prefill_steps, 2)
+        extra["nf4_dgrad_m2048"] = dgrad(dev, args.prefill_steps, args.prefill_warmup)
         log("[bench] mxfp4 dgrad")
-        extra["mxfp4_dgrad_m2048"] = dgrad(dev, args.prefill_steps, 2, "mx")
+        extra["mxfp4_dgrad_m2048"] = dgrad(dev, args.prefill_steps, args.prefill_warmup, "mx")
     extra = {k: r4(v) for k, v in extra.items()}
 
     log("[bench] cpu baseline (oracle)")

@@ -141,8 +141,8 @@ __global__ __launch_bounds__(kGemvMaxThreads) void grouped_gemv_kernel(
   }
 
   // ---- the rows of one pair: kWaveRows -> row i's total on the last lane of
-  // its segment group; otherwise vals[j] of thread t holds row t + j*NT's total ----
-  float vals[kIter];
+  // its segment group; otherwise thread r < R holds row r's total ----
+  float vals[kWaveRows ? kIter : 1];
   auto compute_pair = [&]() {
     float xf[32];
 #pragma unroll
@@ -164,24 +164,20 @@ __global__ __launch_bounds__(kGemvMaxThreads) void grouped_gemv_kernel(
       for (int i = 0; i < kIter; ++i)
         red[i * kStride + tid] = active ? segment_dot<kMx>(lut, cw[i], am[i], sb[i], xf) : 0.f;
       lds_barrier();
-#pragma unroll
-      for (int jr = 0; jr < kIter; ++jr) {                     // R <= kIter * NT
-        const int r = tid + jr * NT;
-        vals[jr] = 0.f;
-        if (r < R) {
-          const int gg = r % G, ii = r / G;
-          const float* src = red + ii * kStride + gg * S;
-          float s0 = 0.f, s1 = 0.f, s2 = 0.f, s3 = 0.f;        // fixed order, 4 chains
-          int j = 0;
-          for (; j + 4 <= S; j += 4) {
-            s0 += src[j];
-            s1 += src[j + 1];
-            s2 += src[j + 2];
-            s3 += src[j + 3];
-          }
-          for (; j < S; ++j) s0 += src[j];
-          vals[jr] = (s0 + s1) + (s2 + s3);
+      vals[0] = 0.f;
+      if (tid < R) {                                           // R <= NT (host check)
+        const int gg = tid % G, ii = tid / G;
+        const float* src = red + ii * kStride + gg * S;
+        float s0 = 0.f, s1 = 0.f, s2 = 0.f, s3 = 0.f;          // fixed order, 4 chains
+        int j = 0;
+        for (; j + 4 <= S; j += 4) {
+          s0 += src[j];
+          s1 += src[j + 1];
+          s2 += src[j + 2];
+          s3 += src[j + 3];
         }
+        for (; j < S; ++j) s0 += src[j];
+        vals[0] = (s0 + s1) + (s2 + s3);
       }
       lds_barrier();
     }
@@ -195,11 +191,8 @@ __global__ __launch_bounds__(kGemvMaxThreads) void grouped_gemv_kernel(
         if (s == W - 1 && n < N) out[(int64_t)p * N + n] = f32_to_bf16_bits(vals[i] * sc);
       }
     } else {
-#pragma unroll
-      for (int jr = 0; jr < kIter; ++jr) {
-        const int r = tid + jr * NT, n = n0 + r;
-        if (r < R && n < N) out[(int64_t)p * N + n] = f32_to_bf16_bits(vals[jr] * sc);
-      }
+      const int n = n0 + tid;
+      if (tid < R && n < N) out[(int64_t)p * N + n] = f32_to_bf16_bits(vals[0] * sc);
     }
   };
 
@@ -282,6 +275,7 @@ static int launch_gemv(const uint16_t* x, int32_t rows, int32_t K, int64_t x_str
   int iter = 8;
   while (iter > 2 && (int64_t)((N + G * iter - 1) / (G * iter)) * P < want_blocks) iter >>= 1;
   const int R = G * iter;
+  if (S > kWave && R > NT) return kNotSupported;     // one reduced row per thread
   const dim3 grid((N + R - 1) / R, (unsigned)P);
   switch (iter) {
     case 8: launch_gemv_iter<kMx, 8>(grid, NT, stream, x, x_stride, K, codes, scl, N, E, ids,
