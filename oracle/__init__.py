@@ -41,3 +41,4 @@ from .grouped import (  # noqa: F401
     compare_slices,
     REL_L2_TOL,
 )
+from .moe import silu, swiglu, gate_up_swiglu, combine, down_combine  # noqa: F401

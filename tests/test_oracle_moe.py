@@ -1,0 +1,89 @@
+"""Pins of the MoE-layer oracle (oracle/moe.py) against closed forms,
+brute force and layout probes."""
+
+import math
+
+import numpy as np
+import pytest
+
+import oracle
+import workloads as wl
+
+
+def test_silu_closed_forms():
+    # sigmoid(1) = e / (1 + e); silu(-z) = silu(z) - z
+    s1 = math.e / (1.0 + math.e)
+    assert oracle.silu(0.0) == 0.0
+    assert oracle.silu(1.0) == pytest.approx(s1, rel=1e-15)
+    assert oracle.silu(-1.0) == pytest.approx(s1 - 1.0, rel=1e-14)
+    z = np.linspace(-9, 9, 37)
+    np.testing.assert_allclose(oracle.silu(-z), oracle.silu(z) - z, rtol=0, atol=1e-14)
+    # large |z|: identity and (almost) zero
+    assert oracle.silu(40.0) == pytest.approx(40.0, rel=1e-15)
+    assert abs(oracle.silu(-40.0)) < 1e-15
+
+
+def test_swiglu_brute_force():
+    g = np.random.default_rng(0)
+    h = g.standard_normal((5, 6)) * 3
+    want = np.array([[h[p, j] / (1 + math.exp(-h[p, j])) * h[p, 3 + j] for j in range(3)]
+                     for p in range(5)])
+    np.testing.assert_allclose(oracle.swiglu(h), want, rtol=1e-14, atol=0)
+    with pytest.raises(ValueError):
+        oracle.swiglu(np.zeros((2, 5)))
+
+
+def test_gate_rows_come_first():
+    """Zero gate rows give silu(0) * up = 0 everywhere; up rows that select
+    x[:, 0] give silu(gate) * x[:, 0], checked against the gate product
+    computed directly.  A layout with the up rows first fails both."""
+    g = np.random.default_rng(1)
+    E, I, H = 2, 4, 64
+    x = wl.draw_bf16(g, (3, H))
+    ids = np.array([[0, 1], [1, 0], [1, 1]])
+    W = g.standard_normal((E, 2 * I, H)).astype(np.float32)
+    W_gate0 = W.copy()
+    W_gate0[:, :I] = 0
+    assert not oracle.gate_up_swiglu(x, W_gate0, ids, E).any()
+    W_up_const = W.copy()
+    W_up_const[:, I:] = 0
+    W_up_const[:, I:, 0] = 1.0                     # up = x[:, 0] for every j
+    act = oracle.gate_up_swiglu(x, W_up_const, ids, E)
+    xf = oracle.bf16_to_f32(x).astype(np.float64)
+    gate = np.stack([xf[p // 2] @ W[ids.reshape(-1)[p], :I].astype(np.float64).T
+                     for p in range(6)])
+    want = gate / (1 + np.exp(-gate)) * xf[np.arange(6) // 2, :1]
+    np.testing.assert_allclose(act, want, rtol=1e-12, atol=1e-12)
+
+
+def test_combine_one_hot_and_uniform():
+    g = np.random.default_rng(2)
+    rows, topk, H = 4, 3, 7
+    y = g.standard_normal((rows * topk, H))
+    w = np.zeros((rows, topk), np.float32)
+    pick = np.array([2, 0, 1, 2])
+    w[np.arange(rows), pick] = 1.0
+    np.testing.assert_array_equal(oracle.combine(y, topk, w), y[np.arange(rows) * topk + pick])
+    same = np.repeat(g.standard_normal((rows, 1, H)), topk, axis=1).reshape(rows * topk, H)
+    u = np.full((rows, topk), 0.25, np.float32)
+    np.testing.assert_allclose(oracle.combine(same, topk, u), same[::topk] * 0.75, rtol=1e-15)
+    np.testing.assert_allclose(oracle.combine(y, topk), y.reshape(rows, topk, H).sum(1))
+
+
+def test_down_combine_brute_force():
+    g = np.random.default_rng(3)
+    E, I, H, rows, topk = 3, 64, 5, 2, 2
+    act = wl.draw_bf16(g, (rows * topk, I))
+    W = g.standard_normal((E, H, I)).astype(np.float32)
+    ids = np.array([[2, 0], [1, 2]])
+    w = np.array([[0.75, 0.25], [0.5, 0.5]], np.float32)
+    af = oracle.bf16_to_f32(act).astype(np.float64)
+    want = np.zeros((rows, H))
+    for t in range(rows):
+        for s in range(topk):
+            p = t * topk + s
+            for n in range(H):
+                want[t, n] += float(w[t, s]) * sum(af[p, i] * float(W[ids[t, s], n, i])
+                                                   for i in range(I))
+    np.testing.assert_allclose(oracle.down_combine(act, W, ids, E, w), want, rtol=1e-12,
+                               atol=1e-12)
