@@ -20,7 +20,9 @@ __all__ = [
     "GQError", "load_library", "library_path", "EXPORTED_SYMBOLS", "TILE_M",
     "gq_route_max_tiles", "gq_route_sort", "gq_nf4_decode", "gq_mxfp4_decode",
     "gq_nf4_grouped_gemv", "gq_mxfp4_grouped_gemv", "gq_nf4_grouped_gemm",
-    "gq_mxfp4_grouped_gemm", "gq_nf4_grouped_dgrad", "gq_mxfp4_grouped_dgrad", "Route",
+    "gq_mxfp4_grouped_gemm", "gq_nf4_grouped_dgrad", "gq_mxfp4_grouped_dgrad",
+    "gq_nf4_grouped_gemv_swiglu", "gq_nf4_grouped_gemm_swiglu", "gq_nf4_grouped_gemv_down_combine",
+    "gq_moe_combine", "Route",
 ]
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
@@ -30,6 +32,8 @@ EXPORTED_SYMBOLS = (
     "gq_status_string", "gq_route_max_tiles", "gq_route_sort", "gq_nf4_decode",
     "gq_mxfp4_decode", "gq_nf4_grouped_gemv", "gq_mxfp4_grouped_gemv", "gq_nf4_grouped_gemm",
     "gq_mxfp4_grouped_gemm", "gq_nf4_grouped_dgrad", "gq_mxfp4_grouped_dgrad",
+    "gq_nf4_grouped_gemv_swiglu", "gq_nf4_grouped_gemm_swiglu", "gq_nf4_grouped_gemv_down_combine",
+    "gq_moe_combine",
 )
 
 _i32, _i64, _p = ctypes.c_int32, ctypes.c_int64, ctypes.c_void_p
@@ -51,6 +55,13 @@ _SIGNATURES = {
                                             _p, _p, _i32, _i32, _p, _p]),
     "gq_mxfp4_grouped_dgrad": (ctypes.c_int, [_p, _i32, _i32, _i64, _p, _p, _i32, _i32, _p, _p,
                                               _p, _p, _i32, _i32, _p, _p]),
+    "gq_nf4_grouped_gemv_swiglu": (ctypes.c_int, [_p, _i32, _i32, _i64, _p, _p, _i32, _i32, _p,
+                                                  _i32, _p, _p]),
+    "gq_nf4_grouped_gemm_swiglu": (ctypes.c_int, [_p, _i32, _i32, _i64, _p, _p, _i32, _i32, _i32,
+                                                  _p, _p, _p, _p, _i32, _i32, _p, _p]),
+    "gq_nf4_grouped_gemv_down_combine": (ctypes.c_int, [_p, _i32, _i32, _i64, _p, _p, _i32, _i32,
+                                                        _p, _i32, _p, _p, _p]),
+    "gq_moe_combine": (ctypes.c_int, [_p, _i32, _i32, _i32, _i64, _p, _p, _p]),
 }
 
 _lib = None
@@ -324,4 +335,80 @@ def gq_mxfp4_grouped_dgrad(dy, blocks, scales, route, out=None):
     st = lib.gq_mxfp4_grouped_dgrad(_ptr(dy), P, N, ds, _ptr(blocks), _ptr(scales), E, K,
                                     *_route_ptrs(route), _ptr(out), _stream(dy))
     _check(st, "gq_mxfp4_grouped_dgrad")
+    return out
+
+
+# ---- MoE-layer epilogues ----------------------------------------------------
+def gq_nf4_grouped_gemv_swiglu(x, codes, absmax, topk_ids, out=None):
+    """Decode gate_up GEMV with SwiGLU fused: codes [E, 2I, K] (gate rows first);
+    returns bf16 [rows*topk, I] = silu(gate) * up."""
+    lib = load_library()
+    rows, K, xs = _x_args(x)
+    E, N2, Kw = _nf4_bank(codes, absmax)
+    if Kw != K or N2 % 2:
+        raise ValueError("x and codes disagree on K, or the gate_up width is odd")
+    _dev(topk_ids, "topk_ids", torch.int32, 2)
+    P = topk_ids.numel()
+    out = _out(out, P, N2 // 2, x.device)
+    st = lib.gq_nf4_grouped_gemv_swiglu(_ptr(x), rows, K, xs, _ptr(codes), _ptr(absmax), E, N2,
+                                        _ptr(topk_ids), topk_ids.shape[1], _ptr(out), _stream(x))
+    _check(st, "gq_nf4_grouped_gemv_swiglu")
+    return out
+
+
+def gq_nf4_grouped_gemm_swiglu(x, codes, absmax, route, out=None):
+    """Prefill gate_up GEMM with SwiGLU fused; returns bf16 [rows*topk, I]."""
+    lib = load_library()
+    rows, K, xs = _x_args(x)
+    E, N2, Kw = _nf4_bank(codes, absmax)
+    if Kw != K or route.rows != rows or route.num_experts != E or N2 % 2:
+        raise ValueError("x, codes and route disagree")
+    P = rows * route.topk
+    out = _out(out, P, N2 // 2, x.device)
+    st = lib.gq_nf4_grouped_gemm_swiglu(_ptr(x), rows, K, xs, _ptr(codes), _ptr(absmax), E, N2,
+                                        route.topk, *_route_ptrs(route), _ptr(out), _stream(x))
+    _check(st, "gq_nf4_grouped_gemm_swiglu")
+    return out
+
+
+def _weights(topk_weights, rows, topk):
+    if topk_weights is None:
+        return None
+    _dev(topk_weights, "topk_weights", torch.float32)
+    if topk_weights.numel() != rows * topk:
+        raise ValueError("topk_weights must hold rows x topk floats")
+    return topk_weights
+
+
+def gq_nf4_grouped_gemv_down_combine(act, codes, absmax, topk_ids, topk_weights=None, out=None):
+    """Decode down GEMV with the router-weighted combine fused: act bf16 [rows*topk, I]
+    (row p is pair p's input), codes [E, H, I]; returns bf16 [rows, H]."""
+    lib = load_library()
+    P, I, a_s = _x_args(act, "act")
+    E, H, Iw = _nf4_bank(codes, absmax)
+    _dev(topk_ids, "topk_ids", torch.int32, 2)
+    rows, topk = topk_ids.shape
+    if Iw != I or rows * topk != P:
+        raise ValueError("act, codes and topk_ids disagree")
+    out = _out(out, rows, H, act.device)
+    st = lib.gq_nf4_grouped_gemv_down_combine(_ptr(act), rows, I, a_s, _ptr(codes), _ptr(absmax),
+                                              E, H, _ptr(topk_ids), topk,
+                                              _ptr(_weights(topk_weights, rows, topk)), _ptr(out),
+                                              _stream(act))
+    _check(st, "gq_nf4_grouped_gemv_down_combine")
+    return out
+
+
+def gq_moe_combine(y_pairs, topk, topk_weights=None, out=None):
+    """y[t] = sum_s w[t, s] * y_pairs[t*topk + s] (plain sum without weights);
+    y_pairs bf16 [rows*topk, H]; returns bf16 [rows, H]."""
+    lib = load_library()
+    P, H, ys = _x_args(y_pairs, "y_pairs")
+    if P % topk:
+        raise ValueError("y_pairs must hold rows*topk rows")
+    rows = P // topk
+    out = _out(out, rows, H, y_pairs.device)
+    st = lib.gq_moe_combine(_ptr(y_pairs), rows, topk, H, ys,
+                            _ptr(_weights(topk_weights, rows, topk)), _ptr(out), _stream(y_pairs))
+    _check(st, "gq_moe_combine")
     return out

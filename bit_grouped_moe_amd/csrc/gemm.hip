@@ -44,7 +44,9 @@ constexpr int kGemmThreads = 256;
 constexpr int kBStride = 72;      // bf16 per LDS row of B (64 + 8 pad: conflict-free 16-B reads)
 constexpr int kCStride = 80;      // bytes per LDS row of raw codes (dgrad staging)
 
-enum BMode { kFwdNF4 = 0, kFwdMX = 1, kDgradNF4 = 2, kDgradMX = 3 };
+// kFwdNF4Glu: NF4 forward on a fused gate_up weight (gate rows [0, I), up
+// rows [I, 2I)) whose epilogue writes SwiGLU(gate, up) = silu(gate) * up.
+enum BMode { kFwdNF4 = 0, kFwdMX = 1, kDgradNF4 = 2, kDgradMX = 3, kFwdNF4Glu = 4 };
 
 struct GemmArgs {
   const uint16_t* x;           // activations (forward) or output gradient (dgrad)
@@ -86,9 +88,17 @@ template <int kMode>
 __device__ __forceinline__ FwdLoad fwd_load(const GemmArgs& g, int e, int n0, int ks, int tid) {
   FwdLoad L;
   const int col = tid & (kTN - 1), h = tid >> 7;
-  const int n = n0 + col;
   const int k0 = ks * kTK + h * 32;
-  L.ok = n < g.Nw && k0 < g.Kw;
+  int n;
+  if constexpr (kMode == kFwdNF4Glu) {
+    // columns [0, 64): gate rows n0 + col; [64, 128): the matching up rows
+    const int j = n0 + (col & 63);
+    L.ok = j < g.Nout && k0 < g.Kw;
+    n = min(j, g.Nout - 1) + (col >= 64 ? g.Nout : 0);
+  } else {
+    n = n0 + col;
+    L.ok = n < g.Nw && k0 < g.Kw;
+  }
   const size_t row = (size_t)e * g.Nw + min(n, g.Nw - 1);
   const size_t kk = (size_t)min(k0, g.Kw - 32);
   L.c = *reinterpret_cast<const u32x4*>(g.codes + row * (size_t)(g.Kw / 2) + kk / 2);
@@ -236,6 +246,8 @@ __device__ __forceinline__ void dg_decode_chunk(const DgCodes& R, int c, const f
 template <int kMode>
 __device__ __forceinline__ void grouped_gemm_body(const GemmArgs& g) {
   constexpr bool kDg = kMode == kDgradNF4 || kMode == kDgradMX;
+  constexpr bool kGlu = kMode == kFwdNF4Glu;
+  constexpr int kTNo = kGlu ? kTN / 2 : kTN;               // output columns per tile
   __shared__ __attribute__((aligned(16))) uint16_t Bs[2][kTN * kBStride];
   __shared__ __attribute__((aligned(16))) uint8_t Cs[kDg ? 2 : 1][kDg ? kTK * kCStride : 16];
   __shared__ float As[kDg ? 2 : 1][kDg ? DgFmt<kMode>::kBlk * kTK : 1];
@@ -251,7 +263,7 @@ __device__ __forceinline__ void grouped_gemm_body(const GemmArgs& g) {
   const int logical = (q / C) * (8 * C) + xcd * C + (q % C);
   if (logical >= g.n_logical) return;
   const int tile = logical / C;
-  const int n0 = (logical % C) * kTN;
+  const int n0 = (logical % C) * kTNo;
   const int T = *g.num_tiles;
 
   if (tile >= T) {
@@ -260,8 +272,8 @@ __device__ __forceinline__ void grouped_gemm_body(const GemmArgs& g) {
     if (dstart >= g.P) return;
     if (dstart < 0) return;
     const int dvalid = min(kTM, g.P - dstart);
-    for (int idx = tid; idx < dvalid * (kTN / 8); idx += kGemmThreads) {
-      const int r = idx / (kTN / 8), c8 = idx % (kTN / 8);
+    for (int idx = tid; idx < dvalid * (kTNo / 8); idx += kGemmThreads) {
+      const int r = idx / (kTNo / 8), c8 = idx % (kTNo / 8);
       const int col = n0 + c8 * 8;
       const int p = g.sorted_pairs[dstart + r];
       if (col < g.Nout && (unsigned)p < (unsigned)g.P) {
@@ -296,7 +308,8 @@ __device__ __forceinline__ void grouped_gemm_body(const GemmArgs& g) {
   const uint16_t* a1 = g.x + (int64_t)row_s[ms1 * 32 + lr] * g.x_stride + lh * 32;
   const int nsteps = (g.Kc + kTK - 1) / kTK;
   const bool ktail = (g.Kc % kTK) != 0;                   // MXFP4 only: last step half full
-  const int ncols = min(kTN, g.Nout - n0);                 // multiple of 32
+  // valid B columns: the SwiGLU tile decodes all 128 (missing ones as zeros)
+  const int ncols = kGlu ? kTN : min(kTN, g.Nout - n0);     // multiple of 32
 
   f32x16 acc[2][4];
 #pragma unroll
@@ -428,6 +441,8 @@ __device__ __forceinline__ void grouped_gemm_body(const GemmArgs& g) {
   // stores instead of scattered 2-byte ones. ----
   constexpr int kOStride = kTN + 8;                         // padded row: conflict-free
   static_assert(4 * 32 * kOStride <= 2 * kTN * kBStride, "staging must fit in Bs");
+  constexpr int kChunks = kTNo / 8;                         // 16-byte chunks per tile row
+  const int ocols = min(kTNo, g.Nout - n0);                 // output columns of this tile
   lds_barrier();
   uint16_t* stage = &Bs[0][0] + wave * (32 * kOStride);
 #pragma unroll
@@ -439,17 +454,25 @@ __device__ __forceinline__ void grouped_gemm_body(const GemmArgs& g) {
       const int rr = (r >> 2) * 8 + lh * 4 + (r & 3);
       const int m = ms * 32 + rr;
       const float sc = (g.pair_scale && m < valid) ? g.pair_scale[pair_s[m]] : 1.f;
+      if constexpr (kGlu) {
+        // column blocks 0, 1 hold gate, 2, 3 the up values of the same outputs
 #pragma unroll
-      for (int c = 0; c < 4; ++c)
-        stage[rr * kOStride + c * 32 + lr] = f32_to_bf16_bits(acc[j][c][r] * sc);
+        for (int c = 0; c < 2; ++c)
+          stage[rr * kOStride + c * 32 + lr] =
+              f32_to_bf16_bits(silu_f32(acc[j][c][r]) * acc[j][c + 2][r] * sc);
+      } else {
+#pragma unroll
+        for (int c = 0; c < 4; ++c)
+          stage[rr * kOStride + c * 32 + lr] = f32_to_bf16_bits(acc[j][c][r] * sc);
+      }
     }
     // a wave's LDS operations complete in order: no barrier needed to read back
 #pragma unroll
-    for (int it = 0; it < 8; ++it) {
-      const int chunk = it * 64 + lane;                   // 32 rows x 16 chunks of 8 bf16
-      const int rr = chunk >> 4, c8 = chunk & 15;
+    for (int it = 0; it < 32 * kChunks / 64; ++it) {
+      const int chunk = it * 64 + lane;                   // 32 rows x kChunks chunks
+      const int rr = chunk / kChunks, c8 = chunk % kChunks;
       const int m = ms * 32 + rr;
-      if (m < valid && c8 * 8 < ncols) {
+      if (m < valid && c8 * 8 < ocols) {
         const u32x4 v = *reinterpret_cast<const u32x4*>(stage + rr * kOStride + c8 * 8);
         *reinterpret_cast<u32x4*>(g.out + (int64_t)pair_s[m] * g.Nout + n0 + c8 * 8) = v;
       }
@@ -473,7 +496,8 @@ static int launch_gemm(GemmArgs g, int32_t max_tiles, int32_t tile_m, hipStream_
   if (tile_m != kTM) return kNotSupported;
   const int64_t need = (int64_t)(g.P + kTM - 1) / kTM + g.E + 1;
   if (max_tiles < need) return kInvalid;
-  g.n_col_tiles = (g.Nout + kTN - 1) / kTN;
+  constexpr int kTNo = kMode == kFwdNF4Glu ? kTN / 2 : kTN;
+  g.n_col_tiles = (g.Nout + kTNo - 1) / kTNo;
   const int64_t n_logical = (int64_t)max_tiles * g.n_col_tiles;
   const int64_t group = 8LL * g.n_col_tiles;
   const int64_t grid = ((n_logical + group - 1) / group) * group;
@@ -501,14 +525,15 @@ static int common_gemm_checks(const uint16_t* x, int64_t x_stride, int32_t Kc,
   return kOk;
 }
 
-template <bool kMx>
+template <bool kMx, bool kGlu = false>
 static int forward_entry(const uint16_t* x, int32_t rows, int32_t K, int64_t x_stride,
                          const uint8_t* codes, const void* scl, int32_t E, int32_t N,
                          int32_t topk, const float* pair_scale, const int32_t* offsets,
                          const int32_t* sorted_pairs, const int32_t* tiles,
                          const int32_t* num_tiles, int32_t max_tiles, int32_t tile_m,
                          uint16_t* out, hipStream_t stream) {
-  if (rows < 0 || topk < 1 || E < 1 || N < 1 || N % 32 || K <= 0 || K % (kMx ? 32 : 64))
+  if (rows < 0 || topk < 1 || E < 1 || N < 1 || N % (kGlu ? 64 : 32) || K <= 0 ||
+      K % (kMx ? 32 : 64))
     return kInvalid;
   if (x_stride < K || x_stride % 8) return kInvalid;
   if (tile_m != kTM) return kNotSupported;
@@ -522,11 +547,12 @@ static int forward_entry(const uint16_t* x, int32_t rows, int32_t K, int64_t x_s
   if (pair_scale && !aligned4(pair_scale)) return kInvalid;
   GemmArgs g{};
   g.x = x; g.x_stride = x_stride; g.codes = codes; g.scl = scl;
-  g.Nw = N; g.Kw = K; g.Kc = K; g.Nout = N;
+  g.Nw = N; g.Kw = K; g.Kc = K; g.Nout = kGlu ? N / 2 : N;
   g.E = E; g.topk = topk; g.P = (int)P; g.pair_scale = pair_scale;
   g.offsets = offsets; g.sorted_pairs = sorted_pairs; g.tiles = tiles; g.num_tiles = num_tiles;
   g.out = out;
-  return launch_gemm<kMx ? kFwdMX : kFwdNF4>(g, max_tiles, tile_m, stream);
+  if constexpr (kGlu) return launch_gemm<kFwdNF4Glu>(g, max_tiles, tile_m, stream);
+  else return launch_gemm<kMx ? kFwdMX : kFwdNF4>(g, max_tiles, tile_m, stream);
 }
 
 }  // namespace gq
@@ -541,6 +567,18 @@ extern "C" int gq_nf4_grouped_gemm(const uint16_t* x, int32_t rows, int32_t K, i
   return gq::forward_entry<false>(x, rows, K, x_stride, codes, absmax, num_experts, N, topk,
                                   pair_scale, expert_offsets, sorted_pairs, tiles, num_tiles,
                                   max_tiles, tile_m, out, stream);
+}
+
+extern "C" int gq_nf4_grouped_gemm_swiglu(const uint16_t* x, int32_t rows, int32_t K,
+                                          int64_t x_stride, const uint8_t* codes,
+                                          const float* absmax, int32_t num_experts, int32_t N,
+                                          int32_t topk, const int32_t* expert_offsets,
+                                          const int32_t* sorted_pairs, const int32_t* tiles,
+                                          const int32_t* num_tiles, int32_t max_tiles,
+                                          int32_t tile_m, uint16_t* act, hipStream_t stream) {
+  return gq::forward_entry<false, true>(x, rows, K, x_stride, codes, absmax, num_experts, N, topk,
+                                        nullptr, expert_offsets, sorted_pairs, tiles, num_tiles,
+                                        max_tiles, tile_m, act, stream);
 }
 
 extern "C" int gq_mxfp4_grouped_gemm(const uint16_t* x, int32_t rows, int32_t K,

@@ -23,6 +23,8 @@
 //    ldexp.  Both keep the decoded weight exact (float32).
 //  * partial sums are reduced in a fixed order (DPP lane moves inside a wave,
 //    LDS across waves): no atomics, bitwise reproducible.
+#include <algorithm>
+
 #include "gq_device.hpp"
 #include "gq_host.hpp"
 #include "../../include/gq.h"
@@ -73,7 +75,7 @@ __device__ __forceinline__ float segment_dot(const float* lut, u32x4 c, float am
 // kWaveRows: a row's S segments lie inside one wave (64 % S == 0) and are
 // summed with DPP lane moves; otherwise partial sums meet in LDS.  Both
 // orders are fixed, so results are reproducible.
-template <bool kMx, int kIter, bool kWaveRows>
+template <bool kMx, int kIter, bool kWaveRows, bool kGlu>
 __global__ __launch_bounds__(kGemvMaxThreads) void grouped_gemv_kernel(
     const uint16_t* __restrict__ x, int64_t x_stride, int K, const uint8_t* __restrict__ codes,
     const void* __restrict__ scl, int N, int E, const int32_t* __restrict__ ids, int topk, int P,
@@ -85,11 +87,25 @@ __global__ __launch_bounds__(kGemvMaxThreads) void grouped_gemv_kernel(
   const int tid = threadIdx.x;                      // NT == blockDim.x
   const int lane = tid & (kWave - 1);
   const int p0 = blockIdx.y;
-  const int R = G * kIter;
-  const int n0 = blockIdx.x * R;
+  const int R = G * kIter;                          // weight rows per workgroup
+  // kGlu: the weight holds gate rows [0, N/2) then up rows [N/2, N); a
+  // workgroup takes output columns [n0, n0 + R/2) and both halves' rows.
+  constexpr int kHalf = kIter / 2;
+  const int Nout = kGlu ? N / 2 : N;                // output columns per pair
+  const int Rout = kGlu ? R / 2 : R;
+  const int n0 = blockIdx.x * Rout;
   const int g = tid / W;                            // row slot
   const int s = tid - g * W;                        // segment
   const bool active = kWaveRows ? s < S : tid < S * G;
+  // weight row of row slot gg, iteration i (clamped into the matrix)
+  auto wrow = [&](int gg, int i) -> int {
+    if constexpr (kGlu) {
+      const int j = min(n0 + gg + G * (i % kHalf), Nout - 1);
+      return i < kHalf ? j : Nout + j;
+    } else {
+      return min(n0 + gg + G * i, N - 1);
+    }
+  };
 
   // ---- round trip 1: expert of p0, routing table (per wave), p0's activations ----
   const int e = ids[p0];
@@ -107,8 +123,8 @@ __global__ __launch_bounds__(kGemvMaxThreads) void grouped_gemv_kernel(
     for (int v = 0; v < 4; ++v) xr[v] = xp[v];
   }
   if ((unsigned)e >= (unsigned)E) {          // dropped pair: its slice is zero
-    for (int r = tid; r < R; r += NT)
-      if (n0 + r < N) out[(int64_t)p0 * N + n0 + r] = 0;
+    for (int r = tid; r < Rout; r += NT)
+      if (n0 + r < Nout) out[(int64_t)p0 * Nout + n0 + r] = 0;
     return;
   }
 
@@ -123,8 +139,7 @@ __global__ __launch_bounds__(kGemvMaxThreads) void grouped_gemv_kernel(
   const int s_cl = active ? s : 0;
 #pragma unroll
   for (int i = 0; i < kIter; ++i) {
-    const int n = min(n0 + g + G * i, N - 1);
-    const size_t row = (size_t)e * N + n;
+    const size_t row = (size_t)e * N + wrow(g, i);
     cw[i] = *reinterpret_cast<const u32x4*>(codes + row * row_bytes + (size_t)s_cl * 16);
     if constexpr (kMx) {
       sb[i] = (uint32_t)static_cast<const uint8_t*>(scl)[row * (size_t)(K / 32) + s_cl];
@@ -158,6 +173,10 @@ __global__ __launch_bounds__(kGemvMaxThreads) void grouped_gemv_kernel(
         const float part = active ? segment_dot<kMx>(lut, cw[i], am[i], sb[i], xf) : 0.f;
         vals[i] = group_sum_last(part, W);                     // total on lane s == W-1
       }
+      if constexpr (kGlu) {
+#pragma unroll
+        for (int i = 0; i < kHalf; ++i) vals[i] = silu_f32(vals[i]) * vals[i + kHalf];
+      }
     } else {
       constexpr int kStride = kGemvMaxThreads + 32;            // pad: spreads banks
 #pragma unroll
@@ -166,7 +185,7 @@ __global__ __launch_bounds__(kGemvMaxThreads) void grouped_gemv_kernel(
       lds_barrier();
       vals[0] = 0.f;
       if (tid < R) {                                           // R <= NT (host check)
-        const int gg = tid % G, ii = tid / G;
+        const int gg = tid % G, ii = tid / G;                  // weight row wrow(gg, ii)
         const float* src = red + ii * kStride + gg * S;
         float s0 = 0.f, s1 = 0.f, s2 = 0.f, s3 = 0.f;          // fixed order, 4 chains
         int j = 0;
@@ -180,19 +199,25 @@ __global__ __launch_bounds__(kGemvMaxThreads) void grouped_gemv_kernel(
         vals[0] = (s0 + s1) + (s2 + s3);
       }
       lds_barrier();
+      if constexpr (kGlu) {                  // gate row r pairs with up row r + R/2
+        if (tid < R) red[tid] = vals[0];
+        lds_barrier();
+        vals[0] = tid < Rout ? silu_f32(red[tid]) * red[tid + Rout] : 0.f;
+        lds_barrier();
+      }
     }
   };
   auto store_pair = [&](int p) {
     const float sc = pair_scale ? pair_scale[p] : 1.f;
     if constexpr (kWaveRows) {
 #pragma unroll
-      for (int i = 0; i < kIter; ++i) {
+      for (int i = 0; i < (kGlu ? kHalf : kIter); ++i) {
         const int n = n0 + g + G * i;
-        if (s == W - 1 && n < N) out[(int64_t)p * N + n] = f32_to_bf16_bits(vals[i] * sc);
+        if (s == W - 1 && n < Nout) out[(int64_t)p * Nout + n] = f32_to_bf16_bits(vals[i] * sc);
       }
     } else {
       const int n = n0 + tid;
-      if (tid < R && n < N) out[(int64_t)p * N + n] = f32_to_bf16_bits(vals[0] * sc);
+      if (tid < Rout && n < Nout) out[(int64_t)p * Nout + n] = f32_to_bf16_bits(vals[0] * sc);
     }
   };
 
@@ -230,20 +255,35 @@ __global__ __launch_bounds__(kGemvMaxThreads) void grouped_gemv_kernel(
   }
 }
 
-template <bool kMx, int kIter>
+template <bool kMx, int kIter, bool kGlu>
 static void launch_gemv_iter(dim3 grid, int NT, hipStream_t stream, const uint16_t* x,
                              int64_t x_stride, int K, const uint8_t* codes, const void* scl,
                              int N, int E, const int32_t* ids, int topk, int P,
                              const float* pair_scale, uint16_t* out, int S, int W, int G) {
   if (S <= kWave)
-    hipLaunchKernelGGL((grouped_gemv_kernel<kMx, kIter, true>), grid, dim3(NT), 0, stream, x,
-                       x_stride, K, codes, scl, N, E, ids, topk, P, pair_scale, out, S, W, G, NT);
+    hipLaunchKernelGGL((grouped_gemv_kernel<kMx, kIter, true, kGlu>), grid, dim3(NT), 0, stream,
+                       x, x_stride, K, codes, scl, N, E, ids, topk, P, pair_scale, out, S, W, G,
+                       NT);
   else
-    hipLaunchKernelGGL((grouped_gemv_kernel<kMx, kIter, false>), grid, dim3(NT), 0, stream, x,
-                       x_stride, K, codes, scl, N, E, ids, topk, P, pair_scale, out, S, W, G, NT);
+    hipLaunchKernelGGL((grouped_gemv_kernel<kMx, kIter, false, kGlu>), grid, dim3(NT), 0, stream,
+                       x, x_stride, K, codes, scl, N, E, ids, topk, P, pair_scale, out, S, W, G,
+                       NT);
 }
 
-template <bool kMx>
+// Segment lanes: S segments of 32 weights per row.  S <= 64: a row's
+// segments go to a group of W = S rounded up to a power of two lanes inside
+// one wave (lanes s >= S idle); longer rows: S consecutive threads, reduced
+// through LDS.
+static void segment_layout(int K, int& S, int& W, int& G, int& NT) {
+  S = K / 32;
+  W = S;
+  if (S <= kWave)
+    while (W & (W - 1)) W += W & -W;
+  G = S > kWave ? (S >= kGemvMaxThreads ? 1 : kGemvMaxThreads / S) : kGemvMaxThreads / W;
+  NT = S > kWave ? ((S * G + kWave - 1) / kWave) * kWave : kGemvMaxThreads;
+}
+
+template <bool kMx, bool kGlu>
 static int launch_gemv(const uint16_t* x, int32_t rows, int32_t K, int64_t x_stride,
                        const uint8_t* codes, const void* scl, int32_t E, int32_t N,
                        const int32_t* ids, int32_t topk, const float* pair_scale, uint16_t* out,
@@ -251,21 +291,15 @@ static int launch_gemv(const uint16_t* x, int32_t rows, int32_t K, int64_t x_str
   if (!x || !codes || !scl || !ids || !out) return kInvalid;
   if (rows < 1 || topk < 1 || E < 1 || N < 1 || K <= 0) return kInvalid;
   if (K % (kMx ? 32 : 64)) return kInvalid;
+  if (kGlu && N % 2) return kInvalid;
   if (x_stride < K || x_stride % 8) return kInvalid;
   if (!aligned16(x) || !aligned16(codes) || !aligned4(ids) || !aligned4(out)) return kInvalid;
   if (!kMx && !aligned4(scl)) return kInvalid;
   if (pair_scale && !aligned4(pair_scale)) return kInvalid;
   const int64_t P = (int64_t)rows * topk;
   if (P > kGemvMaxPairs || K > kGemvMaxK || N >= (1 << 24)) return kNotSupported;
-  // S segments of 32 weights per row.  S <= 64: a row's segments go to a
-  // group of W = S rounded up to a power of two lanes inside one wave (lanes
-  // s >= S idle); longer rows: S consecutive threads, reduced through LDS.
-  const int S = K / 32;
-  int W = S;
-  if (S <= kWave)
-    while (W & (W - 1)) W += W & -W;
-  const int G = S > kWave ? (S >= kGemvMaxThreads ? 1 : kGemvMaxThreads / S) : kGemvMaxThreads / W;
-  const int NT = S > kWave ? ((S * G + kWave - 1) / kWave) * kWave : kGemvMaxThreads;
+  int S, W, G, NT;
+  segment_layout(K, S, W, G, NT);
   // Rows per thread: the largest count (8, 4, 2) that still gives enough
   // workgroups.  With in-wave reductions many small workgroups stream better
   // (about eight per CU: on the one-token gate_up GEMV 1536 workgroups of 2
@@ -278,14 +312,177 @@ static int launch_gemv(const uint16_t* x, int32_t rows, int32_t K, int64_t x_str
   if (S > kWave && R > NT) return kNotSupported;     // one reduced row per thread
   const dim3 grid((N + R - 1) / R, (unsigned)P);
   switch (iter) {
-    case 8: launch_gemv_iter<kMx, 8>(grid, NT, stream, x, x_stride, K, codes, scl, N, E, ids,
-                                     topk, (int)P, pair_scale, out, S, W, G); break;
-    case 4: launch_gemv_iter<kMx, 4>(grid, NT, stream, x, x_stride, K, codes, scl, N, E, ids,
-                                     topk, (int)P, pair_scale, out, S, W, G); break;
-    default: launch_gemv_iter<kMx, 2>(grid, NT, stream, x, x_stride, K, codes, scl, N, E, ids,
-                                      topk, (int)P, pair_scale, out, S, W, G); break;
+    case 8: launch_gemv_iter<kMx, 8, kGlu>(grid, NT, stream, x, x_stride, K, codes, scl, N, E,
+                                           ids, topk, (int)P, pair_scale, out, S, W, G); break;
+    case 4: launch_gemv_iter<kMx, 4, kGlu>(grid, NT, stream, x, x_stride, K, codes, scl, N, E,
+                                           ids, topk, (int)P, pair_scale, out, S, W, G); break;
+    default: launch_gemv_iter<kMx, 2, kGlu>(grid, NT, stream, x, x_stride, K, codes, scl, N, E,
+                                            ids, topk, (int)P, pair_scale, out, S, W, G); break;
   }
   return launch_status();
+}
+
+// ---------------------------------------------------------------------------
+// Down projection of every routed pair with the router-weighted combine
+// fused in (decode: a few tokens).  y[t, n] = sum_s w[t, s] * (act[t*k+s] .
+// W_{ids[t, s]}[n, :]), slots in order, float32, one bf16 rounding.
+//
+// A workgroup owns output rows [n0, n0 + Rb) for EVERY pair, so a token's
+// k products meet in its LDS and are reduced there: no atomics, no second
+// launch.  Lane groups (W lanes, as in the GEMV) take (pair, row) combos;
+// each combo is one 16-byte weight segment per lane plus the pair's 64-byte
+// activation slice.  A pair whose expert is outside [0, E) contributes 0.
+constexpr int kCombineMaxPairs = 64;
+constexpr int kCombineMaxCombos = 512;
+
+template <bool kMx, int kIt>
+__global__ __launch_bounds__(kGemvMaxThreads) void gemv_down_combine_kernel(
+    const uint16_t* __restrict__ act, int64_t a_stride, int I, const uint8_t* __restrict__ codes,
+    const void* __restrict__ scl, int H, int E, const int32_t* __restrict__ ids, int topk, int P,
+    const float* __restrict__ tw, uint16_t* __restrict__ y, int S, int W, int G, int Rb) {
+  __shared__ float lut[16];
+  __shared__ float ys[kCombineMaxCombos];
+
+  const int tid = threadIdx.x;
+  const int n0 = blockIdx.x * Rb;
+  const int g = tid / W, s = tid - g * W;
+  const bool active = s < S;
+  const int s_cl = active ? s : 0;
+  const int C = P * Rb;                                    // combos (pair-major)
+
+  // ---- round trip 1: the combos' experts and activation slices ----
+  int pp[kIt], rr[kIt], ee[kIt];
+  u32x4 xr[kIt][4];
+#pragma unroll
+  for (int it = 0; it < kIt; ++it) {
+    const int c = min(g + G * it, C - 1);                  // clamped: surplus combos repeat
+    pp[it] = c / Rb;
+    rr[it] = c - pp[it] * Rb;
+    ee[it] = ids[pp[it]];
+    const u32x4* ap = reinterpret_cast<const u32x4*>(act + (int64_t)pp[it] * a_stride + s_cl * 32);
+#pragma unroll
+    for (int v = 0; v < 4; ++v) xr[it][v] = ap[v];
+  }
+  // ---- round trip 2: weight segments (dropped pairs read expert 0) ----
+  const size_t row_bytes = (size_t)I / 2;
+  u32x4 cw[kIt];
+  float am[kIt];
+  uint32_t sb[kIt];
+#pragma unroll
+  for (int it = 0; it < kIt; ++it) {
+    const int e = (unsigned)ee[it] < (unsigned)E ? ee[it] : 0;
+    const size_t row = (size_t)e * H + min(n0 + rr[it], H - 1);
+    cw[it] = *reinterpret_cast<const u32x4*>(codes + row * row_bytes + (size_t)s_cl * 16);
+    if constexpr (kMx) {
+      sb[it] = (uint32_t)static_cast<const uint8_t*>(scl)[row * (size_t)(I / 32) + s_cl];
+      am[it] = 0.f;
+    } else {
+      am[it] = static_cast<const float*>(scl)[row * (size_t)(I / 64) + s_cl / 2];
+      sb[it] = 0u;
+    }
+  }
+  if constexpr (!kMx) {
+    nf4_lut_init(lut, tid);
+    lds_barrier();
+  }
+#pragma unroll
+  for (int it = 0; it < kIt; ++it) {
+    float xf[32];
+#pragma unroll
+    for (int v = 0; v < 4; ++v)
+#pragma unroll
+      for (int cc = 0; cc < 4; ++cc) {
+        xf[8 * v + 2 * cc] = bf16lo_to_f32(xr[it][v][cc]);
+        xf[8 * v + 2 * cc + 1] = bf16hi_to_f32(xr[it][v][cc]);
+      }
+    const float part = active ? segment_dot<kMx>(lut, cw[it], am[it], sb[it], xf) : 0.f;
+    const float tot = group_sum_last(part, W);
+    const int c = g + G * it;
+    if (s == W - 1 && c < C) ys[c] = (unsigned)ee[it] < (unsigned)E ? tot : 0.f;
+  }
+  lds_barrier();
+  // ---- combine: thread (t, r) sums its token's slots in order ----
+  const int rows = P / topk;
+  for (int idx = tid; idx < rows * Rb; idx += kGemvMaxThreads) {
+    const int t = idx / Rb, r = idx - t * Rb;
+    const int n = n0 + r;
+    if (n >= H) continue;
+    float acc = 0.f;
+    for (int sl = 0; sl < topk; ++sl) {
+      const int p = t * topk + sl;
+      const float w = tw ? tw[p] : 1.f;
+      acc = __builtin_fmaf(w, ys[p * Rb + r], acc);
+    }
+    y[(int64_t)t * H + n] = f32_to_bf16_bits(acc);
+  }
+}
+
+template <bool kMx>
+static int launch_down_combine(const uint16_t* act, int32_t rows, int32_t I, int64_t a_stride,
+                               const uint8_t* codes, const void* scl, int32_t E, int32_t H,
+                               const int32_t* ids, int32_t topk, const float* tw, uint16_t* y,
+                               hipStream_t stream) {
+  if (!act || !codes || !scl || !ids || !y) return kInvalid;
+  if (rows < 1 || topk < 1 || E < 1 || H < 1 || I <= 0 || I % (kMx ? 32 : 64)) return kInvalid;
+  if (a_stride < I || a_stride % 8) return kInvalid;
+  if (!aligned16(act) || !aligned16(codes) || !aligned4(ids) || !aligned4(y)) return kInvalid;
+  if (!kMx && !aligned4(scl)) return kInvalid;
+  if (tw && !aligned4(tw)) return kInvalid;
+  const int64_t P = (int64_t)rows * topk;
+  if (P > kCombineMaxPairs || I > 32 * kWave || H >= (1 << 24)) return kNotSupported;
+  int S, W, G, NT;
+  segment_layout(I, S, W, G, NT);
+  // rows per workgroup: about two combos per lane group
+  const int Rb = (int)std::max<int64_t>(1, (2 * G) / P);
+  const int64_t C = P * Rb;
+  const int64_t need = (C + G - 1) / G;
+  const dim3 grid((H + Rb - 1) / Rb);
+  if (need <= 1)
+    hipLaunchKernelGGL((gemv_down_combine_kernel<kMx, 1>), grid, dim3(kGemvMaxThreads), 0,
+                       stream, act, a_stride, I, codes, scl, H, E, ids, topk, (int)P, tw, y, S, W,
+                       G, Rb);
+  else if (need <= 2)
+    hipLaunchKernelGGL((gemv_down_combine_kernel<kMx, 2>), grid, dim3(kGemvMaxThreads), 0,
+                       stream, act, a_stride, I, codes, scl, H, E, ids, topk, (int)P, tw, y, S, W,
+                       G, Rb);
+  else if (need <= 4)
+    hipLaunchKernelGGL((gemv_down_combine_kernel<kMx, 4>), grid, dim3(kGemvMaxThreads), 0,
+                       stream, act, a_stride, I, codes, scl, H, E, ids, topk, (int)P, tw, y, S, W,
+                       G, Rb);
+  else if (need <= 8)
+    hipLaunchKernelGGL((gemv_down_combine_kernel<kMx, 8>), grid, dim3(kGemvMaxThreads), 0,
+                       stream, act, a_stride, I, codes, scl, H, E, ids, topk, (int)P, tw, y, S, W,
+                       G, Rb);
+  else
+    return kNotSupported;
+  return launch_status();
+}
+
+// ---------------------------------------------------------------------------
+// Combine of per-pair outputs (prefill): y[t, :] = sum_s w[t, s] * yp[t*k+s, :]
+// in slot order, float32, one bf16 rounding.  Thread = 8 columns of a token.
+__global__ __launch_bounds__(256) void moe_combine_kernel(const uint16_t* __restrict__ yp,
+                                                          int64_t stride, int rows, int topk,
+                                                          int H, const float* __restrict__ tw,
+                                                          uint16_t* __restrict__ y) {
+  const int chunks = H / 8;
+  const int64_t idx = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  if (idx >= (int64_t)rows * chunks) return;
+  const int t = (int)(idx / chunks), c = (int)(idx - (int64_t)t * chunks);
+  float acc[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
+  for (int sl = 0; sl < topk; ++sl) {
+    const int64_t p = (int64_t)t * topk + sl;
+    const float w = tw ? tw[p] : 1.f;
+    const u32x4 v = *reinterpret_cast<const u32x4*>(yp + p * stride + c * 8);
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      acc[2 * q] = __builtin_fmaf(w, bf16lo_to_f32(v[q]), acc[2 * q]);
+      acc[2 * q + 1] = __builtin_fmaf(w, bf16hi_to_f32(v[q]), acc[2 * q + 1]);
+    }
+  }
+  const u32x4 o{pack_bf16x2(acc[0], acc[1]), pack_bf16x2(acc[2], acc[3]),
+                pack_bf16x2(acc[4], acc[5]), pack_bf16x2(acc[6], acc[7])};
+  *reinterpret_cast<u32x4*>(y + (int64_t)t * H + c * 8) = o;
 }
 
 }  // namespace gq
@@ -294,8 +491,43 @@ extern "C" int gq_nf4_grouped_gemv(const uint16_t* x, int32_t rows, int32_t K, i
                                    const uint8_t* codes, const float* absmax, int32_t num_experts,
                                    int32_t N, const int32_t* topk_ids, int32_t topk,
                                    const float* pair_scale, uint16_t* out, hipStream_t stream) {
-  return gq::launch_gemv<false>(x, rows, K, x_stride, codes, absmax, num_experts, N, topk_ids,
-                                topk, pair_scale, out, stream);
+  return gq::launch_gemv<false, false>(x, rows, K, x_stride, codes, absmax, num_experts, N,
+                                       topk_ids, topk, pair_scale, out, stream);
+}
+
+extern "C" int gq_nf4_grouped_gemv_swiglu(const uint16_t* x, int32_t rows, int32_t K,
+                                          int64_t x_stride, const uint8_t* codes,
+                                          const float* absmax, int32_t num_experts, int32_t N,
+                                          const int32_t* topk_ids, int32_t topk, uint16_t* act,
+                                          hipStream_t stream) {
+  return gq::launch_gemv<false, true>(x, rows, K, x_stride, codes, absmax, num_experts, N,
+                                      topk_ids, topk, nullptr, act, stream);
+}
+
+extern "C" int gq_nf4_grouped_gemv_down_combine(const uint16_t* act, int32_t rows, int32_t I,
+                                                int64_t act_stride, const uint8_t* codes,
+                                                const float* absmax, int32_t num_experts,
+                                                int32_t H, const int32_t* topk_ids, int32_t topk,
+                                                const float* topk_weights, uint16_t* y,
+                                                hipStream_t stream) {
+  return gq::launch_down_combine<false>(act, rows, I, act_stride, codes, absmax, num_experts, H,
+                                        topk_ids, topk, topk_weights, y, stream);
+}
+
+extern "C" int gq_moe_combine(const uint16_t* y_pairs, int32_t rows, int32_t topk, int32_t H,
+                              int64_t stride, const float* topk_weights, uint16_t* y,
+                              hipStream_t stream) {
+  using namespace gq;
+  if (rows < 0 || topk < 1 || H < 1 || H % 8 || stride < H || stride % 8) return kInvalid;
+  if (rows == 0) return kOk;
+  if (!y_pairs || !y || !aligned16(y_pairs) || !aligned16(y)) return kInvalid;
+  if (topk_weights && !aligned4(topk_weights)) return kInvalid;
+  const int64_t threads = (int64_t)rows * (H / 8);
+  const int64_t blocks = (threads + 255) / 256;
+  if (blocks > INT32_MAX || (int64_t)rows * topk >= INT32_MAX) return kNotSupported;
+  hipLaunchKernelGGL(moe_combine_kernel, dim3((unsigned)blocks), dim3(256), 0, stream, y_pairs,
+                     stride, rows, topk, H, topk_weights, y);
+  return launch_status();
 }
 
 extern "C" int gq_mxfp4_grouped_gemv(const uint16_t* x, int32_t rows, int32_t K, int64_t x_stride,
@@ -303,6 +535,6 @@ extern "C" int gq_mxfp4_grouped_gemv(const uint16_t* x, int32_t rows, int32_t K,
                                      int32_t num_experts, int32_t N, const int32_t* topk_ids,
                                      int32_t topk, const float* pair_scale, uint16_t* out,
                                      hipStream_t stream) {
-  return gq::launch_gemv<true>(x, rows, K, x_stride, blocks, scales, num_experts, N, topk_ids,
-                               topk, pair_scale, out, stream);
+  return gq::launch_gemv<true, false>(x, rows, K, x_stride, blocks, scales, num_experts, N,
+                                      topk_ids, topk, pair_scale, out, stream);
 }

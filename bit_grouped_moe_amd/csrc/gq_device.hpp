@@ -117,6 +117,9 @@ __device__ __forceinline__ void nf4_decode8_bf16(const float* lut, uint32_t d, f
   for (int b = 0; b < 4; ++b) out[b] = pack_bf16x2(q[2 * b] * absmax, q[2 * b + 1] * absmax);
 }
 
+// SiLU, z * sigmoid(z), in float32.
+__device__ __forceinline__ float silu_f32(float z) { return z / (1.0f + expf(-z)); }
+
 // ---- MXFP4 ---------------------------------------------------------------
 // Byte j of a 16-byte block holds element 2j in its low nibble, 2j+1 in its
 // high nibble.  e2m1 -> float32 is exact; the e8m0 factor 2^(s-127) is then

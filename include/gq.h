@@ -226,6 +226,64 @@ int gq_mxfp4_grouped_dgrad(const uint16_t* dy, int32_t P, int32_t N, int64_t dy_
                            const int32_t* tiles, const int32_t* num_tiles, int32_t max_tiles,
                            int32_t tile_m, uint16_t* dx, hipStream_t stream);
 
+/* ------------------------------------------------------------------------
+ * MoE-layer epilogues.  The pages benchmark the grouped products on the
+ * Qwen3-30B-A3B expert shapes, whose experts are SwiGLU MLPs; [P1] header
+ * (one launch for the active experts) and [P4] "Functions" ([M, top_k]
+ * routing, per-slot [M, top_k, N] outputs that the caller reduces over
+ * top_k).  The pages leave the activation and the reduction to the caller;
+ * these entry points fuse them (readings: gate rows [0, I) then up rows
+ * [I, 2I) in a fused gate_up weight; SwiGLU act = silu(gate) * up with
+ * silu(z) = z / (1 + exp(-z)); combine = router-weighted sum over a
+ * token's slots, in slot order).  All arithmetic float32, one bf16
+ * rounding per output.
+ *
+ * gq_nf4_grouped_gemv_swiglu / gq_nf4_grouped_gemm_swiglu:
+ *   act[p, j] = bf16( silu(g) * u ),  g = sum_k x[p/topk, k] * W[j, k],
+ *                                     u = sum_k x[p/topk, k] * W[I + j, k]
+ *   codes/absmax [E, N, K] with N = 2I; act uint16 bf16 [rows*topk, I].
+ *   Arguments, grouping and errors as gq_nf4_grouped_gemv / _gemm without
+ *   pair_scale; InvalidValue also for N odd (GEMV) or N % 64 (GEMM).
+ *
+ * gq_nf4_grouped_gemv_down_combine (decode, rows*topk <= 64):
+ *   y[t, n] = bf16( sum_s w[t, s] * sum_i act[t*topk + s, i] * W_{ids[t, s]}[n, i] )
+ *   act   uint16 bf16 [rows*topk, I], row stride act_stride elements
+ *   codes/absmax [E, H, I] NF4 (I % 64 == 0); topk_weights float [rows, topk]
+ *   or NULL (weights 1); y uint16 bf16 [rows, H].  A slot whose expert is
+ *   outside [0, E) contributes 0.
+ *   InvalidValue: null pointer (topk_weights may be NULL), rows < 1,
+ *     topk < 1, E < 1, H < 1, I not a positive multiple of 64, bad stride
+ *     or alignment.  NotSupported: rows*topk > 64, I > 2048, H >= 2^24,
+ *     or more than 8 (pair, row) products per lane group (I = 2048 with
+ *     rows*topk > 32).
+ *
+ * gq_moe_combine (prefill):
+ *   y[t, :] = bf16( sum_s w[t, s] * y_pairs[t*topk + s, :] )
+ *   y_pairs uint16 bf16 [rows*topk, H] (row stride `stride` elements);
+ *   topk_weights float [rows, topk] or NULL (plain sum, e.g. when the
+ *   router weight was applied as pair_scale); y uint16 bf16 [rows, H].
+ *   InvalidValue: rows < 0, topk < 1, H < 1 or H % 8, stride < H or
+ *   stride % 8, null or misaligned pointers.  rows == 0 enqueues nothing.
+ */
+int gq_nf4_grouped_gemv_swiglu(const uint16_t* x, int32_t rows, int32_t K, int64_t x_stride,
+                               const uint8_t* codes, const float* absmax, int32_t num_experts,
+                               int32_t N, const int32_t* topk_ids, int32_t topk, uint16_t* act,
+                               hipStream_t stream);
+int gq_nf4_grouped_gemm_swiglu(const uint16_t* x, int32_t rows, int32_t K, int64_t x_stride,
+                               const uint8_t* codes, const float* absmax, int32_t num_experts,
+                               int32_t N, int32_t topk, const int32_t* expert_offsets,
+                               const int32_t* sorted_pairs, const int32_t* tiles,
+                               const int32_t* num_tiles, int32_t max_tiles, int32_t tile_m,
+                               uint16_t* act, hipStream_t stream);
+int gq_nf4_grouped_gemv_down_combine(const uint16_t* act, int32_t rows, int32_t I,
+                                     int64_t act_stride, const uint8_t* codes,
+                                     const float* absmax, int32_t num_experts, int32_t H,
+                                     const int32_t* topk_ids, int32_t topk,
+                                     const float* topk_weights, uint16_t* y,
+                                     hipStream_t stream);
+int gq_moe_combine(const uint16_t* y_pairs, int32_t rows, int32_t topk, int32_t H,
+                   int64_t stride, const float* topk_weights, uint16_t* y, hipStream_t stream);
+
 #ifdef __cplusplus
 }
 #endif

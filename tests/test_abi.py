@@ -183,3 +183,34 @@ def test_probe_library_exports_its_header():
     assert plib.gq_probe_copy(F2, F, 16, None) == INVALID         # misaligned source
     assert plib.gq_probe_copy(NULL, F, 16, None) == INVALID
     assert plib.gq_probe_copy(F, F, 0, None) == INVALID
+
+
+def test_epilogue_entry_points_reject(lib):
+    # SwiGLU GEMV: odd gate_up width, bad K
+    assert lib.gq_nf4_grouped_gemv_swiglu(F, 1, 2048, 2048, F, F, 128, 1535, F, 8, F, None) == INVALID
+    assert lib.gq_nf4_grouped_gemv_swiglu(F, 1, 2040, 2048, F, F, 128, 1536, F, 8, F, None) == INVALID
+    assert lib.gq_nf4_grouped_gemv_swiglu(NULL, 1, 2048, 2048, F, F, 128, 1536, F, 8, F,
+                                          None) == INVALID
+    # SwiGLU GEMM: N % 64, tile_m
+    assert lib.gq_nf4_grouped_gemm_swiglu(F, 4096, 2048, 2048, F, F, 128, 1568, 8, F, F, F, F,
+                                          257, 256, F, None) == INVALID
+    assert lib.gq_nf4_grouped_gemm_swiglu(F, 4096, 2048, 2048, F, F, 128, 1536, 8, F, F, F, F,
+                                          257, 128, F, None) == NOT_SUPPORTED
+    assert lib.gq_nf4_grouped_gemm_swiglu(F, 0, 2048, 2048, F, F, 128, 1536, 8, F, F, F, F,
+                                          129, 256, F, None) == 0
+    # down + combine: I % 64, too many pairs, I beyond one wave of segments
+    assert lib.gq_nf4_grouped_gemv_down_combine(F, 1, 736, 736, F, F, 128, 2048, F, 8, NULL, F,
+                                                None) == INVALID
+    assert lib.gq_nf4_grouped_gemv_down_combine(F, 9, 768, 768, F, F, 128, 2048, F, 8, NULL, F,
+                                                None) == NOT_SUPPORTED
+    assert lib.gq_nf4_grouped_gemv_down_combine(F, 1, 4096, 4096, F, F, 128, 2048, F, 8, NULL, F,
+                                                None) == NOT_SUPPORTED
+    assert lib.gq_nf4_grouped_gemv_down_combine(F, 8, 2048, 2048, F, F, 128, 1024, F, 8, NULL, F,
+                                                None) == NOT_SUPPORTED
+    assert lib.gq_nf4_grouped_gemv_down_combine(F, 1, 768, 768, F, F, 128, 2048, F, 8, F2, F,
+                                                None) == INVALID          # misaligned weights
+    # combine: H % 8, stride, rows == 0
+    assert lib.gq_moe_combine(F, 4, 8, 2044, 2048, NULL, F, None) == INVALID
+    assert lib.gq_moe_combine(F, 4, 8, 2048, 2040, NULL, F, None) == INVALID
+    assert lib.gq_moe_combine(F2, 4, 8, 2048, 2048, NULL, F, None) == INVALID
+    assert lib.gq_moe_combine(NULL, 0, 8, 2048, 2048, NULL, NULL, None) == 0
