@@ -26,7 +26,9 @@ The same line carries
     weights) -- route sort + gate_up GEMM + down GEMM -- in TFLOP/s against
     the dense bf16 MFMA peak;
   * ``extra``: MXFP4 gpt-oss-20b decode (M = 1), prefill (M = 2048) and dgrad
-    (M = 2048, top-4), NF4 dgrad (M = 2048, top-8) and the NF4 M = 4 decode.
+    (M = 2048, top-4), NF4 dgrad (M = 2048, top-8), the NF4 M = 4 decode, and
+    the whole NF4 MoE layer (SwiGLU and router-weighted combine fused) at
+    decode (M = 1) and prefill (M = 4096).
 All inputs are synthetic and resident in HBM before timing starts.
 """
 
@@ -263,6 +265,97 @@ def decode_mx(dev, steps, warmup):
             "gate_up_frac_hbm": bg / (us * 1e-6) / 1e9 / HBM_PEAK_GBS}
 
 
+def decode_layer_nf4(dev, steps, warmup, M=1):
+    """Qwen3 NF4 MoE layer, decode: SwiGLU-fused gate_up GEMV + down GEMV with
+    the router-weighted combine fused (two launches per step, graph-replayed,
+    cold bank copy per step).  Bytes: active experts' packed weights, x, y."""
+    E, topk = wl.QWEN["E"], wl.QWEN["topk"]
+    (Ng, Kg), (Nd, Kd) = wl.QWEN["gate_up"], wl.QWEN["down"]
+    banks_g = [wl.random_nf4_bank(E, Ng, Kg, dev, seed=50 + c) for c in range(COPIES)]
+    banks_d = [wl.random_nf4_bank(E, Nd, Kd, dev, seed=500 + c) for c in range(COPIES)]
+    g = wl.rng(wl.CFG_QWEN_DECODE, 70)
+    ids = [wl.route_uniform(g, M, E, topk) for _ in range(steps + warmup)]
+    t_ids = [torch.from_numpy(i).to(dev) for i in ids]
+    tw = torch.from_numpy(wl.router_weights(g, M, topk)).to(dev)
+    x = bf16_dev(wl.draw_bf16(wl.rng(wl.CFG_QWEN_DECODE, 71), (M, Kg)), dev)
+    act = torch.empty((M * topk, Ng // 2), dtype=torch.bfloat16, device=dev)
+    y = torch.empty((M, Nd), dtype=torch.bfloat16, device=dev)
+
+    def step(i):
+        c, a = banks_g[i % COPIES]
+        gq.gq_nf4_grouped_gemv_swiglu(x, c, a, t_ids[i], out=act)
+        c, a = banks_d[i % COPIES]
+        gq.gq_nf4_grouped_gemv_down_combine(act, c, a, t_ids[i], tw, out=y)
+
+    for i in range(steps, steps + warmup):
+        step(i)
+    gr = capture(step, steps)
+    gr.replay()
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    gr.replay()
+    torch.cuda.synchronize()
+    dt = time.perf_counter() - t0
+    total = 0
+    for i in range(steps):
+        d = len(set(ids[i].reshape(-1).tolist()))
+        total += d * (nf4_expert_bytes(Ng, Kg) + nf4_expert_bytes(Nd, Kd)) + M * Kg * 2 + M * Nd * 2
+    return {"workload": f"qwen3-30b-a3b nf4 moe layer decode M={M}: swiglu gate_up gemv + "
+                        f"down gemv with router-weighted combine (2 launches)",
+            "ms_per_step": 1e3 * dt / steps, "gbs": total / dt / 1e9,
+            "bytes_per_step": total / steps}
+
+
+def prefill_layer_nf4(dev, steps, warmup):
+    """Qwen3 NF4 MoE layer, prefill (M=4096 Zipf top-8): route sort + SwiGLU-
+    fused gate_up GEMM + down GEMM (router weight as pair scale) + combine."""
+    cfgd, M, cfg = wl.QWEN, 4096, wl.CFG_QWEN_PREFILL
+    E, topk = cfgd["E"], cfgd["topk"]
+    (Ng, Kg), (Nd, Kd) = cfgd["gate_up"], cfgd["down"]
+    P = M * topk
+    route = wl.route_zipf(wl.rng(cfg, wl.S_ROUTE), M, E, topk)
+    cg, ag = wl.random_nf4_bank(E, Ng, Kg, dev, seed=31)
+    cd, ad = wl.random_nf4_bank(E, Nd, Kd, dev, seed=301)
+    ids = torch.from_numpy(route).to(dev)
+    sc = torch.from_numpy(wl.router_weights(wl.rng(cfg, wl.S_LOGITS), M, topk)).to(dev)
+    x = bf16_dev(wl.draw_bf16(wl.rng(cfg, wl.S_X), (M, Kg)), dev)
+    act = torch.empty((P, Ng // 2), dtype=torch.bfloat16, device=dev)
+    yp = torch.empty((P, Nd), dtype=torch.bfloat16, device=dev)
+    y = torch.empty((M, Nd), dtype=torch.bfloat16, device=dev)
+    tg, td, tc = Timer(), Timer(), Timer()
+
+    def run(timed):
+        r = gq.gq_route_sort(ids, E)
+        rd = r._replace(rows=P, topk=1)
+        ev = tg.start() if timed else None
+        gq.gq_nf4_grouped_gemm_swiglu(x, cg, ag, r, out=act)
+        if timed:
+            tg.stop(ev)
+            ev = td.start()
+        gq.gq_nf4_grouped_gemm(act, cd, ad, rd, pair_scale=sc, out=yp)
+        if timed:
+            td.stop(ev)
+            ev = tc.start()
+        gq.gq_moe_combine(yp, topk, out=y)
+        if timed:
+            tc.stop(ev)
+
+    for _ in range(warmup):
+        run(False)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for _ in range(steps):
+        run(True)
+    torch.cuda.synchronize()
+    dt = time.perf_counter() - t0
+    flops = 2.0 * P * (Ng * Kg + Nd * Kd)
+    return {"workload": "qwen3-30b-a3b nf4 moe layer prefill M=4096 top-8 Zipf(1.1): route sort "
+                        "+ swiglu gate_up gemm + down gemm (router-weight scale) + combine",
+            "ms_per_step": 1e3 * dt / steps, "tflops": flops * steps / dt / 1e12,
+            "gate_up_swiglu_us": tg.avg_us(), "down_us": td.avg_us(), "combine_us": tc.avg_us(),
+            "combine_gbs": (P * Nd * 2 + M * Nd * 2) / (tc.avg_us() * 1e-6) / 1e9}
+
+
 def prefill(dev, steps, warmup, fmt):
     """NF4 Qwen3 (M=4096 Zipf top-8) or MXFP4 gpt-oss (M=2048 uniform top-4):
     route sort + gate_up GEMM + down GEMM per step (eager; kernels are long)."""
@@ -490,6 +583,11 @@ def main():
         mp["gate_up_frac_bf16_peak"] = mp["gate_up_tflops"] / BF16_PEAK_TFLOPS
         mp["gate_up_frac_fp4_peak"] = mp["gate_up_tflops"] / FP4_PEAK_TFLOPS
         extra["mxfp4_prefill_m2048"] = mp
+        log("[bench] nf4 moe layer decode M=1")
+        extra["nf4_moe_layer_decode_m1"] = decode_layer_nf4(dev, args.steps, args.warmup)
+        log("[bench] nf4 moe layer prefill M=4096")
+        extra["nf4_moe_layer_prefill_m4096"] = prefill_layer_nf4(dev, args.prefill_steps,
+                                                                 args.prefill_warmup)
         log("[bench] nf4 dgrad")
         extra["nf4_dgrad_m2048"] = dgrad(dev, args.prefill_steps, args.prefill_warmup)
         log("[bench] mxfp4 dgrad")
