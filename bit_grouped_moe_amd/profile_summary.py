@@ -31,25 +31,20 @@ HERE = os.path.dirname(os.path.abspath(__file__))
 CSRC = os.path.join(HERE, "csrc")
 
 # Launch shapes (grid size in threads) of the bench's Qwen3 NF4 workloads.
-GATE_UP_GEMV = ("grouped_gemv_kernel<false", 196608)      # N=1536, K=2048, M=1, top-8
+GATE_UP_GEMV = ("grouped_gemv_kernel<false, 2, true, false>", 393216)  # N=1536, K=2048, M=1, top-8
 GATE_UP_GEMM = ("grouped_gemm_fwd_kernel<0>", 811008)      # M=4096 top-8, 257 x 12 tiles
 SOURCES = {"gemv_nf4_gate_up_m1": ["gemv.hip", "gq_device.hpp"],
            "gemm_nf4_gate_up_prefill": ["gemm.hip", "gq_device.hpp"]}
 
 
-_KERNELS = ("grouped_gemv_kernel<false", "grouped_gemv_kernel<true", "grouped_gemm_fwd_kernel<0>",
-            "grouped_gemm_fwd_kernel<1>", "grouped_dgrad_kernel", "route_sort_kernel",
-            "nf4_decode_kernel", "mxfp4_decode_kernel")
 _PROBES = ("stream_read_kernel(", "copy_kernel(", "empty_kernel(")
 
 
 def _short(name):
-    """Short name of a libgq or probe kernel; None for any other kernel."""
+    """Kernel name with template arguments for libgq and probe kernels; None
+    for any other kernel (torch's own)."""
     if name.startswith("gq::") or name.startswith("void gq::"):
-        full = name.split("gq::", 1)[1].split("(", 1)[0]
-        for key in _KERNELS:
-            if full.startswith(key):
-                return full
+        return name.split("gq::", 1)[1].split("(", 1)[0]
     if name.startswith("(anonymous namespace)::"):
         for key in _PROBES:
             if name.startswith("(anonymous namespace)::" + key):
