@@ -251,6 +251,7 @@ __device__ __forceinline__ void grouped_gemm_body(const GemmArgs& g) {
   __shared__ __attribute__((aligned(16))) uint16_t Bs[2][kTN * kBStride];
   __shared__ __attribute__((aligned(16))) uint8_t Cs[kDg ? 2 : 1][kDg ? kTK * kCStride : 16];
   __shared__ float As[kDg ? 2 : 1][kDg ? DgFmt<kMode>::kBlk * kTK : 1];
+  __shared__ __attribute__((aligned(16))) uint16_t Aw[4][64 * kTK];   // per-wave A staging
   __shared__ int pair_s[kTM];
   __shared__ int row_s[kTM];
   __shared__ float lut[16];
@@ -304,8 +305,6 @@ __device__ __forceinline__ void grouped_gemm_body(const GemmArgs& g) {
   const int lr = lane & 31, lh = lane >> 5;
   const int ms0 = wave, ms1 = wave + 4;                    // owned 32-row sub-tiles
   const bool act0 = ms0 * 32 < valid, act1 = ms1 * 32 < valid;
-  const uint16_t* a0 = g.x + (int64_t)row_s[ms0 * 32 + lr] * g.x_stride + lh * 32;
-  const uint16_t* a1 = g.x + (int64_t)row_s[ms1 * 32 + lr] * g.x_stride + lh * 32;
   const int nsteps = (g.Kc + kTK - 1) / kTK;
   const bool ktail = (g.Kc % kTK) != 0;                   // MXFP4 only: last step half full
   // valid B columns: the SwiGLU tile decodes all 128 (missing ones as zeros)
@@ -319,14 +318,47 @@ __device__ __forceinline__ void grouped_gemm_body(const GemmArgs& g) {
 #pragma unroll
       for (int r = 0; r < 16; ++r) acc[j][c][r] = 0.f;
 
-  // Activation loads are unconditional (rows of inactive sub-tiles point at a
-  // valid row; the half-step past a K tail re-reads the last valid half and
-  // is zeroed just before use), see the note at fwd_load.
-  const int a_koff_max = g.Kc - 32 - lh * 32;             // keeps k within the row
-  auto load_a_slice = [&](int ks, int sl, u32x4 (&A)[2][4]) {
-    const int koff = min(ks * kTK, a_koff_max);
-    A[0][sl] = *reinterpret_cast<const u32x4*>(a0 + koff + sl * 8);
-    A[1][sl] = *reinterpret_cast<const u32x4*>(a1 + koff + sl * 8);
+  // ---- A operand: the gathered activation rows, staged per wave through LDS.
+  // Global loads are coalesced: load i (0..7) of a lane reads 16 bytes, chunk
+  // lane%8 of the K step, of the wave's local row
+  //   r(i) = (i/4)*32 + (i%4)*8 + lane/8   (rows 0..31: sub-tile ms0, 32..63: ms1)
+  // so 8 lanes cover one row's 128 bytes (MFMA-fragment-shaped loads touch 32
+  // rows per instruction and were the kernel's largest cost).  The wave writes
+  // them into its own LDS area with the chunk slot XOR-swizzled by
+  // (row >> 1) & 7 and reads MFMA fragments (row lr, chunk lh*4 + sl) back;
+  // both directions are free of bank conflicts, and no other wave touches the
+  // area, so no barrier.  Loads are unconditional (rows of inactive sub-tiles
+  // are valid rows; chunks past a K tail re-read the last valid chunk and are
+  // zeroed when read), see the note at fwd_load.
+  uint16_t* aw = &Aw[wave][0];
+  // The lane's 8 row offsets are re-read from LDS at every step (registers
+  // are short); element offsets fit 32 bits (host check).
+  auto load_a = [&](int ks, u32x4 (&Ar)[8]) {
+    const int k = min(ks * kTK + (lane & 7) * 8, g.Kc - 8);
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      const int off = row_s[(i < 4 ? ms0 : ms1) * 32 + (i & 3) * 8 + (lane >> 3)] * (int)g.x_stride;
+      Ar[i] = *reinterpret_cast<const u32x4*>(g.x + off + k);
+    }
+  };
+  auto stage_a = [&](const u32x4 (&Ar)[8]) {
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      const int r = (i >> 2) * 32 + (i & 3) * 8 + (lane >> 3);
+      const int slot = (lane & 7) ^ ((r >> 1) & 7);
+      *reinterpret_cast<u32x4*>(aw + r * kTK + slot * 8) = Ar[i];
+    }
+  };
+  auto read_a = [&](int sl, u32x4 (&a)[2], bool zero_hi) {
+#pragma unroll
+    for (int j = 0; j < 2; ++j) {
+      const int r = j * 32 + lr;
+      const int slot = (lh * 4 + sl) ^ ((r >> 1) & 7);
+      a[j] = *reinterpret_cast<const u32x4*>(aw + r * kTK + slot * 8);
+      if constexpr (kMode == kFwdMX) {                     // K tail: zero the missing half
+        if (zero_hi) a[j] = u32x4{0u, 0u, 0u, 0u};
+      }
+    }
   };
   auto load_b_slice = [&](const uint16_t* B, int sl, bf16x8 (&b)[4]) {
 #pragma unroll
@@ -336,36 +368,38 @@ __device__ __forceinline__ void grouped_gemm_body(const GemmArgs& g) {
   };
   // kRows = number of active 32-row sub-tiles of this wave (1 or 2) with all
   // 128 columns valid: unguarded MFMAs.  kRows == 0: generic guarded path.
-  auto mfma_slice = [&](auto rows_c, const u32x4 (&A)[2][4], int sl, const bf16x8 (&b)[4]) {
+  auto mfma_slice = [&](auto rows_c, const u32x4 (&a)[2], const bf16x8 (&b)[4]) {
     constexpr int kRows = decltype(rows_c)::value;
 #pragma unroll
     for (int c = 0; c < 4; ++c) {
       if constexpr (kRows == 0) {
         if (c * 32 >= ncols) continue;
         if (act0)
-          acc[0][c] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(A[0][sl]), b[c],
-                                                              acc[0][c], 0, 0, 0);
+          acc[0][c] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(a[0]), b[c], acc[0][c],
+                                                              0, 0, 0);
         if (act1)
-          acc[1][c] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(A[1][sl]), b[c],
-                                                              acc[1][c], 0, 0, 0);
+          acc[1][c] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(a[1]), b[c], acc[1][c],
+                                                              0, 0, 0);
       } else {
-        acc[0][c] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(A[0][sl]), b[c],
-                                                            acc[0][c], 0, 0, 0);
+        acc[0][c] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(a[0]), b[c], acc[0][c],
+                                                            0, 0, 0);
         if constexpr (kRows == 2)
-          acc[1][c] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(A[1][sl]), b[c],
-                                                              acc[1][c], 0, 0, 0);
+          acc[1][c] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(a[1]), b[c], acc[1][c],
+                                                              0, 0, 0);
       }
     }
   };
 
-  u32x4 A[2][4];
+  u32x4 Ar[8];
   FwdLoad F0{}, F1{};
   DgLoad D{};
   DgCodes R{};
 
-  // ---- prologue: step 0 decoded into Bs[0]; step 1's codes in flight ----
-#pragma unroll
-  for (int sl = 0; sl < 4; ++sl) load_a_slice(0, sl, A);
+  // ---- prologue: step 0 decoded into Bs[0] and staged in Aw; step 1's
+  // activations and codes in flight ----
+  load_a(0, Ar);
+  stage_a(Ar);
+  load_a(min(1, nsteps - 1), Ar);
   if constexpr (kDg) {
     D = dg_load<kMode>(g, e, n0, 0, tid);
     dg_stage<kMode>(D, Cs[0], As[0], tid);
@@ -384,28 +418,26 @@ __device__ __forceinline__ void grouped_gemm_body(const GemmArgs& g) {
   }
   lds_barrier();
 
-  // ---- main loop: step ks runs its MFMAs slice by slice; between them it
-  // decodes a quarter of step ks+1 into the other LDS buffer and refills the
-  // consumed activation registers with step ks+1.  All prefetches and decodes
-  // are unconditional (indices clamped to the last step): loads under a branch
-  // make the compiler wait for them early.  Unrolled by two so the two code
-  // register sets swap roles without copies. ----
+  // ---- main loop: step ks runs its MFMAs slice by slice, its operands read
+  // from LDS one slice ahead; between slices it decodes a quarter of step
+  // ks+1 into the other B buffer.  After the last slice it stages step ks+1's
+  // activations (loaded during step ks-1) and loads step ks+2's.  All
+  // prefetches and decodes are unconditional (indices clamped to the last
+  // step): loads under a branch make the compiler wait for them early.
+  // Unrolled by two so the two code register sets swap roles without copies. ----
   auto run_loop = [&](auto rows_c) {
     auto step = [&](int ks, FwdLoad& F_dec, FwdLoad& F_fill) {
-      const int k1 = min(ks + 1, nsteps - 1);
       const uint16_t* B = Bs[ks & 1];
       uint16_t* Bn = Bs[(ks + 1) & 1];
+      const bool zero_hi = ktail && ks == nsteps - 1 && lh == 1;
       if constexpr (!kDg) F_fill = fwd_load<kMode>(g, e, n0, min(ks + 2, nsteps - 1), tid);
-      if constexpr (kMode == kFwdMX) {                     // K tail: zero the missing half
-        if (ktail && ks == nsteps - 1 && lh == 1) {
-#pragma unroll
-          for (int sl = 0; sl < 4; ++sl) A[0][sl] = A[1][sl] = u32x4{0u, 0u, 0u, 0u};
-        }
-      }
       // B fragments ping-pong between two register sets (no copies): slice
-      // sl's MFMAs read one set while slice sl+1's fragments load into the other.
+      // sl's MFMAs read one set while slice sl+1's load into the other.  The
+      // slice's A fragments are read at its start (registers are short).
       bf16x8 b0[4], b1[4];
       auto slice = [&](int sl, const bf16x8 (&bc)[4], bf16x8 (&bn)[4]) {
+        u32x4 ac[2];
+        read_a(sl, ac, zero_hi);
         if (sl < 3) load_b_slice(B, sl + 1, bn);
         if constexpr (kDg) {
           if (sl == 0) dg_read_codes<kMode>(Cs[(ks + 1) & 1], As[(ks + 1) & 1], tid, R);
@@ -417,14 +449,15 @@ __device__ __forceinline__ void grouped_gemm_body(const GemmArgs& g) {
         } else {
           fwd_decode_chunk<kMode>(F_dec, sl, lut, Bn, tid);
         }
-        mfma_slice(rows_c, A, sl, bc);
-        load_a_slice(k1, sl, A);
+        mfma_slice(rows_c, ac, bc);
       };
       load_b_slice(B, 0, b0);
       slice(0, b0, b1);
       slice(1, b1, b0);
       slice(2, b0, b1);
       slice(3, b1, b0);
+      stage_a(Ar);                                       // step ks+1 (own area: no barrier)
+      load_a(min(ks + 2, nsteps - 1), Ar);
       lds_barrier();
     };
     for (int ks = 0; ks < nsteps; ks += 2) {
@@ -512,13 +545,14 @@ static int launch_gemm(GemmArgs g, int32_t max_tiles, int32_t tile_m, hipStream_
   return launch_status();
 }
 
-static int common_gemm_checks(const uint16_t* x, int64_t x_stride, int32_t Kc,
+static int common_gemm_checks(const uint16_t* x, int64_t x_rows, int64_t x_stride, int32_t Kc,
                               const uint8_t* codes, const void* scl, const int32_t* offsets,
                               const int32_t* sorted_pairs, const int32_t* tiles,
                               const int32_t* num_tiles, const uint16_t* out) {
   if (!x || !codes || !scl || !offsets || !sorted_pairs || !tiles || !num_tiles || !out)
     return kInvalid;
   if (x_stride < Kc || x_stride % 8) return kInvalid;
+  if (x_rows * x_stride >= INT32_MAX) return kNotSupported;   // 32-bit activation offsets
   if (!aligned16(x) || !aligned16(codes) || !aligned16(out)) return kInvalid;
   if (!aligned4(offsets) || !aligned4(sorted_pairs) || !aligned4(tiles) || !aligned4(num_tiles))
     return kInvalid;
@@ -540,7 +574,7 @@ static int forward_entry(const uint16_t* x, int32_t rows, int32_t K, int64_t x_s
   const int64_t P = (int64_t)rows * topk;
   if (P >= INT32_MAX) return kNotSupported;
   if (P == 0) return kOk;                                  // nothing to enqueue
-  int st = common_gemm_checks(x, x_stride, K, codes, scl, offsets, sorted_pairs, tiles,
+  int st = common_gemm_checks(x, rows, x_stride, K, codes, scl, offsets, sorted_pairs, tiles,
                               num_tiles, out);
   if (st != kOk) return st;
   if (!kMx && !aligned4(scl)) return kInvalid;
@@ -606,7 +640,7 @@ static int dgrad_entry(const uint16_t* dy, int32_t P, int32_t N, int64_t dy_stri
   if (dy_stride < N || dy_stride % 8) return kInvalid;
   if (tile_m != kTM) return kNotSupported;
   if (P == 0) return kOk;                                  // nothing to enqueue
-  int st = common_gemm_checks(dy, dy_stride, N, codes, scl, offsets, sorted_pairs, tiles,
+  int st = common_gemm_checks(dy, P, dy_stride, N, codes, scl, offsets, sorted_pairs, tiles,
                               num_tiles, dx);
   if (st != kOk) return st;
   if (!kMx && !aligned4(scl)) return kInvalid;
