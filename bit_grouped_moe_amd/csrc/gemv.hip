@@ -329,56 +329,61 @@ static int launch_gemv(const uint16_t* x, int32_t rows, int32_t K, int64_t x_str
 //
 // A workgroup owns output rows [n0, n0 + Rb) for EVERY pair, so a token's
 // k products meet in its LDS and are reduced there: no atomics, no second
-// launch.  Lane groups (W lanes, as in the GEMV) take (pair, row) combos;
-// each combo is one 16-byte weight segment per lane plus the pair's 64-byte
-// activation slice.  A pair whose expert is outside [0, E) contributes 0.
+// launch.  Wave w takes pairs w, w + NWv, ... (kPPW of them; the expert id is
+// one scalar load per pair, as in the GEMV); its lane groups (W lanes) take
+// kR consecutive rows each, one 16-byte weight segment per lane and row, all
+// against the pair's 64-byte activation slice.  A pair whose expert is
+// outside [0, E) contributes 0.
 constexpr int kCombineMaxPairs = 64;
-constexpr int kCombineMaxCombos = 512;
+constexpr int kCombineMaxWaves = 16;
+constexpr int kCombineMaxYs = 1024;
 
-template <bool kMx, int kIt>
-__global__ __launch_bounds__(kGemvMaxThreads) void gemv_down_combine_kernel(
+template <bool kMx, int kR, int kPPW>
+__global__ __launch_bounds__(kWave * kCombineMaxWaves) void gemv_down_combine_kernel(
     const uint16_t* __restrict__ act, int64_t a_stride, int I, const uint8_t* __restrict__ codes,
     const void* __restrict__ scl, int H, int E, const int32_t* __restrict__ ids, int topk, int P,
-    const float* __restrict__ tw, uint16_t* __restrict__ y, int S, int W, int G, int Rb) {
+    const float* __restrict__ tw, uint16_t* __restrict__ y, int S, int W, int NWv) {
   __shared__ float lut[16];
-  __shared__ float ys[kCombineMaxCombos];
+  __shared__ float ys[kCombineMaxYs];                      // [P][Rb]
 
-  const int tid = threadIdx.x;
+  const int tid = threadIdx.x, lane = tid & (kWave - 1), wave = tid / kWave;
+  const int slots = kWave / W;                             // lane groups per wave
+  const int Rb = slots * kR;                               // rows per workgroup
   const int n0 = blockIdx.x * Rb;
-  const int g = tid / W, s = tid - g * W;
+  const int g = lane / W, s = lane - g * W;
   const bool active = s < S;
   const int s_cl = active ? s : 0;
-  const int C = P * Rb;                                    // combos (pair-major)
+  const size_t row_bytes = (size_t)I / 2;
 
-  // ---- round trip 1: the combos' experts and activation slices ----
-  int pp[kIt], rr[kIt], ee[kIt];
-  u32x4 xr[kIt][4];
+  // ---- round trip 1: the wave's experts (scalar) and activation slices ----
+  int pp[kPPW], ee[kPPW];
+  u32x4 xr[kPPW][4];
 #pragma unroll
-  for (int it = 0; it < kIt; ++it) {
-    const int c = min(g + G * it, C - 1);                  // clamped: surplus combos repeat
-    pp[it] = c / Rb;
-    rr[it] = c - pp[it] * Rb;
-    ee[it] = ids[pp[it]];
-    const u32x4* ap = reinterpret_cast<const u32x4*>(act + (int64_t)pp[it] * a_stride + s_cl * 32);
+  for (int q = 0; q < kPPW; ++q) {
+    pp[q] = min(wave + NWv * q, P - 1);                    // surplus pairs repeat the last
+    ee[q] = ids[pp[q]];
+    const u32x4* ap = reinterpret_cast<const u32x4*>(act + (int64_t)pp[q] * a_stride + s_cl * 32);
 #pragma unroll
-    for (int v = 0; v < 4; ++v) xr[it][v] = ap[v];
+    for (int v = 0; v < 4; ++v) xr[q][v] = ap[v];
   }
   // ---- round trip 2: weight segments (dropped pairs read expert 0) ----
-  const size_t row_bytes = (size_t)I / 2;
-  u32x4 cw[kIt];
-  float am[kIt];
-  uint32_t sb[kIt];
+  u32x4 cw[kPPW][kR];
+  float am[kPPW][kR];
+  uint32_t sb[kPPW][kR];
 #pragma unroll
-  for (int it = 0; it < kIt; ++it) {
-    const int e = (unsigned)ee[it] < (unsigned)E ? ee[it] : 0;
-    const size_t row = (size_t)e * H + min(n0 + rr[it], H - 1);
-    cw[it] = *reinterpret_cast<const u32x4*>(codes + row * row_bytes + (size_t)s_cl * 16);
-    if constexpr (kMx) {
-      sb[it] = (uint32_t)static_cast<const uint8_t*>(scl)[row * (size_t)(I / 32) + s_cl];
-      am[it] = 0.f;
-    } else {
-      am[it] = static_cast<const float*>(scl)[row * (size_t)(I / 64) + s_cl / 2];
-      sb[it] = 0u;
+  for (int q = 0; q < kPPW; ++q) {
+    const int e = (unsigned)ee[q] < (unsigned)E ? ee[q] : 0;
+#pragma unroll
+    for (int i = 0; i < kR; ++i) {
+      const size_t row = (size_t)e * H + min(n0 + g * kR + i, H - 1);
+      cw[q][i] = *reinterpret_cast<const u32x4*>(codes + row * row_bytes + (size_t)s_cl * 16);
+      if constexpr (kMx) {
+        sb[q][i] = (uint32_t)static_cast<const uint8_t*>(scl)[row * (size_t)(I / 32) + s_cl];
+        am[q][i] = 0.f;
+      } else {
+        am[q][i] = static_cast<const float*>(scl)[row * (size_t)(I / 64) + s_cl / 2];
+        sb[q][i] = 0u;
+      }
     }
   }
   if constexpr (!kMx) {
@@ -386,24 +391,27 @@ __global__ __launch_bounds__(kGemvMaxThreads) void gemv_down_combine_kernel(
     lds_barrier();
   }
 #pragma unroll
-  for (int it = 0; it < kIt; ++it) {
+  for (int q = 0; q < kPPW; ++q) {
     float xf[32];
 #pragma unroll
     for (int v = 0; v < 4; ++v)
 #pragma unroll
       for (int cc = 0; cc < 4; ++cc) {
-        xf[8 * v + 2 * cc] = bf16lo_to_f32(xr[it][v][cc]);
-        xf[8 * v + 2 * cc + 1] = bf16hi_to_f32(xr[it][v][cc]);
+        xf[8 * v + 2 * cc] = bf16lo_to_f32(xr[q][v][cc]);
+        xf[8 * v + 2 * cc + 1] = bf16hi_to_f32(xr[q][v][cc]);
       }
-    const float part = active ? segment_dot<kMx>(lut, cw[it], am[it], sb[it], xf) : 0.f;
-    const float tot = group_sum_last(part, W);
-    const int c = g + G * it;
-    if (s == W - 1 && c < C) ys[c] = (unsigned)ee[it] < (unsigned)E ? tot : 0.f;
+    const int p = wave + NWv * q;
+#pragma unroll
+    for (int i = 0; i < kR; ++i) {
+      const float part = active ? segment_dot<kMx>(lut, cw[q][i], am[q][i], sb[q][i], xf) : 0.f;
+      const float tot = group_sum_last(part, W);
+      if (s == W - 1 && p < P) ys[p * Rb + g * kR + i] = (unsigned)ee[q] < (unsigned)E ? tot : 0.f;
+    }
   }
   lds_barrier();
   // ---- combine: thread (t, r) sums its token's slots in order ----
   const int rows = P / topk;
-  for (int idx = tid; idx < rows * Rb; idx += kGemvMaxThreads) {
+  for (int idx = tid; idx < rows * Rb; idx += kWave * NWv) {
     const int t = idx / Rb, r = idx - t * Rb;
     const int n = n0 + r;
     if (n >= H) continue;
@@ -415,6 +423,15 @@ __global__ __launch_bounds__(kGemvMaxThreads) void gemv_down_combine_kernel(
     }
     y[(int64_t)t * H + n] = f32_to_bf16_bits(acc);
   }
+}
+
+template <bool kMx, int kR, int kPPW>
+static void launch_dc(dim3 grid, int NWv, hipStream_t stream, const uint16_t* act,
+                      int64_t a_stride, int I, const uint8_t* codes, const void* scl, int H,
+                      int E, const int32_t* ids, int topk, int P, const float* tw, uint16_t* y,
+                      int S, int W) {
+  hipLaunchKernelGGL((gemv_down_combine_kernel<kMx, kR, kPPW>), grid, dim3(kWave * NWv), 0,
+                     stream, act, a_stride, I, codes, scl, H, E, ids, topk, P, tw, y, S, W, NWv);
 }
 
 template <bool kMx>
@@ -432,29 +449,22 @@ static int launch_down_combine(const uint16_t* act, int32_t rows, int32_t I, int
   if (P > kCombineMaxPairs || I > 32 * kWave || H >= (1 << 24)) return kNotSupported;
   int S, W, G, NT;
   segment_layout(I, S, W, G, NT);
-  // rows per workgroup: about two combos per lane group
-  const int Rb = (int)std::max<int64_t>(1, (2 * G) / P);
-  const int64_t C = P * Rb;
-  const int64_t need = (C + G - 1) / G;
+  const int NWv = (int)std::min<int64_t>(P, kCombineMaxWaves);
+  const int ppw = (int)((P + NWv - 1) / NWv);               // 1..4
+  // rows per lane group: 2 for one pair per wave (as the GEMV), 1 otherwise
+  const int kr = ppw == 1 ? 2 : 1;
+  const int Rb = (kWave / W) * kr;
+  if (P * Rb > kCombineMaxYs) return kNotSupported;
   const dim3 grid((H + Rb - 1) / Rb);
-  if (need <= 1)
-    hipLaunchKernelGGL((gemv_down_combine_kernel<kMx, 1>), grid, dim3(kGemvMaxThreads), 0,
-                       stream, act, a_stride, I, codes, scl, H, E, ids, topk, (int)P, tw, y, S, W,
-                       G, Rb);
-  else if (need <= 2)
-    hipLaunchKernelGGL((gemv_down_combine_kernel<kMx, 2>), grid, dim3(kGemvMaxThreads), 0,
-                       stream, act, a_stride, I, codes, scl, H, E, ids, topk, (int)P, tw, y, S, W,
-                       G, Rb);
-  else if (need <= 4)
-    hipLaunchKernelGGL((gemv_down_combine_kernel<kMx, 4>), grid, dim3(kGemvMaxThreads), 0,
-                       stream, act, a_stride, I, codes, scl, H, E, ids, topk, (int)P, tw, y, S, W,
-                       G, Rb);
-  else if (need <= 8)
-    hipLaunchKernelGGL((gemv_down_combine_kernel<kMx, 8>), grid, dim3(kGemvMaxThreads), 0,
-                       stream, act, a_stride, I, codes, scl, H, E, ids, topk, (int)P, tw, y, S, W,
-                       G, Rb);
+  if (ppw == 1)
+    launch_dc<kMx, 2, 1>(grid, NWv, stream, act, a_stride, I, codes, scl, H, E, ids, topk,
+                         (int)P, tw, y, S, W);
+  else if (ppw == 2)
+    launch_dc<kMx, 1, 2>(grid, NWv, stream, act, a_stride, I, codes, scl, H, E, ids, topk,
+                         (int)P, tw, y, S, W);
   else
-    return kNotSupported;
+    launch_dc<kMx, 1, 4>(grid, NWv, stream, act, a_stride, I, codes, scl, H, E, ids, topk,
+                         (int)P, tw, y, S, W);
   return launch_status();
 }
 

@@ -253,9 +253,7 @@ int gq_mxfp4_grouped_dgrad(const uint16_t* dy, int32_t P, int32_t N, int64_t dy_
  *   outside [0, E) contributes 0.
  *   InvalidValue: null pointer (topk_weights may be NULL), rows < 1,
  *     topk < 1, E < 1, H < 1, I not a positive multiple of 64, bad stride
- *     or alignment.  NotSupported: rows*topk > 64, I > 2048, H >= 2^24,
- *     or more than 8 (pair, row) products per lane group (I = 2048 with
- *     rows*topk > 32).
+ *     or alignment.  NotSupported: rows*topk > 64, I > 2048, H >= 2^24.
  *
  * gq_moe_combine (prefill):
  *   y[t, :] = bf16( sum_s w[t, s] * y_pairs[t*topk + s, :] )

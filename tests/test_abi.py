@@ -205,8 +205,6 @@ def test_epilogue_entry_points_reject(lib):
                                                 None) == NOT_SUPPORTED
     assert lib.gq_nf4_grouped_gemv_down_combine(F, 1, 4096, 4096, F, F, 128, 2048, F, 8, NULL, F,
                                                 None) == NOT_SUPPORTED
-    assert lib.gq_nf4_grouped_gemv_down_combine(F, 8, 2048, 2048, F, F, 128, 1024, F, 8, NULL, F,
-                                                None) == NOT_SUPPORTED
     assert lib.gq_nf4_grouped_gemv_down_combine(F, 1, 768, 768, F, F, 128, 2048, F, 8, F2, F,
                                                 None) == INVALID          # misaligned weights
     # combine: H % 8, stride, rows == 0
