@@ -42,7 +42,7 @@ constexpr int kTN = 128;          // tile columns (output features)
 constexpr int kTK = 64;           // contraction per step
 constexpr int kGemmThreads = 256;
 constexpr int kBStride = 72;      // bf16 per LDS row of B (64 + 8 pad: conflict-free 16-B reads)
-constexpr int kCStride = 80;      // bytes per LDS row of raw codes (dgrad staging)
+constexpr int kCStride = 64;      // bytes per LDS row of raw codes (dgrad staging)
 
 // kFwdNF4Glu: NF4 forward on a fused gate_up weight (gate rows [0, I), up
 // rows [I, 2I)) whose epilogue writes SwiGLU(gate, up) = silu(gate) * up.
@@ -251,9 +251,12 @@ __device__ __forceinline__ void grouped_gemm_body(const GemmArgs& g) {
   __shared__ __attribute__((aligned(16))) uint16_t Bs[2][kTN * kBStride];
   __shared__ __attribute__((aligned(16))) uint8_t Cs[kDg ? 2 : 1][kDg ? kTK * kCStride : 16];
   __shared__ float As[kDg ? 2 : 1][kDg ? DgFmt<kMode>::kBlk * kTK : 1];
-  __shared__ __attribute__((aligned(16))) uint16_t Aw[4][64 * kTK];   // per-wave A staging
+  __shared__ __attribute__((aligned(16))) uint16_t Aw[kDg ? 1 : 4][kDg ? 8 : 64 * kTK];  // A staging
   __shared__ int pair_s[kTM];
-  __shared__ int row_s[kTM];
+  // dgrad rows are the pairs themselves: row_s aliases pair_s (saves 1 KB of
+  // LDS, which lets two dgrad workgroups share a CU)
+  __shared__ int row_s_buf[kDg ? 1 : kTM];
+  int* const row_s = kDg ? pair_s : row_s_buf;
   __shared__ float lut[16];
 
   const int tid = threadIdx.x;
@@ -295,7 +298,7 @@ __device__ __forceinline__ void grouped_gemm_body(const GemmArgs& g) {
     int p = g.sorted_pairs[start + min(r, valid - 1)];
     p = ((unsigned)p < (unsigned)g.P) ? p : 0;
     pair_s[r] = p;
-    row_s[r] = kDg ? p : p / g.topk;
+    if constexpr (!kDg) row_s[r] = p / g.topk;
   }
   if constexpr (kMode == kDgradMX) e2m1_lut_init(lut, tid);
   else if constexpr (kMode != kFwdMX) nf4_lut_init(lut, tid);
@@ -330,7 +333,7 @@ __device__ __forceinline__ void grouped_gemm_body(const GemmArgs& g) {
   // area, so no barrier.  Loads are unconditional (rows of inactive sub-tiles
   // are valid rows; chunks past a K tail re-read the last valid chunk and are
   // zeroed when read), see the note at fwd_load.
-  uint16_t* aw = &Aw[wave][0];
+  uint16_t* aw = &Aw[kDg ? 0 : wave][0];
   // The lane's 8 row offsets are re-read from LDS at every step (registers
   // are short); element offsets fit 32 bits (host check).
   auto load_a = [&](int ks, u32x4 (&Ar)[8]) {
@@ -359,6 +362,17 @@ __device__ __forceinline__ void grouped_gemm_body(const GemmArgs& g) {
         if (zero_hi) a[j] = u32x4{0u, 0u, 0u, 0u};
       }
     }
+  };
+  // dgrad (one wave per SIMD, LDS already busy with the code staging) keeps
+  // the activation operand out of LDS: each lane loads its MFMA fragments
+  // (row lr, 16 bytes at k = lh*32 + sl*8) straight into registers, one step
+  // ahead.  Rows are the pairs; the contraction (N) is a multiple of 64.
+  const uint16_t* ad0 = g.x + (int64_t)row_s[ms0 * 32 + lr] * g.x_stride + lh * 32;
+  const uint16_t* ad1 = g.x + (int64_t)row_s[ms1 * 32 + lr] * g.x_stride + lh * 32;
+  auto load_a_direct = [&](int ks, int sl, u32x4 (&Ad)[2][4]) {
+    const int koff = ks * kTK;
+    Ad[0][sl] = *reinterpret_cast<const u32x4*>(ad0 + koff + sl * 8);
+    Ad[1][sl] = *reinterpret_cast<const u32x4*>(ad1 + koff + sl * 8);
   };
   auto load_b_slice = [&](const uint16_t* B, int sl, bf16x8 (&b)[4]) {
 #pragma unroll
@@ -390,16 +404,22 @@ __device__ __forceinline__ void grouped_gemm_body(const GemmArgs& g) {
     }
   };
 
-  u32x4 Ar[8];
+  u32x4 Ar[kDg ? 1 : 8];                                   // forward: staged A prefetch
+  u32x4 Ad[2][kDg ? 4 : 1];                                // dgrad: direct A fragments
   FwdLoad F0{}, F1{};
   DgLoad D{};
   DgCodes R{};
 
   // ---- prologue: step 0 decoded into Bs[0] and staged in Aw; step 1's
   // activations and codes in flight ----
-  load_a(0, Ar);
-  stage_a(Ar);
-  load_a(min(1, nsteps - 1), Ar);
+  if constexpr (kDg) {
+#pragma unroll
+    for (int sl = 0; sl < 4; ++sl) load_a_direct(0, sl, Ad);
+  } else {
+    load_a(0, Ar);
+    stage_a(Ar);
+    load_a(min(1, nsteps - 1), Ar);
+  }
   if constexpr (kDg) {
     D = dg_load<kMode>(g, e, n0, 0, tid);
     dg_stage<kMode>(D, Cs[0], As[0], tid);
@@ -437,7 +457,12 @@ __device__ __forceinline__ void grouped_gemm_body(const GemmArgs& g) {
       bf16x8 b0[4], b1[4];
       auto slice = [&](int sl, const bf16x8 (&bc)[4], bf16x8 (&bn)[4]) {
         u32x4 ac[2];
-        read_a(sl, ac, zero_hi);
+        if constexpr (kDg) {
+          ac[0] = Ad[0][sl];
+          ac[1] = Ad[1][sl];
+        } else {
+          read_a(sl, ac, zero_hi);
+        }
         if (sl < 3) load_b_slice(B, sl + 1, bn);
         if constexpr (kDg) {
           if (sl == 0) dg_read_codes<kMode>(Cs[(ks + 1) & 1], As[(ks + 1) & 1], tid, R);
@@ -450,14 +475,17 @@ __device__ __forceinline__ void grouped_gemm_body(const GemmArgs& g) {
           fwd_decode_chunk<kMode>(F_dec, sl, lut, Bn, tid);
         }
         mfma_slice(rows_c, ac, bc);
+        if constexpr (kDg) load_a_direct(min(ks + 1, nsteps - 1), sl, Ad);
       };
       load_b_slice(B, 0, b0);
       slice(0, b0, b1);
       slice(1, b1, b0);
       slice(2, b0, b1);
       slice(3, b1, b0);
-      stage_a(Ar);                                       // step ks+1 (own area: no barrier)
-      load_a(min(ks + 2, nsteps - 1), Ar);
+      if constexpr (!kDg) {
+        stage_a(Ar);                                     // step ks+1 (own area: no barrier)
+        load_a(min(ks + 2, nsteps - 1), Ar);
+      }
       lds_barrier();
     };
     for (int ks = 0; ks < nsteps; ks += 2) {
