@@ -196,8 +196,7 @@ __device__ __forceinline__ void dg_stage(const DgLoad& L, uint8_t* Cs, float* As
 // thread's column quad (8 consecutive contraction values, 16 bytes).  The
 // thread's raw codes and absmax are read from LDS once, by chunk 0.
 struct DgCodes {
-  uint32_t two[8];   // bytes j4*2, j4*2+1 of rows r8*8 .. +8
-  float a[8];
+  uint32_t two[4];   // bytes j4*2, j4*2+1 of rows r8*8 + 2i (low half) and + 2i+1 (high half)
 };
 
 template <int kMode>
@@ -209,17 +208,19 @@ __device__ __forceinline__ void dg_read_codes(const uint8_t* Cs, const float* As
 #pragma unroll
   for (int i = 0; i < 8; ++i) {
     const int r = r8 * 8 + i;
-    R.two[i] = *reinterpret_cast<const uint16_t*>(Cs + r * kCStride + j4 * 2);
-    R.a[i] = As[r * F::kBlk + blk];
+    const uint32_t v = *reinterpret_cast<const uint16_t*>(Cs + r * kCStride + j4 * 2);
+    R.two[i >> 1] = (i & 1) ? (R.two[i >> 1] | (v << 16)) : v;
   }
 }
 
 // The LUT holds the NF4 codebook or the e2m1 values; weight = value * factor
 // in float32 (exact for e2m1 times a power of two), then bf16 RNE.
 template <int kMode>
-__device__ __forceinline__ void dg_decode_chunk(const DgCodes& R, int c, const float* lut,
-                                                uint16_t* Bs, int tid) {
+__device__ __forceinline__ void dg_decode_chunk(const DgCodes& R, const float* As, int c,
+                                                const float* lut, uint16_t* Bs, int tid) {
+  using F = DgFmt<kMode>;
   const int j4 = tid & 31, r8 = tid >> 5;
+  const int blk = (j4 * 4) / F::kBlkK;
   float w[8];
   // bytes j4*2, j4*2+1 hold columns 4*j4 .. 4*j4+3; element 2j sits in the
   // high nibble (NF4) or the low nibble (MXFP4) of byte j
@@ -227,8 +228,9 @@ __device__ __forceinline__ void dg_decode_chunk(const DgCodes& R, int c, const f
 #pragma unroll
   for (int i = 0; i < 8; ++i) {
     const bool lo = ((c & 1) != 0) != kLowFirst;
-    const float qv = lo ? nf4_q_lo(lut, R.two[i], c >> 1) : nf4_q_hi(lut, R.two[i], c >> 1);
-    w[i] = qv * R.a[i];
+    const int byte = (c >> 1) + 2 * (i & 1);
+    const float qv = lo ? nf4_q_lo(lut, R.two[i >> 1], byte) : nf4_q_hi(lut, R.two[i >> 1], byte);
+    w[i] = qv * As[(r8 * 8 + i) * F::kBlk + blk];           // factor re-read: registers are short
   }
   const u32x4 v{pack_bf16x2(w[0], w[1]), pack_bf16x2(w[2], w[3]), pack_bf16x2(w[4], w[5]),
                 pack_bf16x2(w[6], w[7])};
@@ -427,7 +429,7 @@ __device__ __forceinline__ void grouped_gemm_body(const GemmArgs& g) {
     lds_barrier();
     dg_read_codes<kMode>(Cs[0], As[0], tid, R);
 #pragma unroll
-    for (int c = 0; c < 4; ++c) dg_decode_chunk<kMode>(R, c, lut, Bs[0], tid);
+    for (int c = 0; c < 4; ++c) dg_decode_chunk<kMode>(R, As[0], c, lut, Bs[0], tid);
     dg_stage<kMode>(D, Cs[1], As[1], tid);
     D = dg_load<kMode>(g, e, n0, min(2, nsteps - 1), tid);
   } else {
@@ -466,7 +468,7 @@ __device__ __forceinline__ void grouped_gemm_body(const GemmArgs& g) {
         if (sl < 3) load_b_slice(B, sl + 1, bn);
         if constexpr (kDg) {
           if (sl == 0) dg_read_codes<kMode>(Cs[(ks + 1) & 1], As[(ks + 1) & 1], tid, R);
-          dg_decode_chunk<kMode>(R, sl, lut, Bn, tid);
+          dg_decode_chunk<kMode>(R, As[(ks + 1) & 1], sl, lut, Bn, tid);
           if (sl == 3) {                                   // codes of step ks+2, then ks+3
             dg_stage<kMode>(D, Cs[ks & 1], As[ks & 1], tid);
             D = dg_load<kMode>(g, e, n0, min(ks + 3, nsteps - 1), tid);
@@ -541,14 +543,14 @@ __device__ __forceinline__ void grouped_gemm_body(const GemmArgs& g) {
   }
 }
 
-// Forward kernels fit 2 waves per SIMD (2 workgroups per CU) without spills;
-// the dgrad kernel needs a few more registers and runs 1 wave per SIMD.
+// Both kernels fit 2 waves per SIMD (2 workgroups per CU): the dgrad keeps
+// its code words two rows per register and re-reads the row factors from LDS.
 template <int kMode>
 __global__ __launch_bounds__(kGemmThreads, 2) void grouped_gemm_fwd_kernel(GemmArgs g) {
   grouped_gemm_body<kMode>(g);
 }
 template <int kMode>
-__global__ __launch_bounds__(kGemmThreads, 1) void grouped_dgrad_kernel(GemmArgs g) {
+__global__ __launch_bounds__(kGemmThreads, 2) void grouped_dgrad_kernel(GemmArgs g) {
   grouped_gemm_body<kMode>(g);
 }
 
