@@ -6,11 +6,15 @@
 //
 // Launch: E + 1 workgroups of 1024 threads.  Workgroup b < E owns expert b,
 // workgroup E owns the dropped pairs.  Each workgroup
-//   1. builds the full expert histogram in LDS (integer LDS atomics: the
-//      counts do not depend on their order),
-//   2. reduces it to its own segment start and tile base,
-//   3. compacts its pairs in ascending pair order with one block-wide
-//      exclusive scan over contiguous per-thread chunks, and
+//   1. stages the ids in LDS with coalesced loads (32768 per pass),
+//   2. builds the full expert histogram in LDS (integer LDS atomics: the
+//      counts do not depend on their order) and reduces it to its own
+//      segment start and tile base,
+//   3. compacts its pairs in ascending pair order: wave w owns a contiguous
+//      range of 2048 ids, lane l takes ids range + 64j + l (conflict-free LDS
+//      reads), and a pair's place is the workgroup's cursor + the earlier
+//      waves' counts + the wave's running count + its rank among the
+//      matching lanes (ballot bit count), and
 //   4. writes its offsets entry and its tiles.
 // No global atomics, no workspace; the result is the unique stable order.
 #include "gq_device.hpp"
@@ -21,6 +25,9 @@ namespace gq {
 
 constexpr int kSortThreads = 1024;
 constexpr int kSortWaves = kSortThreads / kWave;
+constexpr int kChunkIds = 32768;                          // ids staged in LDS per pass
+constexpr int kPerLane = kChunkIds / kSortThreads;        // 32
+constexpr int kPastEnd = INT32_MIN;                       // slots beyond the last pair
 
 // Block-wide sum of v (all threads get the result).
 __device__ __forceinline__ int block_sum(int v, int* red) {
@@ -35,59 +42,42 @@ __device__ __forceinline__ int block_sum(int v, int* red) {
   return s;
 }
 
-// Block-wide exclusive scan of v; *total gets the sum.
-__device__ __forceinline__ int block_exclusive_scan(int v, int* red, int* total) {
-  const int lane = threadIdx.x & (kWave - 1), w = threadIdx.x / kWave;
-  int inc = wave_inclusive_scan(v);
-  __syncthreads();
-  if (lane == kWave - 1) red[w] = inc;
-  __syncthreads();
-  int base = 0, all = 0;
+// Stage ids [c0, c0 + kChunkIds) in LDS (kPastEnd past P); loads issued first.
+__device__ __forceinline__ void stage_ids(const int32_t* __restrict__ ids, int32_t P, int64_t c0,
+                                          int* s_ids) {
+  int v[kPerLane];
 #pragma unroll
-  for (int i = 0; i < kSortWaves; ++i) {
-    int r = red[i];
-    base += (i < w) ? r : 0;
-    all += r;
-  }
-  *total = all;
-  return base + inc - v;
-}
-
-constexpr int kIdsPerThread = 16;
-constexpr int kSuperChunk = kSortThreads * kIdsPerThread;
-constexpr int kPastEnd = INT32_MIN;  // marks slots beyond the last pair
-
-// Load the kIdsPerThread contiguous ids of this thread in super-chunk sc.
-// All loads are issued before any is used.
-__device__ __forceinline__ void load_ids(const int32_t* __restrict__ ids, int32_t P, int sc,
-                                         int v[kIdsPerThread]) {
-  const int64_t base = (int64_t)sc * kSuperChunk + (int64_t)threadIdx.x * kIdsPerThread;
-#pragma unroll
-  for (int j = 0; j < kIdsPerThread; ++j) {
-    int64_t idx = base + j;
+  for (int j = 0; j < kPerLane; ++j) {
+    const int64_t idx = c0 + (int64_t)j * kSortThreads + threadIdx.x;
     v[j] = idx < P ? ids[idx] : kPastEnd;
   }
+#pragma unroll
+  for (int j = 0; j < kPerLane; ++j) s_ids[j * kSortThreads + threadIdx.x] = v[j];
 }
 
 __global__ __launch_bounds__(kSortThreads) void route_sort_kernel(
     const int32_t* __restrict__ ids, int32_t P, int32_t E, int32_t tile_m,
     int32_t* __restrict__ offsets, int32_t* __restrict__ sorted_pairs,
     int32_t* __restrict__ tiles, int32_t max_tiles, int32_t* __restrict__ num_tiles) {
+  __shared__ int s_ids[kChunkIds];                        // 128 KB
   __shared__ int hist[1024];
   __shared__ int red[kSortWaves];
+  __shared__ int wcount[kSortWaves];
   const int b = blockIdx.x;
-  const int tid = threadIdx.x;
+  const int tid = threadIdx.x, lane = tid & (kWave - 1), wave = tid / kWave;
   const unsigned uE = (unsigned)E;
-  const int n_super = (P + kSuperChunk - 1) / kSuperChunk;
+  const int n_chunks = (P + kChunkIds - 1) / kChunkIds;
 
   for (int e = tid; e < E; e += kSortThreads) hist[e] = 0;
-  __syncthreads();
-  for (int sc = 0; sc < n_super; ++sc) {
-    int v[kIdsPerThread];
-    load_ids(ids, P, sc, v);
-#pragma unroll
-    for (int j = 0; j < kIdsPerThread; ++j)
-      if ((unsigned)v[j] < uE) atomicAdd(&hist[v[j]], 1);
+  for (int ch = 0; ch < n_chunks; ++ch) {
+    __syncthreads();                                       // s_ids free, hist zeroed
+    stage_ids(ids, P, (int64_t)ch * kChunkIds, s_ids);
+    __syncthreads();
+#pragma unroll 8
+    for (int j = 0; j < kPerLane; ++j) {
+      const int v = s_ids[j * kSortThreads + tid];
+      if ((unsigned)v < uE) atomicAdd(&hist[v], 1);
+    }
   }
   __syncthreads();
 
@@ -99,27 +89,45 @@ __global__ __launch_bounds__(kSortThreads) void route_sort_kernel(
   const int valid_total = block_sum(c, red);
   const int tile_total = block_sum(t, red);
 
-  // Stable compaction of this workgroup's pairs: thread-contiguous chunks
-  // in ascending pair order, placed by a block-wide exclusive scan.
+  // Stable compaction of this workgroup's pairs (see the file comment).
   int cursor = (b < E) ? seg_start : valid_total;
-  for (int sc = 0; sc < n_super; ++sc) {
-    int v[kIdsPerThread];
-    load_ids(ids, P, sc, v);
-    int mine = 0;
-#pragma unroll
-    for (int j = 0; j < kIdsPerThread; ++j) {
-      bool hit = (b < E) ? (v[j] == b) : (v[j] != kPastEnd && (unsigned)v[j] >= uE);
-      mine += hit ? 1 : 0;
+  for (int ch = 0; ch < n_chunks; ++ch) {
+    if (n_chunks > 1) {                                    // one chunk: still staged
+      __syncthreads();
+      stage_ids(ids, P, (int64_t)ch * kChunkIds, s_ids);
+      __syncthreads();
     }
-    int total = 0;
-    int pos = cursor + block_exclusive_scan(mine, red, &total);
-    const int base = sc * kSuperChunk + tid * kIdsPerThread;
+    const int wbase = wave * (kChunkIds / kSortWaves);     // the wave's 2048 ids
+    int mine = 0;
+#pragma unroll 8
+    for (int j = 0; j < kPerLane; ++j) {
+      const int v = s_ids[wbase + j * kWave + lane];
+      const bool hit = (b < E) ? (v == b) : (v != kPastEnd && (unsigned)v >= uE);
+      mine += __popcll(__ballot(hit));
+    }
+    if (lane == 0) wcount[wave] = mine;
+    __syncthreads();
+    int before = 0, total = 0;
 #pragma unroll
-    for (int j = 0; j < kIdsPerThread; ++j) {
-      bool hit = (b < E) ? (v[j] == b) : (v[j] != kPastEnd && (unsigned)v[j] >= uE);
-      if (hit) sorted_pairs[pos++] = base + j;
+    for (int i = 0; i < kSortWaves; ++i) {
+      const int n = wcount[i];
+      before += i < wave ? n : 0;
+      total += n;
+    }
+    int pos = cursor + before;
+    const int64_t pbase = (int64_t)ch * kChunkIds + wbase;
+#pragma unroll 8
+    for (int j = 0; j < kPerLane; ++j) {
+      const int v = s_ids[wbase + j * kWave + lane];
+      const bool hit = (b < E) ? (v == b) : (v != kPastEnd && (unsigned)v >= uE);
+      const uint64_t bal = __ballot(hit);
+      if (hit)
+        sorted_pairs[pos + __popcll(bal & ((1ull << lane) - 1ull))] =
+            (int)(pbase + j * kWave + lane);
+      pos += __popcll(bal);
     }
     cursor += total;
+    __syncthreads();                                       // wcount reused
   }
 
   if (b < E) {
