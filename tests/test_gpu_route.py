@@ -61,5 +61,6 @@ def test_degenerate():
     _check(ids, 8)
     _check(g.integers(0, 1, (50, 1)).astype(np.int32), 1)                  # E = 1
     _check(g.integers(0, 1024, (40, 4)).astype(np.int32), 1024)            # E = 1024, most empty
-    _check(g.integers(0, 16, (16385, 3)).astype(np.int32), 16)             # several super-chunks
+    _check(g.integers(0, 16, (16385, 3)).astype(np.int32), 16)             # two LDS chunks
+    _check(g.integers(-2, 64, (9000, 8)).astype(np.int32), 64)             # three chunks, dropped
     _check(np.full((1, 1), -1, dtype=np.int32), 4)                          # only a dropped pair
