@@ -30,6 +30,7 @@
 //  * tiles past the last expert tile zero the rows of dropped pairs, in the
 //    same launch.  Every output element is written once: no atomics.
 #include <type_traits>
+#include <utility>
 
 #include "gq_device.hpp"
 #include "gq_host.hpp"
@@ -237,6 +238,56 @@ __device__ __forceinline__ void dg_decode_chunk(const DgCodes& R, const float* A
   *reinterpret_cast<u32x4*>(Bs + (j4 * 4 + c) * kBStride + r8 * 8) = v;
 }
 
+// Epilogue shared by the forward and dgrad kernels.  A transposed
+// accumulator block (32 columns x 32 rows, weights as the first MFMA
+// operand) gives lane (lr, lh) the row lr of the sub-tile at columns
+// 8q + 4 lh + [0, 4), q = r / 4.  The lane scales by its row's pair weight,
+// rounds to bf16 and swaps half of its words with the partner lane 32 away
+// (v_permlane32_swap), after which each lane holds 8 consecutive columns and
+// writes them as one 16-byte piece of the output row.
+__device__ __forceinline__ void store_block_t(const float (&v)[16], uint16_t* orow, int lh) {
+  uint32_t w[4][2];                                        // columns 8q + 4 lh + [0, 4)
+#pragma unroll
+  for (int q = 0; q < 4; ++q) {
+    w[q][0] = pack_bf16x2(v[4 * q], v[4 * q + 1]);
+    w[q][1] = pack_bf16x2(v[4 * q + 2], v[4 * q + 3]);
+  }
+#pragma unroll
+  for (int jp = 0; jp < 2; ++jp) {
+    // after the swap: lane half 0 holds columns 16 jp + [0, 8), half 1
+    // columns 16 jp + [8, 16)
+    const auto s0 = __builtin_amdgcn_permlane32_swap(w[2 * jp][0], w[2 * jp + 1][0], false, false);
+    const auto s1 = __builtin_amdgcn_permlane32_swap(w[2 * jp][1], w[2 * jp + 1][1], false, false);
+    *reinterpret_cast<u32x4*>(orow + 16 * jp + 8 * lh) = u32x4{s0[0], s1[0], s0[1], s1[1]};
+  }
+}
+
+// Rows of sub-tiles ms0, ms1 (32 rows each) for the 128 B columns of a
+// 256 x 128 tile (SwiGLU: 64 outputs from gate blocks 0, 1 and up blocks 2, 3).
+template <bool kGlu, int kTNo>
+__device__ __forceinline__ void store_rows_t(const f32x16 (&acc)[2][4], bool act0, bool act1,
+                                             int ms0, int ms1, int valid, const int* pair_s,
+                                             const GemmArgs& g, int n0, int lr, int lh) {
+#pragma unroll
+  for (int j = 0; j < 2; ++j) {
+    if (!(j ? act1 : act0)) continue;
+    const int m = (j ? ms1 : ms0) * 32 + lr;
+    const int p = pair_s[m];
+    const float sc = (g.pair_scale && m < valid) ? g.pair_scale[p] : 1.f;
+#pragma unroll
+    for (int c = 0; c < kTNo / 32; ++c) {
+      const int col = n0 + 32 * c;
+      if (m < valid && col < g.Nout) {
+        float v[16];
+#pragma unroll
+        for (int r = 0; r < 16; ++r)
+          v[r] = kGlu ? silu_f32(acc[j][c][r]) * acc[j][c + 2][r] * sc : acc[j][c][r] * sc;
+        store_block_t(v, g.out + (int64_t)p * g.Nout + col, lh);
+      }
+    }
+  }
+}
+
 // ---- the kernel ----
 // Software pipeline, one barrier per K step.  Iteration ks:
 //   issue the global loads that step ks+1 (activations) and ks+2 (codes)
@@ -388,19 +439,21 @@ __device__ __forceinline__ void grouped_gemm_body(const GemmArgs& g) {
     constexpr int kRows = decltype(rows_c)::value;
 #pragma unroll
     for (int c = 0; c < 4; ++c) {
+      // weights as the first operand: the accumulator holds the transposed
+      // tile, one output row per lane
       if constexpr (kRows == 0) {
         if (c * 32 >= ncols) continue;
         if (act0)
-          acc[0][c] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(a[0]), b[c], acc[0][c],
+          acc[0][c] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(b[c], as_bf16x8(a[0]), acc[0][c],
                                                               0, 0, 0);
         if (act1)
-          acc[1][c] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(a[1]), b[c], acc[1][c],
+          acc[1][c] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(b[c], as_bf16x8(a[1]), acc[1][c],
                                                               0, 0, 0);
       } else {
-        acc[0][c] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(a[0]), b[c], acc[0][c],
+        acc[0][c] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(b[c], as_bf16x8(a[0]), acc[0][c],
                                                             0, 0, 0);
         if constexpr (kRows == 2)
-          acc[1][c] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(a[1]), b[c], acc[1][c],
+          acc[1][c] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(b[c], as_bf16x8(a[1]), acc[1][c],
                                                               0, 0, 0);
       }
     }
@@ -499,79 +552,406 @@ __device__ __forceinline__ void grouped_gemm_body(const GemmArgs& g) {
   else if (ncols == kTN && act0) run_loop(std::integral_constant<int, 1>{});
   else run_loop(std::integral_constant<int, 0>{});
 
-  // ---- epilogue: scale, round to bf16, stage each 32-row sub-tile in LDS
-  // (the B buffers are free now), then write whole output rows with 16-byte
-  // stores instead of scattered 2-byte ones. ----
-  constexpr int kOStride = kTN + 8;                         // padded row: conflict-free
-  static_assert(4 * 32 * kOStride <= 2 * kTN * kBStride, "staging must fit in Bs");
-  constexpr int kChunks = kTNo / 8;                         // 16-byte chunks per tile row
-  const int ocols = min(kTNo, g.Nout - n0);                 // output columns of this tile
+  // ---- epilogue: one output row per lane, written from registers ----
+  store_rows_t<kGlu, kTNo>(acc, act0, act1, ms0, ms1, valid, pair_s, g, n0, lr, lh);
+}
+
+// The dgrad fits 2 waves per SIMD (2 workgroups per CU): it keeps its code
+// words two rows per register and re-reads the row factors from LDS.
+template <int kMode>
+__global__ __launch_bounds__(kGemmThreads, 2) void grouped_dgrad_kernel(GemmArgs g) {
+  grouped_gemm_body<kMode>(g);
+}
+// Forward products with a short contraction (few K steps per tile) run on
+// the two-workgroups-per-CU kernel: one workgroup's prologue and epilogue
+// then overlap the other's matrix work.
+template <int kMode>
+__global__ __launch_bounds__(kGemmThreads, 2) void grouped_gemm_fwd_shortk_kernel(GemmArgs g) {
+  grouped_gemm_body<kMode>(g);
+}
+
+// ---- forward kernel: 256 x 256 output tile, one wave per SIMD ----
+// Workgroup = 4 waves on one CU (one workgroup per CU: ~137 KB of LDS).
+//  * A (gathered activation rows, 256 x 64 per K step) goes from global
+//    memory straight into LDS with LDS-direct loads (no register round trip),
+//    double-buffered; rows are 128 bytes with the 16-byte chunk slot
+//    XOR-swizzled by (row >> 1) & 7 (conflict-free fragment reads).  Lane L
+//    of a load instruction fills slot L % 8 of row L / 8 of an 8-row group,
+//    so it fetches the global chunk (L % 8) ^ swizzle(row).
+//  * B (256 weight rows x 64 K per step) is decoded once per workgroup: thread
+//    t decodes the 64 codes of B column t (one NF4 absmax block or two MXFP4
+//    scale blocks) into bf16 in LDS (double-buffered, padded rows).
+//  * wave w owns the 32-row sub-tiles (w & 1) + 2i, i < 4 (interleaved so
+//    that short expert segments keep all four SIMDs busy) times the 128
+//    columns 128 * (w >> 1) + [0, 128): 4 x 4 v_mfma_f32_32x32x16_bf16 per
+//    16-wide K slice, accumulators in AGPRs.
+//  * K step ks: issue the LDS-direct loads of step ks+1's activations and the
+//    code loads of step ks+2; per slice, read the next slice's fragments,
+//    decode an eighth of step ks+1's B tile into the other buffer and run
+//    the slice's 16 MFMAs; wait for the step's loads, one barrier.
+// For the SwiGLU variant the 256 B columns are gate rows j0 + [0, 64), the
+// matching up rows, gate rows j0 + [64, 128), their up rows: each wave holds
+// the gate and up values of the same 64 outputs.
+constexpr int kXN = 256;                                  // B columns per tile
+
+typedef __attribute__((address_space(3))) void lds_void_t;
+typedef __attribute__((address_space(1))) const void glb_void_t;
+
+struct XLoad {
+  u32x4 c0, c1;    // codes of chunks 0-3 and 4-7 (8 weights each)
+  float a;         // NF4 absmax
+  uint32_t s0, s1; // MXFP4 scale bytes of the two 32-weight blocks
+  bool ok, ok1;    // column inside the matrix; second MXFP4 block inside K
+};
+
+template <int kMode>
+__device__ __forceinline__ XLoad x_load(const GemmArgs& g, int e, int n0, int ks, int t) {
+  XLoad L;
+  int n;
+  if constexpr (kMode == kFwdNF4Glu) {
+    const int j = n0 + (t & 63) + ((t >> 7) << 6);         // output column
+    L.ok = j < g.Nout;
+    n = min(j, g.Nout - 1) + (((t >> 6) & 1) ? g.Nout : 0);
+  } else {
+    n = n0 + t;
+    L.ok = n < g.Nw;
+    n = min(n, g.Nw - 1);
+  }
+  const int k0 = ks * kTK;                                  // < Kw
+  const bool full = k0 + kTK <= g.Kw;                       // MXFP4 K tail: half a step
+  const size_t row = (size_t)e * g.Nw + n;
+  const uint8_t* p = g.codes + row * (size_t)(g.Kw / 2) + k0 / 2;
+  L.c0 = *reinterpret_cast<const u32x4*>(p);
+  L.c1 = *reinterpret_cast<const u32x4*>(full ? p + 16 : p);
+  if constexpr (kMode == kFwdMX) {
+    const uint8_t* sp = static_cast<const uint8_t*>(g.scl) + row * (size_t)(g.Kw / 32) + k0 / 32;
+    L.s0 = sp[0];
+    L.s1 = sp[full ? 1 : 0];
+    L.ok1 = L.ok && full;
+    L.a = 0.f;
+  } else {
+    L.a = static_cast<const float*>(g.scl)[row * (size_t)(g.Kw / 64) + ks];
+    L.s0 = L.s1 = 0u;
+    L.ok1 = L.ok;
+  }
+  return L;
+}
+
+template <int kMode>
+__device__ __forceinline__ void x_decode_chunk(const XLoad& L, int q, const float* lut,
+                                               uint16_t* B, int t) {
+  const uint32_t cw = q < 4 ? L.c0[q & 3] : L.c1[q & 3];
+  uint32_t p[4];
+  if constexpr (kMode == kFwdMX) {
+    const float sc = q < 4 ? (L.ok ? e8m0_to_f32(L.s0) : 0.f) : (L.ok1 ? e8m0_to_f32(L.s1) : 0.f);
+#pragma unroll
+    for (int b = 0; b < 4; ++b) p[b] = e2m1_pair_bf16_scaled(cw, b, sc);
+  } else {
+    nf4_decode8_bf16(lut, cw, L.ok ? L.a : 0.f, p);
+  }
+  *reinterpret_cast<u32x4*>(B + t * kBStride + 8 * q) = u32x4{p[0], p[1], p[2], p[3]};
+}
+
+// NF4 decode split in two so the table reads can run a slice ahead of their
+// use: fetch the codebook values of chunks q, q+1, then scale, round and
+// store them.
+__device__ __forceinline__ uint32_t x_chunk_word(const XLoad& L, int q) {
+  return q < 4 ? L.c0[q & 3] : L.c1[q & 3];
+}
+__device__ __forceinline__ void x_fetch2(const XLoad& L, int q, const float* lut, float (&v)[16]) {
+  nf4_lookup8(lut, x_chunk_word(L, q), v);
+  nf4_lookup8(lut, x_chunk_word(L, q + 1), v + 8);
+}
+__device__ __forceinline__ void x_finish2(const XLoad& L, int q, const float (&v)[16], uint16_t* B,
+                                          int t) {
+  const float a = L.ok ? L.a : 0.f;
+#pragma unroll
+  for (int c = 0; c < 2; ++c) {
+    uint32_t p[4];
+#pragma unroll
+    for (int b = 0; b < 4; ++b) p[b] = pack_bf16x2(v[8 * c + 2 * b] * a, v[8 * c + 2 * b + 1] * a);
+    *reinterpret_cast<u32x4*>(B + t * kBStride + 8 * (q + c)) = u32x4{p[0], p[1], p[2], p[3]};
+  }
+}
+
+// Instruction interleave for one K slice of kM MFMAs: after each MFMA, an
+// even share of the slice's LDS reads, VALU ops and LDS writes, so that the
+// single wave of a SIMD keeps the matrix core fed while it decodes.
+template <int kM, int kDs, int kValu, int kDsw, int m>
+__device__ __forceinline__ void sched_one() {
+  __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+  constexpr int ds = kDs * (m + 1) / kM - kDs * m / kM;
+  constexpr int va = kValu * (m + 1) / kM - kValu * m / kM;
+  constexpr int dw = kDsw * (m + 1) / kM - kDsw * m / kM;
+  if constexpr (ds > 0) __builtin_amdgcn_sched_group_barrier(0x100, ds, 0);
+  if constexpr (va > 0) __builtin_amdgcn_sched_group_barrier(0x002, va, 0);
+  if constexpr (dw > 0) __builtin_amdgcn_sched_group_barrier(0x200, dw, 0);
+}
+template <int kM, int kDs, int kValu, int kDsw, int... I>
+__device__ __forceinline__ void sched_slice_seq(std::integer_sequence<int, I...>) {
+  (sched_one<kM, kDs, kValu, kDsw, I>(), ...);
+}
+template <int kM, int kDs, int kValu, int kDsw>
+__device__ __forceinline__ void sched_slice() {
+  sched_slice_seq<kM, kDs, kValu, kDsw>(std::make_integer_sequence<int, kM>{});
+}
+
+template <int kMode>
+__global__ __launch_bounds__(kGemmThreads, 1) void grouped_gemm_fwd_kernel(GemmArgs g) {
+  constexpr bool kGlu = kMode == kFwdNF4Glu;
+  constexpr bool kMx = kMode == kFwdMX;
+  constexpr int kTNo = kGlu ? kXN / 2 : kXN;               // output columns per tile
+  // Separate arrays: the compiler then knows that an LDS-direct load into one
+  // buffer does not alias reads of the other (no extra waits).
+  __shared__ __attribute__((aligned(16))) uint16_t A0[kTM * kTK];
+  __shared__ __attribute__((aligned(16))) uint16_t A1[kTM * kTK];
+  __shared__ __attribute__((aligned(16))) uint16_t B0[kXN * kBStride];
+  __shared__ __attribute__((aligned(16))) uint16_t B1[kXN * kBStride];
+  __shared__ int pair_s[kTM];
+  __shared__ float lut[16];
+
+  const int tid = threadIdx.x;
+  const int C = g.n_col_tiles;
+  const int bid = blockIdx.x;
+  const int qb = bid >> 3, xcd = bid & 7;
+  const int logical = (qb / C) * (8 * C) + xcd * C + (qb % C);
+  if (logical >= g.n_logical) return;
+  const int tile = logical / C;
+  const int n0 = (logical % C) * kTNo;
+  const int T = *g.num_tiles;
+
+  if (tile >= T) {
+    // Zero the rows of dropped pairs (ids outside [0, E)), columns [n0, n0+kTNo).
+    const int dstart = g.offsets[g.E] + (tile - T) * kTM;
+    if (dstart >= g.P || dstart < 0) return;
+    const int dvalid = min(kTM, g.P - dstart);
+    for (int idx = tid; idx < dvalid * (kTNo / 8); idx += kGemmThreads) {
+      const int r = idx / (kTNo / 8), c8 = idx % (kTNo / 8);
+      const int col = n0 + c8 * 8;
+      const int p = g.sorted_pairs[dstart + r];
+      if (col < g.Nout && (unsigned)p < (unsigned)g.P)
+        *reinterpret_cast<u32x4*>(g.out + (int64_t)p * g.Nout + col) = u32x4{0u, 0u, 0u, 0u};
+    }
+    return;
+  }
+
+  const int e = g.tiles[2 * tile];
+  const int start = g.tiles[2 * tile + 1];
+  if ((unsigned)e >= (unsigned)g.E || (unsigned)start >= (unsigned)g.P) return;
+  const int valid = min(kTM, min(g.offsets[e + 1], g.P) - start);
+  if (valid <= 0) return;
+  {
+    int p = g.sorted_pairs[start + min(tid, valid - 1)];
+    pair_s[tid] = ((unsigned)p < (unsigned)g.P) ? p : 0;
+  }
+  if constexpr (!kMx) nf4_lut_init(lut, tid);
   lds_barrier();
-  uint16_t* stage = &Bs[0][0] + wave * (32 * kOStride);
+
+  // wave index as a scalar: per-wave branches stay scalar branches
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6), lane = tid & 63;
+  const int lr = lane & 31, lh = lane >> 5;
+  const int rg = wave & 1, hc = wave >> 1;
+  const int nsteps = (g.Kc + kTK - 1) / kTK;
+  const bool ktail = kMx && (g.Kc % kTK) != 0;             // MXFP4: last step half full
+  const int ovalid = g.Nout - n0;                          // output columns left (multiple of 32)
+
+  // LDS-direct activation loads: instruction j of wave w fills rows
+  // 64w + 8j + [0, 8).  Byte offsets of the lane's 8 source chunks; they
+  // fit 32 bits (host check on rows * stride).
+  uint32_t voff[8];
+  uint32_t tailbits = 0;                                   // chunk >= 4 (MXFP4 K tail)
 #pragma unroll
-  for (int j = 0; j < 2; ++j) {
-    const int ms = j ? ms1 : ms0;
-    if (!(j ? act1 : act0)) continue;
+  for (int j = 0; j < 8; ++j) {
+    const int R = 64 * wave + 8 * j + (lane >> 3);
+    const int c = (lane & 7) ^ ((R >> 1) & 7);
+    voff[j] = (uint32_t)(pair_s[R] / g.topk) * (uint32_t)(g.x_stride * 2) + 16u * (uint32_t)c;
+    tailbits |= (c >= 4 ? 1u : 0u) << j;
+  }
+  // MXFP4 K tail (last step half full): lanes whose chunk lies past K write
+  // zeros to their LDS slot instead of loading, so no operand needs masking.
+  auto dma_a = [&](int ks, uint16_t* Adst) {
+    const char* xb = reinterpret_cast<const char*>(g.x) + (size_t)ks * (kTK * 2);
+    const bool tail = ktail && ks == nsteps - 1;
 #pragma unroll
-    for (int r = 0; r < 16; ++r) {
-      const int rr = (r >> 2) * 8 + lh * 4 + (r & 3);
-      const int m = ms * 32 + rr;
-      const float sc = (g.pair_scale && m < valid) ? g.pair_scale[pair_s[m]] : 1.f;
-      if constexpr (kGlu) {
-        // column blocks 0, 1 hold gate, 2, 3 the up values of the same outputs
-#pragma unroll
-        for (int c = 0; c < 2; ++c)
-          stage[rr * kOStride + c * 32 + lr] =
-              f32_to_bf16_bits(silu_f32(acc[j][c][r]) * acc[j][c + 2][r] * sc);
-      } else {
-#pragma unroll
-        for (int c = 0; c < 4; ++c)
-          stage[rr * kOStride + c * 32 + lr] = f32_to_bf16_bits(acc[j][c][r] * sc);
+    for (int j = 0; j < 8; ++j) {
+      if (64 * wave + 8 * j < valid) {                     // rows past the segment: skipped
+        uint16_t* dst = Adst + (64 * wave + 8 * j) * kTK;
+        if (kMx && tail && ((tailbits >> j) & 1u)) {
+          *reinterpret_cast<u32x4*>(dst + lane * 8) = u32x4{0u, 0u, 0u, 0u};
+        } else {
+          __builtin_amdgcn_global_load_lds((glb_void_t*)(xb + voff[j]), (lds_void_t*)dst, 16, 0,
+                                           0);
+        }
       }
     }
-    // a wave's LDS operations complete in order: no barrier needed to read back
+  };
+  // Fragment reads: A rows 32 * (2i + rg) + lr, B columns 128 hc + 32 cb + lr;
+  // lane half lh takes K chunk 4 lh + sl of slice sl.
+  const int aslot_x = (lr >> 1) & 7;
+  auto read_a = [&](const uint16_t* A, int i, int sl) -> u32x4 {
+    const int R = 32 * (2 * i + rg) + lr;
+    return *reinterpret_cast<const u32x4*>(A + R * kTK + (((lh * 4 + sl) ^ aslot_x) * 8));
+  };
+  auto read_b = [&](const uint16_t* B, int cb, int sl) -> bf16x8 {
+    return as_bf16x8(*reinterpret_cast<const u32x4*>(
+        B + (128 * hc + 32 * cb + lr) * kBStride + (lh * 4 + sl) * 8));
+  };
+
+  f32x16 acc[4][4];
 #pragma unroll
-    for (int it = 0; it < 32 * kChunks / 64; ++it) {
-      const int chunk = it * 64 + lane;                   // 32 rows x kChunks chunks
-      const int rr = chunk / kChunks, c8 = chunk % kChunks;
-      const int m = ms * 32 + rr;
-      if (m < valid && c8 * 8 < ocols) {
-        const u32x4 v = *reinterpret_cast<const u32x4*>(stage + rr * kOStride + c8 * 8);
-        *reinterpret_cast<u32x4*>(g.out + (int64_t)pair_s[m] * g.Nout + n0 + c8 * 8) = v;
+  for (int i = 0; i < 4; ++i)
+#pragma unroll
+    for (int c = 0; c < 4; ++c)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) acc[i][c][r] = 0.f;
+
+  bool act[4], cok[4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    act[i] = 32 * (2 * i + rg) < valid;
+    // SwiGLU: column blocks 0, 1 hold gate, 2, 3 the up values of outputs 64 hc + 32 (i & 1)
+    cok[i] = kGlu ? 64 * hc + 32 * (i & 1) < ovalid : 128 * hc + 32 * i < ovalid;
+  }
+  int nrows = 0;
+#pragma unroll
+  for (int i = 0; i < 4; ++i) nrows += act[i] ? 1 : 0;
+  const bool allcols = kGlu ? 64 * hc + 64 <= ovalid : 128 * hc + 128 <= ovalid;
+
+  // ---- prologue: step 0 staged and decoded; step 1's codes in flight ----
+  XLoad X = x_load<kMode>(g, e, n0, 0, tid);
+  XLoad Y = x_load<kMode>(g, e, n0, min(1, nsteps - 1), tid);
+  dma_a(0, A0);
+#pragma unroll
+  for (int q = 0; q < 8; ++q) x_decode_chunk<kMode>(X, q, lut, B0, tid);
+  float qn[16];                                             // NF4: fetched table values in flight
+  if constexpr (!kMx) x_fetch2(Y, 0, lut, qn);
+  __builtin_amdgcn_s_waitcnt(0);                            // everything, incl. the LDS-direct loads
+  lds_barrier();
+
+  auto run_loop = [&](auto rows_c) {
+    constexpr int kRows = decltype(rows_c)::value;         // -1: guarded generic path
+    auto step = [&](int ks, const uint16_t* Ac, uint16_t* An, const uint16_t* Bc, uint16_t* Bn,
+                    XLoad& Ldec, XLoad& Lfill) {
+      dma_a(min(ks + 1, nsteps - 1), An);
+      Lfill = x_load<kMode>(g, e, n0, min(ks + 2, nsteps - 1), tid);
+      __builtin_amdgcn_sched_barrier(0);                   // keep the loads at the step start
+      u32x4 fa[2][4];
+      bf16x8 fb[2][4];
+      auto frags = [&](int sl, u32x4 (&a)[4], bf16x8 (&b)[4]) {
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          if (kRows >= 0 ? i < kRows : true) a[i] = read_a(Ac, i, sl);
+        }
+#pragma unroll
+        for (int c = 0; c < 4; ++c) b[c] = read_b(Bc, c, sl);
+      };
+      auto mfmas = [&](const u32x4 (&a)[4], const bf16x8 (&b)[4]) {
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+#pragma unroll
+          for (int c = 0; c < 4; ++c) {
+            // weights as the first operand: the accumulator holds the
+            // transposed tile, one output row per lane
+            if constexpr (kRows >= 0) {
+              if (i < kRows)
+                acc[i][c] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(b[c], as_bf16x8(a[i]),
+                                                                    acc[i][c], 0, 0, 0);
+            } else {
+              if (act[i] && cok[c])
+                acc[i][c] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(b[c], as_bf16x8(a[i]),
+                                                                    acc[i][c], 0, 0, 0);
+            }
+          }
+      };
+      frags(0, fa[0], fb[0]);
+#pragma unroll
+      for (int sl = 0; sl < 4; ++sl) {
+        if (sl < 3) frags(sl + 1, fa[(sl + 1) & 1], fb[(sl + 1) & 1]);
+        if constexpr (kMx) {
+          x_decode_chunk<kMode>(Ldec, 2 * sl, lut, Bn, tid);
+          x_decode_chunk<kMode>(Ldec, 2 * sl + 1, lut, Bn, tid);
+        } else {
+          // table values of the next slice's chunks (the next step's first
+          // two after the last slice), then finish this slice's two chunks
+          float qf[16];
+          if (sl < 3) x_fetch2(Ldec, 2 * sl + 2, lut, qf);
+          else x_fetch2(Lfill, 0, lut, qf);
+          x_finish2(Ldec, 2 * sl, qn, Bn, tid);
+#pragma unroll
+          for (int u = 0; u < 16; ++u) qn[u] = qf[u];
+        }
+        mfmas(fa[sl & 1], fb[sl & 1]);
+        if constexpr (kRows > 0) {
+          constexpr int kM = 4 * kRows;
+          if constexpr (kMx) sched_slice<kM, 4 + kRows, 10, 2>();
+          else sched_slice<kM, 20 + kRows, 48, 2>();
+        }
+      }
+      __builtin_amdgcn_s_waitcnt(0x0F70);                  // vmcnt(0): this step's loads landed
+      lds_barrier();
+    };
+    for (int ks = 0; ks < nsteps; ks += 2) {
+      step(ks, A0, A1, B0, B1, Y, X);
+      if (ks + 1 < nsteps) step(ks + 1, A1, A0, B1, B0, X, Y);
+    }
+  };
+  if (allcols && nrows == 4) run_loop(std::integral_constant<int, 4>{});
+  else if (allcols && nrows == 3) run_loop(std::integral_constant<int, 3>{});
+  else if (allcols && nrows == 2) run_loop(std::integral_constant<int, 2>{});
+  else if (allcols && nrows == 1) run_loop(std::integral_constant<int, 1>{});
+  else run_loop(std::integral_constant<int, -1>{});
+
+  // ---- epilogue: one output row per lane (see store_block_t) ----
+  constexpr int kWo = kGlu ? 64 : 128;                     // output columns per wave
+  const int c0 = n0 + hc * kWo;                             // first output column of the wave
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    if (!act[i]) continue;
+    const int m = 32 * (2 * i + rg) + lr;
+    const int p = pair_s[m];
+    const float sc = (g.pair_scale && m < valid) ? g.pair_scale[p] : 1.f;
+#pragma unroll
+    for (int c = 0; c < kWo / 32; ++c) {
+      const int col = c0 + 32 * c;
+      if (m < valid && col < g.Nout) {
+        float v[16];
+#pragma unroll
+        for (int r = 0; r < 16; ++r)
+          v[r] = kGlu ? silu_f32(acc[i][c][r]) * acc[i][c + 2][r] * sc : acc[i][c][r] * sc;
+        store_block_t(v, g.out + (int64_t)p * g.Nout + col, lh);
       }
     }
   }
 }
 
-// Both kernels fit 2 waves per SIMD (2 workgroups per CU): the dgrad keeps
-// its code words two rows per register and re-reads the row factors from LDS.
-template <int kMode>
-__global__ __launch_bounds__(kGemmThreads, 2) void grouped_gemm_fwd_kernel(GemmArgs g) {
-  grouped_gemm_body<kMode>(g);
-}
-template <int kMode>
-__global__ __launch_bounds__(kGemmThreads, 2) void grouped_dgrad_kernel(GemmArgs g) {
-  grouped_gemm_body<kMode>(g);
-}
+// Contractions of at least this many elements use the 256 x 256 kernel
+// (one wave per SIMD); shorter ones the 256 x 128 kernel, two workgroups per CU.
+constexpr int kLongK = 1024;
 
 template <int kMode>
 static int launch_gemm(GemmArgs g, int32_t max_tiles, int32_t tile_m, hipStream_t stream) {
   if (tile_m != kTM) return kNotSupported;
   const int64_t need = (int64_t)(g.P + kTM - 1) / kTM + g.E + 1;
   if (max_tiles < need) return kInvalid;
-  constexpr int kTNo = kMode == kFwdNF4Glu ? kTN / 2 : kTN;
+  constexpr bool kDgMode = kMode == kDgradNF4 || kMode == kDgradMX;
+  const bool wide = !kDgMode && g.Kc >= kLongK;
+  const int kW = wide ? kXN : kTN;                          // B columns per tile
+  const int kTNo = kMode == kFwdNF4Glu ? kW / 2 : kW;       // output columns per tile
   g.n_col_tiles = (g.Nout + kTNo - 1) / kTNo;
   const int64_t n_logical = (int64_t)max_tiles * g.n_col_tiles;
   const int64_t group = 8LL * g.n_col_tiles;
   const int64_t grid = ((n_logical + group - 1) / group) * group;
   if (grid > INT32_MAX) return kNotSupported;
   g.n_logical = (int)n_logical;
-  if constexpr (kMode == kDgradNF4 || kMode == kDgradMX)
+  if constexpr (kDgMode)
     hipLaunchKernelGGL(grouped_dgrad_kernel<kMode>, dim3((unsigned)grid), dim3(kGemmThreads), 0,
                        stream, g);
-  else
+  else if (wide)
     hipLaunchKernelGGL(grouped_gemm_fwd_kernel<kMode>, dim3((unsigned)grid), dim3(kGemmThreads),
                        0, stream, g);
+  else
+    hipLaunchKernelGGL(grouped_gemm_fwd_shortk_kernel<kMode>, dim3((unsigned)grid),
+                       dim3(kGemmThreads), 0, stream, g);
   return launch_status();
 }
 

@@ -50,11 +50,14 @@ def test_tiny_workload():
         assert_slices(bf16_to_host_f32(out), ref, ids, E)
 
 
-@pytest.mark.parametrize("fmt,N,K", [("nf4", 320, 768), ("mx", 288, 544), ("mx", 160, 576)])
+@pytest.mark.parametrize("fmt,N,K", [("nf4", 320, 768), ("mx", 288, 544), ("mx", 160, 576),
+                                     ("nf4", 320, 1088), ("nf4", 544, 1024), ("mx", 288, 1056),
+                                     ("mx", 160, 1120)])
 def test_ragged_multi_tile(fmt, N, K):
     """Skewed routing: one expert spans several 256-row tiles with a ragged
-    tail, others are short or empty; N is not a multiple of 128; MXFP4 K=544
-    leaves a half 64-step; some ids are dropped."""
+    tail, others are short or empty; N is not a multiple of the column tile
+    (128 for K < 1024, 256 from K = 1024 on, where the other kernel runs);
+    MXFP4 K = 544, 1056, 1120 leave a half 64-step; some ids are dropped."""
     dev = device()
     g = np.random.default_rng(N + K)
     E, M, topk = 6, 700, 2
@@ -71,18 +74,21 @@ def test_ragged_multi_tile(fmt, N, K):
     assert_slices(bf16_to_host_f32(out), ref, ids, E)
 
 
-@pytest.mark.parametrize("fmt", ["nf4", "mx"])
-def test_one_hot_probe_is_bit_exact(fmt):
+@pytest.mark.parametrize("fmt,K", [("nf4", 256), ("mx", 256), ("nf4", 1088), ("mx", 1056)])
+def test_one_hot_probe_is_bit_exact(fmt, K):
+    """A one-hot activation row picks one weight column: the output is the
+    decoded weight, bit for bit, in both forward kernels (K = 1056 ends in a
+    half-filled MXFP4 step)."""
     dev = device()
     g = np.random.default_rng(5)
-    E, N, K = 2, 128, 256
+    E, N = 2, 128
     bank = packed_nf4_bank(g, E, N, K) if fmt == "nf4" else packed_mx_bank(g, E, N, K)
     W = LazyDecoded(fmt, *bank)
-    ks = np.array([0, 1, 31, 32, 63, 64, 100, 255])
+    ks = np.array(sorted({0, 1, 31, 32, 63, 64, 100, K // 2 + 7, K - 33, K - 32, K - 1}))
     x = np.zeros((len(ks), K), dtype=np.uint16)
     x[np.arange(len(ks)), ks] = 0x3F80
     ids = np.stack([np.zeros(len(ks)), np.ones(len(ks))], axis=1).astype(np.int32)
-    say("gemm one-hot", fmt)
+    say("gemm one-hot", fmt, K)
     out = bf16_bits(_gemm(fmt, x, to_dev(bank[0], dev), to_dev(bank[1], dev), ids, E, dev))
     for t, k in enumerate(ks):
         for s in range(2):

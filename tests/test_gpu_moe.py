@@ -63,9 +63,11 @@ def test_gemv_swiglu_qwen(M):
     assert_slices(bf16_to_host_f32(act), ref, ids, E)
 
 
-@pytest.mark.parametrize("E,I,K,M,topk", [(6, 160, 384, 300, 2), (3, 96, 256, 70, 3)])
+@pytest.mark.parametrize("E,I,K,M,topk", [(6, 160, 384, 300, 2), (3, 96, 256, 70, 3),
+                                          (6, 160, 1024, 300, 2), (3, 96, 1152, 70, 3)])
 def test_gemm_swiglu_small(E, I, K, M, topk):
-    """Several row tiles, a ragged last tile; I = 96 leaves a 32-column tile."""
+    """Several row tiles, a ragged last tile; I = 96 and I = 160 leave a
+    partial output tile (64 outputs per tile below K = 1024, 128 from there)."""
     dev = device()
     g = wl.rng(wl.CFG_TINY, 500 + I + M)
     codes, absmax = packed_nf4_bank(g, E, 2 * I, K)
