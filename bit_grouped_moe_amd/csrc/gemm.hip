@@ -707,7 +707,9 @@ __global__ __launch_bounds__(kGemmThreads, 1) void grouped_gemm_fwd_kernel(GemmA
   __shared__ __attribute__((aligned(16))) uint16_t A1[kTM * kTK];
   __shared__ __attribute__((aligned(16))) uint16_t B0[kXN * kBStride];
   __shared__ __attribute__((aligned(16))) uint16_t B1[kXN * kBStride];
-  __shared__ int pair_s[kTM];
+  __shared__ int pair_s[kTM];                              // pair of each tile row
+  __shared__ int row_s[kTM];                               // its activation row (pair / topk)
+  __shared__ float scale_s[kTM];                           // its pair weight (1 if none)
   __shared__ float lut[16];
 
   const int tid = threadIdx.x;
@@ -740,9 +742,19 @@ __global__ __launch_bounds__(kGemmThreads, 1) void grouped_gemm_fwd_kernel(GemmA
   if ((unsigned)e >= (unsigned)g.E || (unsigned)start >= (unsigned)g.P) return;
   const int valid = min(kTM, min(g.offsets[e + 1], g.P) - start);
   if (valid <= 0) return;
+  const int nsteps = (g.Kc + kTK - 1) / kTK;
+  // The codes of steps 0 and 1 depend on the tile only: their loads go out
+  // first, alongside the pair ids (fewer dependent round trips before the
+  // first MFMA).
+  XLoad X = x_load<kMode>(g, e, n0, 0, tid);
+  XLoad Y = x_load<kMode>(g, e, n0, min(1, nsteps - 1), tid);
+  float sc_t;                                              // pair weight of tile row tid
   {
     int p = g.sorted_pairs[start + min(tid, valid - 1)];
-    pair_s[tid] = ((unsigned)p < (unsigned)g.P) ? p : 0;
+    p = ((unsigned)p < (unsigned)g.P) ? p : 0;
+    pair_s[tid] = p;
+    row_s[tid] = p / g.topk;
+    sc_t = g.pair_scale ? g.pair_scale[p] : 1.f;
   }
   if constexpr (!kMx) nf4_lut_init(lut, tid);
   lds_barrier();
@@ -751,7 +763,6 @@ __global__ __launch_bounds__(kGemmThreads, 1) void grouped_gemm_fwd_kernel(GemmA
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6), lane = tid & 63;
   const int lr = lane & 31, lh = lane >> 5;
   const int rg = wave & 1, hc = wave >> 1;
-  const int nsteps = (g.Kc + kTK - 1) / kTK;
   const bool ktail = kMx && (g.Kc % kTK) != 0;             // MXFP4: last step half full
   const int ovalid = g.Nout - n0;                          // output columns left (multiple of 32)
 
@@ -764,7 +775,7 @@ __global__ __launch_bounds__(kGemmThreads, 1) void grouped_gemm_fwd_kernel(GemmA
   for (int j = 0; j < 8; ++j) {
     const int R = 64 * wave + 8 * j + (lane >> 3);
     const int c = (lane & 7) ^ ((R >> 1) & 7);
-    voff[j] = (uint32_t)(pair_s[R] / g.topk) * (uint32_t)(g.x_stride * 2) + 16u * (uint32_t)c;
+    voff[j] = (uint32_t)row_s[R] * (uint32_t)(g.x_stride * 2) + 16u * (uint32_t)c;
     tailbits |= (c >= 4 ? 1u : 0u) << j;
   }
   // MXFP4 K tail (last step half full): lanes whose chunk lies past K write
@@ -818,13 +829,12 @@ __global__ __launch_bounds__(kGemmThreads, 1) void grouped_gemm_fwd_kernel(GemmA
   const bool allcols = kGlu ? 64 * hc + 64 <= ovalid : 128 * hc + 128 <= ovalid;
 
   // ---- prologue: step 0 staged and decoded; step 1's codes in flight ----
-  XLoad X = x_load<kMode>(g, e, n0, 0, tid);
-  XLoad Y = x_load<kMode>(g, e, n0, min(1, nsteps - 1), tid);
   dma_a(0, A0);
 #pragma unroll
   for (int q = 0; q < 8; ++q) x_decode_chunk<kMode>(X, q, lut, B0, tid);
   float qn[16];                                             // NF4: fetched table values in flight
   if constexpr (!kMx) x_fetch2(Y, 0, lut, qn);
+  scale_s[tid] = sc_t;                                      // read in the epilogue
   __builtin_amdgcn_s_waitcnt(0);                            // everything, incl. the LDS-direct loads
   lds_barrier();
 
@@ -881,11 +891,9 @@ __global__ __launch_bounds__(kGemmThreads, 1) void grouped_gemm_fwd_kernel(GemmA
           for (int u = 0; u < 16; ++u) qn[u] = qf[u];
         }
         mfmas(fa[sl & 1], fb[sl & 1]);
-        if constexpr (kRows > 0) {
-          constexpr int kM = 4 * kRows;
-          if constexpr (kMx) sched_slice<kM, 4 + kRows, 10, 2>();
-          else sched_slice<kM, 20 + kRows, 48, 2>();
-        }
+        // (the MXFP4 decode is light enough that the default order is
+        // faster than this interleave)
+        if constexpr (kRows > 0 && !kMx) sched_slice<4 * kRows, 20 + kRows, 48, 2>();
       }
       __builtin_amdgcn_s_waitcnt(0x0F70);                  // vmcnt(0): this step's loads landed
       lds_barrier();
@@ -909,7 +917,7 @@ __global__ __launch_bounds__(kGemmThreads, 1) void grouped_gemm_fwd_kernel(GemmA
     if (!act[i]) continue;
     const int m = 32 * (2 * i + rg) + lr;
     const int p = pair_s[m];
-    const float sc = (g.pair_scale && m < valid) ? g.pair_scale[p] : 1.f;
+    const float sc = scale_s[m];
 #pragma unroll
     for (int c = 0; c < kWo / 32; ++c) {
       const int col = c0 + 32 * c;

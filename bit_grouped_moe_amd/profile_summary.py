@@ -32,7 +32,7 @@ CSRC = os.path.join(HERE, "csrc")
 
 # Launch shapes (grid size in threads) of the bench's Qwen3 NF4 workloads.
 GATE_UP_GEMV = ("grouped_gemv_kernel<false, 2, true, false>", 393216)  # N=1536, K=2048, M=1, top-8
-GATE_UP_GEMM = ("grouped_gemm_fwd_kernel<0>", 811008)      # M=4096 top-8, 257 x 12 tiles
+GATE_UP_GEMM = ("grouped_gemm_fwd_kernel<0>", 405504)      # M=4096 top-8, 257 x 6 tiles
 SOURCES = {"gemv_nf4_gate_up_m1": ["gemv.hip", "gq_device.hpp"],
            "gemm_nf4_gate_up_prefill": ["gemm.hip", "gq_device.hpp"]}
 
