@@ -658,9 +658,9 @@ __device__ __forceinline__ void x_decode_chunk(const XLoad& L, int q, const floa
 __device__ __forceinline__ uint32_t x_chunk_word(const XLoad& L, int q) {
   return q < 4 ? L.c0[q & 3] : L.c1[q & 3];
 }
-__device__ __forceinline__ void x_fetch2(const XLoad& L, int q, const float* lut, float (&v)[16]) {
-  nf4_lookup8(lut, x_chunk_word(L, q), v);
-  nf4_lookup8(lut, x_chunk_word(L, q + 1), v + 8);
+__device__ __forceinline__ void x_fetch2(const XLoad& L, int q, const f32x2* tab, float (&v)[16]) {
+  nf4_pairs8(tab, x_chunk_word(L, q), v);
+  nf4_pairs8(tab, x_chunk_word(L, q + 1), v + 8);
 }
 __device__ __forceinline__ void x_finish2(const XLoad& L, int q, const float (&v)[16], uint16_t* B,
                                           int t) {
@@ -711,6 +711,8 @@ __global__ __launch_bounds__(kGemmThreads, 1) void grouped_gemm_fwd_kernel(GemmA
   __shared__ int row_s[kTM];                               // its activation row (pair / topk)
   __shared__ float scale_s[kTM];                           // its pair weight (1 if none)
   __shared__ float lut[16];
+  // NF4 code-byte pair table; the alignment places it at LDS address 0
+  __shared__ __attribute__((aligned(4096))) f32x2 lut2[256];
 
   const int tid = threadIdx.x;
   const int C = g.n_col_tiles;
@@ -756,7 +758,10 @@ __global__ __launch_bounds__(kGemmThreads, 1) void grouped_gemm_fwd_kernel(GemmA
     row_s[tid] = p / g.topk;
     sc_t = g.pair_scale ? g.pair_scale[p] : 1.f;
   }
-  if constexpr (!kMx) nf4_lut_init(lut, tid);
+  if constexpr (!kMx) {
+    nf4_lut_init(lut, tid);
+    nf4_pairs_init(lut2, tid);
+  }
   lds_barrier();
 
   // wave index as a scalar: per-wave branches stay scalar branches
@@ -833,7 +838,7 @@ __global__ __launch_bounds__(kGemmThreads, 1) void grouped_gemm_fwd_kernel(GemmA
 #pragma unroll
   for (int q = 0; q < 8; ++q) x_decode_chunk<kMode>(X, q, lut, B0, tid);
   float qn[16];                                             // NF4: fetched table values in flight
-  if constexpr (!kMx) x_fetch2(Y, 0, lut, qn);
+  if constexpr (!kMx) x_fetch2(Y, 0, lut2, qn);
   scale_s[tid] = sc_t;                                      // read in the epilogue
   __builtin_amdgcn_s_waitcnt(0);                            // everything, incl. the LDS-direct loads
   lds_barrier();
@@ -884,8 +889,8 @@ __global__ __launch_bounds__(kGemmThreads, 1) void grouped_gemm_fwd_kernel(GemmA
           // table values of the next slice's chunks (the next step's first
           // two after the last slice), then finish this slice's two chunks
           float qf[16];
-          if (sl < 3) x_fetch2(Ldec, 2 * sl + 2, lut, qf);
-          else x_fetch2(Lfill, 0, lut, qf);
+          if (sl < 3) x_fetch2(Ldec, 2 * sl + 2, lut2, qf);
+          else x_fetch2(Lfill, 0, lut2, qf);
           x_finish2(Ldec, 2 * sl, qn, Bn, tid);
 #pragma unroll
           for (int u = 0; u < 16; ++u) qn[u] = qf[u];
@@ -893,7 +898,7 @@ __global__ __launch_bounds__(kGemmThreads, 1) void grouped_gemm_fwd_kernel(GemmA
         mfmas(fa[sl & 1], fb[sl & 1]);
         // (the MXFP4 decode is light enough that the default order is
         // faster than this interleave)
-        if constexpr (kRows > 0 && !kMx) sched_slice<4 * kRows, 20 + kRows, 48, 2>();
+        if constexpr (kRows > 0 && !kMx) sched_slice<4 * kRows, 12 + kRows, 32, 2>();
       }
       __builtin_amdgcn_s_waitcnt(0x0F70);                  // vmcnt(0): this step's loads landed
       lds_barrier();

@@ -117,6 +117,33 @@ __device__ __forceinline__ void nf4_decode8_bf16(const float* lut, uint32_t d, f
   for (int b = 0; b < 4; ++b) out[b] = pack_bf16x2(q[2 * b] * absmax, q[2 * b + 1] * absmax);
 }
 
+// 256-entry table of codebook value pairs indexed by a code byte: entry b
+// holds {value of the high nibble (element 2j), value of the low nibble
+// (element 2j+1)}.  One 8-byte LDS read yields both weights of a byte; with
+// the table at LDS address 0 its byte offset (b << 3) is a single shift.
+__device__ __forceinline__ void nf4_pairs_init(f32x2* tab, int t) {
+  uint32_t hi = 0u, lo = 0u;
+#pragma unroll
+  for (int i = 0; i < 16; ++i) {
+    hi = ((t >> 4) == i) ? kNF4Bits[i] : hi;
+    lo = ((t & 15) == i) ? kNF4Bits[i] : lo;
+  }
+  if (t < 256) tab[t] = f32x2{__uint_as_float(hi), __uint_as_float(lo)};
+}
+
+// NF4 codebook values of the 8 weights of one code dword, in element order,
+// from the pair table.
+__device__ __forceinline__ void nf4_pairs8(const f32x2* tab, uint32_t d, float q[8]) {
+  const char* base = reinterpret_cast<const char*>(tab);
+#pragma unroll
+  for (int b = 0; b < 4; ++b) {
+    const f32x2 v =
+        *reinterpret_cast<const f32x2*>(base + (__builtin_amdgcn_ubfe(d, 8 * b, 8) << 3));
+    q[2 * b] = v.x;
+    q[2 * b + 1] = v.y;
+  }
+}
+
 // SiLU, z * sigmoid(z), in float32.
 __device__ __forceinline__ float silu_f32(float z) { return z / (1.0f + expf(-z)); }
 
