@@ -9,26 +9,27 @@
 // The tiling below is this library's own design for CDNA4.
 //
 // One launch covers every tile of every expert (tile list from
-// gq_route_sort).  A workgroup computes a 256 x 128 output tile:
-//  * rows = 256 routed pairs of one expert (gathered activation rows),
-//  * cols = 128 output features,
-//  * K loop in steps of 64: the B tile (128 x 64 weights) is decoded ONCE
-//    per workgroup from packed codes into bf16 in LDS (double-buffered, one
-//    barrier per step) and shared by the 4 waves; each wave streams its own
-//    activation rows straight from global memory into MFMA registers (no LDS
-//    round trip for A).
-//  * wave w owns the 32-row sub-tiles w and w+4 (interleaved so that short
-//    expert segments still spread over all four SIMDs) across all 128
-//    columns: 2 x 4 v_mfma_f32_32x32x16_bf16 per 16-wide K slice.  Sub-tiles
-//    beyond the expert's row count skip their MFMAs.
-//  * the K order inside a 64-step is permuted identically for A and B
-//    (lane half h takes k in [32h, 32h+32)), which makes every operand load
-//    a contiguous 16-byte piece.
-//  * block index -> tile is XCD-aware: the hardware deals blocks round-robin
-//    to the 8 XCDs; consecutive blocks of one XCD get all column tiles of a
-//    row tile, so the gathered activation rows are reused from that XCD's L2.
-//  * tiles past the last expert tile zero the rows of dropped pairs, in the
-//    same launch.  Every output element is written once: no atomics.
+// gq_route_sort): a workgroup takes 256 routed pairs of one expert (gathered
+// activation rows) times a column tile, and the K loop runs in steps of 64.
+// Two kernels share the tile list, the decode routines and the epilogue:
+//  * contractions of at least 1024 (grouped_gemm_fwd_kernel): 256 columns
+//    per tile, one wave per SIMD, activation tiles loaded straight into LDS
+//    (see the comment above that kernel);
+//  * shorter contractions and the input gradient (grouped_gemm_body): 128
+//    columns per tile, two workgroups per CU so that one workgroup's
+//    prologue and epilogue overlap the other's matrix work.
+// In both, the B tile (weights x 64 K) is decoded ONCE per workgroup from
+// packed codes into bf16 in LDS (double-buffered, one barrier per step) and
+// shared by the waves; the K order inside a step is permuted identically
+// for A and B (lane half h takes k in [32h, 32h+32)), so every operand load
+// is a contiguous 16-byte piece; the weights are the first MFMA operand, so
+// a lane accumulates one output row and the epilogue writes rows from
+// registers.  Block index -> tile is XCD-aware: the hardware deals blocks
+// round-robin to the 8 XCDs, and consecutive blocks of one XCD get all
+// column tiles of a row tile, so the gathered activation rows are reused
+// from that XCD's L2.  Tiles past the last expert tile zero the rows of
+// dropped pairs, in the same launch.  Every output element is written once:
+// no atomics.
 #include <type_traits>
 #include <utility>
 
@@ -288,7 +289,10 @@ __device__ __forceinline__ void store_rows_t(const f32x16 (&acc)[2][4], bool act
   }
 }
 
-// ---- the kernel ----
+// ---- the 256 x 128 kernel (short contractions, input gradient) ----
+// Wave w owns the 32-row sub-tiles w and w+4 (interleaved so that short
+// expert segments still spread over all four SIMDs) across all 128 columns:
+// 2 x 4 v_mfma_f32_32x32x16_bf16 per 16-wide K slice.
 // Software pipeline, one barrier per K step.  Iteration ks:
 //   issue the global loads that step ks+1 (activations) and ks+2 (codes)
 //   need; decode step ks+1 into the LDS buffer the MFMAs are not reading;
@@ -571,7 +575,7 @@ __global__ __launch_bounds__(kGemmThreads, 2) void grouped_gemm_fwd_shortk_kerne
 }
 
 // ---- forward kernel: 256 x 256 output tile, one wave per SIMD ----
-// Workgroup = 4 waves on one CU (one workgroup per CU: ~137 KB of LDS).
+// Workgroup = 4 waves on one CU (one workgroup per CU: ~141 KB of LDS).
 //  * A (gathered activation rows, 256 x 64 per K step) goes from global
 //    memory straight into LDS with LDS-direct loads (no register round trip),
 //    double-buffered; rows are 128 bytes with the 16-byte chunk slot
@@ -580,7 +584,9 @@ __global__ __launch_bounds__(kGemmThreads, 2) void grouped_gemm_fwd_shortk_kerne
 //    so it fetches the global chunk (L % 8) ^ swizzle(row).
 //  * B (256 weight rows x 64 K per step) is decoded once per workgroup: thread
 //    t decodes the 64 codes of B column t (one NF4 absmax block or two MXFP4
-//    scale blocks) into bf16 in LDS (double-buffered, padded rows).
+//    scale blocks) into bf16 in LDS (double-buffered, padded rows).  NF4
+//    goes through the code-byte pair table (nf4_pairs8) at LDS address 0,
+//    its reads one slice ahead of their use.
 //  * wave w owns the 32-row sub-tiles (w & 1) + 2i, i < 4 (interleaved so
 //    that short expert segments keep all four SIMDs busy) times the 128
 //    columns 128 * (w >> 1) + [0, 128): 4 x 4 v_mfma_f32_32x32x16_bf16 per
@@ -588,7 +594,9 @@ __global__ __launch_bounds__(kGemmThreads, 2) void grouped_gemm_fwd_shortk_kerne
 //  * K step ks: issue the LDS-direct loads of step ks+1's activations and the
 //    code loads of step ks+2; per slice, read the next slice's fragments,
 //    decode an eighth of step ks+1's B tile into the other buffer and run
-//    the slice's 16 MFMAs; wait for the step's loads, one barrier.
+//    the slice's 16 MFMAs (NF4: interleaved with the LDS reads and the
+//    decode's VALU work, sched_slice); wait for the step's loads, one
+//    barrier.
 // For the SwiGLU variant the 256 B columns are gate rows j0 + [0, 64), the
 // matching up rows, gate rows j0 + [64, 128), their up rows: each wave holds
 // the gate and up values of the same 64 outputs.
