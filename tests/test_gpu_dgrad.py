@@ -25,8 +25,11 @@ def _dgrad(dy_bits, codes, absmax, pe, E, dev):
     return out
 
 
-@pytest.mark.parametrize("E,N,K,P", [(4, 256, 512, 64), (6, 320, 704, 900)])
+@pytest.mark.parametrize("E,N,K,P", [(4, 256, 512, 64), (6, 320, 704, 900),
+                                     (4, 1024, 512, 600), (6, 1088, 704, 900)])
 def test_small_and_ragged(E, N, K, P):
+    """Several row tiles per expert with a ragged tail, dropped pairs, and a
+    partial column tile (K = 704: 5.5 tiles of 128 columns)."""
     dev = device()
     g = np.random.default_rng(N + K)
     codes, absmax = packed_nf4_bank(g, E, N, K)
@@ -40,20 +43,22 @@ def test_small_and_ragged(E, N, K, P):
     assert_slices(bf16_to_host_f32(out), ref, pe, E)
 
 
-def test_one_hot_probe_is_bit_exact():
-    """dY = e_n makes dX row p the decoded weight row W[n, :] rounded once."""
+@pytest.mark.parametrize("N,K", [(128, 256), (1024, 320)])
+def test_one_hot_probe_is_bit_exact(N, K):
+    """dY = e_n makes dX row p the decoded weight row W[n, :] rounded once
+    (K = 320 leaves a 64-column tile)."""
     dev = device()
     g = np.random.default_rng(6)
-    E, N, K = 2, 128, 256
+    E = 2
     codes, absmax = packed_nf4_bank(g, E, N, K)
     W = LazyDecoded("nf4", codes, absmax)
-    ns = np.array([0, 1, 63, 64, 127])
+    ns = np.array(sorted({0, 1, 63, 64, N // 2 + 9, N - 1}))
     dy = np.zeros((2 * len(ns), N), dtype=np.uint16)
     pe = np.zeros(2 * len(ns), dtype=np.int32)
     for i, n in enumerate(ns):
         dy[2 * i, n] = dy[2 * i + 1, n] = 0x3F80
         pe[2 * i + 1] = 1
-    say("dgrad one-hot")
+    say("dgrad one-hot", N, K)
     out = bf16_bits(_dgrad(dy, to_dev(codes, dev), to_dev(absmax, dev), pe, E, dev))
     for i, n in enumerate(ns):
         for s in range(2):
@@ -102,9 +107,11 @@ def _dgrad_mx(dy_bits, blocks, scales, pe, E, dev):
     return out
 
 
-@pytest.mark.parametrize("E,N,K,P", [(4, 128, 256, 64), (5, 192, 352, 700), (3, 320, 2880, 300)])
+@pytest.mark.parametrize("E,N,K,P", [(4, 128, 256, 64), (5, 192, 352, 700), (3, 320, 2880, 300),
+                                     (3, 1024, 2880, 300), (4, 1152, 352, 500)])
 def test_mx_small_and_ragged(E, N, K, P):
-    """K = 352 and 2880 leave a partial 128-column tile (K % 64 == 32 for 352)."""
+    """K = 352 and 2880 leave a partial 128-column tile (K % 64 == 32 for
+    352); N = 1024, 1152 give 16-18 contraction steps."""
     dev = device()
     g = np.random.default_rng(N + 3 * K)
     blocks, scales = packed_mx_bank(g, E, N, K)
@@ -120,20 +127,22 @@ def test_mx_small_and_ragged(E, N, K, P):
     assert not bf16_bits(out)[dropped].any() or not dropped.any()
 
 
-def test_mx_one_hot_probe_is_bit_exact():
-    """dY = e_n makes dX row p the decoded MXFP4 weight row W[n, :] (exact in bf16)."""
+@pytest.mark.parametrize("N,K", [(128, 224), (1024, 288)])
+def test_mx_one_hot_probe_is_bit_exact(N, K):
+    """dY = e_n makes dX row p the decoded MXFP4 weight row W[n, :] (exact in
+    bf16); K = 288 leaves a 32-column tile."""
     dev = device()
     g = np.random.default_rng(16)
-    E, N, K = 2, 128, 224
+    E = 2
     blocks, scales = packed_mx_bank(g, E, N, K)
     W = LazyDecoded("mx", blocks, scales)
-    ns = np.array([0, 1, 63, 64, 127])
+    ns = np.array(sorted({0, 1, 63, 64, N // 2 + 9, N - 1}))
     dy = np.zeros((2 * len(ns), N), dtype=np.uint16)
     pe = np.zeros(2 * len(ns), dtype=np.int32)
     for i, n in enumerate(ns):
         dy[2 * i, n] = dy[2 * i + 1, n] = 0x3F80
         pe[2 * i + 1] = 1
-    say("mx dgrad one-hot")
+    say("mx dgrad one-hot", N, K)
     out = bf16_bits(_dgrad_mx(dy, to_dev(blocks, dev), to_dev(scales, dev), pe, E, dev))
     for i, n in enumerate(ns):
         for s in range(2):
