@@ -204,9 +204,7 @@ struct DgCodes {
 template <int kMode>
 __device__ __forceinline__ void dg_read_codes(const uint8_t* Cs, const float* As, int tid,
                                               DgCodes& R) {
-  using F = DgFmt<kMode>;
   const int j4 = tid & 31, r8 = tid >> 5;
-  const int blk = (j4 * 4) / F::kBlkK;
 #pragma unroll
   for (int i = 0; i < 8; ++i) {
     const int r = r8 * 8 + i;

@@ -75,15 +75,32 @@ __device__ __forceinline__ float segment_dot(const float* lut, u32x4 c, float am
 // kWaveRows: a row's S segments lie inside one wave (64 % S == 0) and are
 // summed with DPP lane moves; otherwise partial sums meet in LDS.  Both
 // orders are fixed, so results are reproducible.
+// Argument order: what the first loads need (routing ids, activations,
+// weights, sizes) comes first, in the 14 dwords that the build preloads into
+// SGPRs, so the expert-id load issues without waiting for a kernel-argument
+// load; the segment layout is derived from K rather than passed.
 template <bool kMx, int kIter, bool kWaveRows, bool kGlu>
 __global__ __launch_bounds__(kGemvMaxThreads) void grouped_gemv_kernel(
-    const uint16_t* __restrict__ x, int64_t x_stride, int K, const uint8_t* __restrict__ codes,
-    const void* __restrict__ scl, int N, int E, const int32_t* __restrict__ ids, int topk, int P,
-    const float* __restrict__ pair_scale, uint16_t* __restrict__ out, int S, int W, int G,
-    int NT) {
+    const int32_t* __restrict__ ids, const uint16_t* __restrict__ x,
+    const uint8_t* __restrict__ codes, const void* __restrict__ scl, int K, int N, int E,
+    int x_stride, int topk, int P, const float* __restrict__ pair_scale,
+    uint16_t* __restrict__ out) {
   __shared__ float lut[16];
   __shared__ float red[kWaveRows ? 1 : kIter * (kGemvMaxThreads + 32)];
 
+  // segment layout (the host's segment_layout, derived from K)
+  const int S = K >> 5;
+  int W, G, NT;
+  if constexpr (kWaveRows) {
+    const int lgW = S > 1 ? 32 - __builtin_clz(S - 1) : 0;
+    W = 1 << lgW;
+    G = kGemvMaxThreads >> lgW;
+    NT = kGemvMaxThreads;
+  } else {
+    W = S;
+    G = S >= kGemvMaxThreads ? 1 : kGemvMaxThreads / S;
+    NT = ((S * G + kWave - 1) / kWave) * kWave;
+  }
   const int tid = threadIdx.x;                      // NT == blockDim.x
   const int lane = tid & (kWave - 1);
   const int p0 = blockIdx.y;
@@ -256,18 +273,16 @@ __global__ __launch_bounds__(kGemvMaxThreads) void grouped_gemv_kernel(
 }
 
 template <bool kMx, int kIter, bool kGlu>
-static void launch_gemv_iter(dim3 grid, int NT, hipStream_t stream, const uint16_t* x,
-                             int64_t x_stride, int K, const uint8_t* codes, const void* scl,
-                             int N, int E, const int32_t* ids, int topk, int P,
-                             const float* pair_scale, uint16_t* out, int S, int W, int G) {
-  if (S <= kWave)
+static void launch_gemv_iter(dim3 grid, int NT, bool wave_rows, hipStream_t stream,
+                             const uint16_t* x, int x_stride, int K, const uint8_t* codes,
+                             const void* scl, int N, int E, const int32_t* ids, int topk, int P,
+                             const float* pair_scale, uint16_t* out) {
+  if (wave_rows)
     hipLaunchKernelGGL((grouped_gemv_kernel<kMx, kIter, true, kGlu>), grid, dim3(NT), 0, stream,
-                       x, x_stride, K, codes, scl, N, E, ids, topk, P, pair_scale, out, S, W, G,
-                       NT);
+                       ids, x, codes, scl, K, N, E, x_stride, topk, P, pair_scale, out);
   else
     hipLaunchKernelGGL((grouped_gemv_kernel<kMx, kIter, false, kGlu>), grid, dim3(NT), 0, stream,
-                       x, x_stride, K, codes, scl, N, E, ids, topk, P, pair_scale, out, S, W, G,
-                       NT);
+                       ids, x, codes, scl, K, N, E, x_stride, topk, P, pair_scale, out);
 }
 
 // Segment lanes: S segments of 32 weights per row.  S <= 64: a row's
@@ -298,6 +313,7 @@ static int launch_gemv(const uint16_t* x, int32_t rows, int32_t K, int64_t x_str
   if (pair_scale && !aligned4(pair_scale)) return kInvalid;
   const int64_t P = (int64_t)rows * topk;
   if (P > kGemvMaxPairs || K > kGemvMaxK || N >= (1 << 24)) return kNotSupported;
+  if (x_stride > INT32_MAX) return kNotSupported;
   int S, W, G, NT;
   segment_layout(K, S, W, G, NT);
   // Rows per thread: the largest count (8, 4, 2) that still gives enough
@@ -312,12 +328,18 @@ static int launch_gemv(const uint16_t* x, int32_t rows, int32_t K, int64_t x_str
   if (S > kWave && R > NT) return kNotSupported;     // one reduced row per thread
   const dim3 grid((N + R - 1) / R, (unsigned)P);
   switch (iter) {
-    case 8: launch_gemv_iter<kMx, 8, kGlu>(grid, NT, stream, x, x_stride, K, codes, scl, N, E,
-                                           ids, topk, (int)P, pair_scale, out, S, W, G); break;
-    case 4: launch_gemv_iter<kMx, 4, kGlu>(grid, NT, stream, x, x_stride, K, codes, scl, N, E,
-                                           ids, topk, (int)P, pair_scale, out, S, W, G); break;
-    default: launch_gemv_iter<kMx, 2, kGlu>(grid, NT, stream, x, x_stride, K, codes, scl, N, E,
-                                            ids, topk, (int)P, pair_scale, out, S, W, G); break;
+    case 8:
+      launch_gemv_iter<kMx, 8, kGlu>(grid, NT, S <= kWave, stream, x, (int)x_stride, K, codes, scl,
+                                     N, E, ids, topk, (int)P, pair_scale, out);
+      break;
+    case 4:
+      launch_gemv_iter<kMx, 4, kGlu>(grid, NT, S <= kWave, stream, x, (int)x_stride, K, codes, scl,
+                                     N, E, ids, topk, (int)P, pair_scale, out);
+      break;
+    default:
+      launch_gemv_iter<kMx, 2, kGlu>(grid, NT, S <= kWave, stream, x, (int)x_stride, K, codes, scl,
+                                     N, E, ids, topk, (int)P, pair_scale, out);
+      break;
   }
   return launch_status();
 }
@@ -340,12 +362,17 @@ constexpr int kCombineMaxYs = 1024;
 
 template <bool kMx, int kR, int kPPW>
 __global__ __launch_bounds__(kWave * kCombineMaxWaves) void gemv_down_combine_kernel(
-    const uint16_t* __restrict__ act, int64_t a_stride, int I, const uint8_t* __restrict__ codes,
-    const void* __restrict__ scl, int H, int E, const int32_t* __restrict__ ids, int topk, int P,
-    const float* __restrict__ tw, uint16_t* __restrict__ y, int S, int W, int NWv) {
+    const int32_t* __restrict__ ids, const uint16_t* __restrict__ act,
+    const uint8_t* __restrict__ codes, const void* __restrict__ scl, int I, int H, int E,
+    int a_stride, int topk, int P, const float* __restrict__ tw, uint16_t* __restrict__ y) {
   __shared__ float lut[16];
   __shared__ float ys[kCombineMaxYs];                      // [P][Rb]
 
+  // layout derived from I and P as on the host (arguments ordered as in
+  // grouped_gemv_kernel)
+  const int S = I >> 5;
+  const int W = S > 1 ? 1 << (32 - __builtin_clz(S - 1)) : 1;
+  const int NWv = min(P, kCombineMaxWaves);
   const int tid = threadIdx.x, lane = tid & (kWave - 1), wave = tid / kWave;
   const int slots = kWave / W;                             // lane groups per wave
   const int Rb = slots * kR;                               // rows per workgroup
@@ -426,12 +453,11 @@ __global__ __launch_bounds__(kWave * kCombineMaxWaves) void gemv_down_combine_ke
 }
 
 template <bool kMx, int kR, int kPPW>
-static void launch_dc(dim3 grid, int NWv, hipStream_t stream, const uint16_t* act,
-                      int64_t a_stride, int I, const uint8_t* codes, const void* scl, int H,
-                      int E, const int32_t* ids, int topk, int P, const float* tw, uint16_t* y,
-                      int S, int W) {
+static void launch_dc(dim3 grid, int NWv, hipStream_t stream, const uint16_t* act, int a_stride,
+                      int I, const uint8_t* codes, const void* scl, int H, int E,
+                      const int32_t* ids, int topk, int P, const float* tw, uint16_t* y) {
   hipLaunchKernelGGL((gemv_down_combine_kernel<kMx, kR, kPPW>), grid, dim3(kWave * NWv), 0,
-                     stream, act, a_stride, I, codes, scl, H, E, ids, topk, P, tw, y, S, W, NWv);
+                     stream, ids, act, codes, scl, I, H, E, a_stride, topk, P, tw, y);
 }
 
 template <bool kMx>
@@ -447,6 +473,7 @@ static int launch_down_combine(const uint16_t* act, int32_t rows, int32_t I, int
   if (tw && !aligned4(tw)) return kInvalid;
   const int64_t P = (int64_t)rows * topk;
   if (P > kCombineMaxPairs || I > 32 * kWave || H >= (1 << 24)) return kNotSupported;
+  if (a_stride > INT32_MAX) return kNotSupported;
   int S, W, G, NT;
   segment_layout(I, S, W, G, NT);
   const int NWv = (int)std::min<int64_t>(P, kCombineMaxWaves);
@@ -457,14 +484,14 @@ static int launch_down_combine(const uint16_t* act, int32_t rows, int32_t I, int
   if (P * Rb > kCombineMaxYs) return kNotSupported;
   const dim3 grid((H + Rb - 1) / Rb);
   if (ppw == 1)
-    launch_dc<kMx, 2, 1>(grid, NWv, stream, act, a_stride, I, codes, scl, H, E, ids, topk,
-                         (int)P, tw, y, S, W);
+    launch_dc<kMx, 2, 1>(grid, NWv, stream, act, (int)a_stride, I, codes, scl, H, E, ids, topk,
+                         (int)P, tw, y);
   else if (ppw == 2)
-    launch_dc<kMx, 1, 2>(grid, NWv, stream, act, a_stride, I, codes, scl, H, E, ids, topk,
-                         (int)P, tw, y, S, W);
+    launch_dc<kMx, 1, 2>(grid, NWv, stream, act, (int)a_stride, I, codes, scl, H, E, ids, topk,
+                         (int)P, tw, y);
   else
-    launch_dc<kMx, 1, 4>(grid, NWv, stream, act, a_stride, I, codes, scl, H, E, ids, topk,
-                         (int)P, tw, y, S, W);
+    launch_dc<kMx, 1, 4>(grid, NWv, stream, act, (int)a_stride, I, codes, scl, H, E, ids, topk,
+                         (int)P, tw, y);
   return launch_status();
 }
 

@@ -139,7 +139,7 @@ int gq_mxfp4_decode(const uint8_t* blocks, const uint8_t* scales, int64_t n_rows
  * InvalidValue: null pointer (pair_scale may be NULL), rows < 1,
  *   topk < 1, E < 1, N < 1, K not a positive multiple of 64 (NF4) / 32
  *   (MXFP4), bad stride or alignment.
- * NotSupported: rows*topk > 256, K > 8192, N >= 2^24.
+ * NotSupported: rows*topk > 256, K > 8192, N >= 2^24, x_stride > 2^31 - 1.
  */
 int gq_nf4_grouped_gemv(const uint16_t* x, int32_t rows, int32_t K, int64_t x_stride,
                         const uint8_t* codes, const float* absmax, int32_t num_experts,
@@ -253,7 +253,8 @@ int gq_mxfp4_grouped_dgrad(const uint16_t* dy, int32_t P, int32_t N, int64_t dy_
  *   outside [0, E) contributes 0.
  *   InvalidValue: null pointer (topk_weights may be NULL), rows < 1,
  *     topk < 1, E < 1, H < 1, I not a positive multiple of 64, bad stride
- *     or alignment.  NotSupported: rows*topk > 64, I > 2048, H >= 2^24.
+ *     or alignment.  NotSupported: rows*topk > 64, I > 2048, H >= 2^24,
+ *     act_stride > 2^31 - 1.
  *
  * gq_moe_combine (prefill):
  *   y[t, :] = bf16( sum_s w[t, s] * y_pairs[t*topk + s, :] )

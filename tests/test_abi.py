@@ -100,6 +100,7 @@ def test_gemv_rejects(lib, fn):
     assert _gemv(lib, fn, x=F2) == INVALID
     assert _gemv(lib, fn, rows=8, topk=33) == NOT_SUPPORTED
     assert _gemv(lib, fn, K=16384, xs=16384) == NOT_SUPPORTED
+    assert _gemv(lib, fn, xs=1 << 31) == NOT_SUPPORTED            # 32-bit stride in the kernel
     if fn == "gq_nf4_grouped_gemv":
         assert _gemv(lib, fn, K=2080, xs=2080) == INVALID      # K % 64
 
@@ -207,6 +208,8 @@ def test_epilogue_entry_points_reject(lib):
                                                 None) == NOT_SUPPORTED
     assert lib.gq_nf4_grouped_gemv_down_combine(F, 1, 768, 768, F, F, 128, 2048, F, 8, F2, F,
                                                 None) == INVALID          # misaligned weights
+    assert lib.gq_nf4_grouped_gemv_down_combine(F, 1, 768, 1 << 31, F, F, 128, 2048, F, 8, NULL,
+                                                F, None) == NOT_SUPPORTED  # 32-bit stride
     # combine: H % 8, stride, rows == 0
     assert lib.gq_moe_combine(F, 4, 8, 2044, 2048, NULL, F, None) == INVALID
     assert lib.gq_moe_combine(F, 4, 8, 2048, 2040, NULL, F, None) == INVALID
