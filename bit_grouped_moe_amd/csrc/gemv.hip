@@ -76,9 +76,10 @@ __device__ __forceinline__ float segment_dot(const float* lut, u32x4 c, float am
 // summed with DPP lane moves; otherwise partial sums meet in LDS.  Both
 // orders are fixed, so results are reproducible.
 // Argument order: what the first loads need (routing ids, activations,
-// weights, sizes) comes first, in the 14 dwords that the build preloads into
-// SGPRs, so the expert-id load issues without waiting for a kernel-argument
-// load; the segment layout is derived from K rather than passed.
+// weights, sizes) comes first, in the first 14 dwords, which are preloaded
+// into SGPRs (every kernel here is compiled with kernel-argument preload),
+// so the expert-id load issues without waiting for a kernel-argument load;
+// the segment layout is derived from K rather than passed.
 template <bool kMx, int kIter, bool kWaveRows, bool kGlu>
 __global__ __launch_bounds__(kGemvMaxThreads) void grouped_gemv_kernel(
     const int32_t* __restrict__ ids, const uint16_t* __restrict__ x,

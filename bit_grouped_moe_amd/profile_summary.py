@@ -71,7 +71,7 @@ def trace(args):
             us = (int(r["End_Timestamp"]) - int(r["Start_Timestamp"])) / 1e3
             groups.setdefault((k, grid, r["Workgroup_Size_X"]), []).append(us)
     lines = ["# rocprofv3 kernel trace: " + args.title, "",
-             "Command (from the repository root on the GPU box):", "", "```", args.cmd, "```", "",
+             "Command (run from the repository root):", "", "```", args.cmd, "```", "",
              "| kernel | grid (threads) | block | calls | median us | mean us | min us | max us |",
              "|---|---|---|---|---|---|---|---|"]
     for (k, grid, wg), v in sorted(groups.items()):
@@ -125,7 +125,7 @@ def traffic(args):
         rows.append(f"| {key} | {kern} | {grid} | {f:.1f} | {w:.1f} | {fb:,.0f} | {wb:,.0f} |")
     json.dump(rec, open(args.json, "w"), indent=1)
     lines = ["# HBM traffic per launch from rocprofv3 counters: " + args.title, "",
-             "Commands (from the repository root on the GPU box):", "", "```", args.cmd, "```", "",
+             "Commands (run from the repository root):", "", "```", args.cmd, "```", "",
              f"Scale factors from the copy control ({args.control_bytes} bytes read and written "
              f"per launch): FETCH_SIZE x {fr:.4f}, WRITE_SIZE x {fw:.4f} "
              f"(raw KiB: fetch {cf:.1f}, write {cw:.1f}).", "",
