@@ -47,11 +47,12 @@ def test_tiny_gather(fmt, rows):
 
 
 @pytest.mark.parametrize("fmt", ["nf4", "mx"])
-@pytest.mark.parametrize("K", [64, 128, 256, 1024, 4096, 192, 96])
+@pytest.mark.parametrize("K", [64, 128, 256, 1024, 4096, 8192, 192, 96])
 def test_k_sweep(fmt, K):
     """Every in-wave reduction width (K/32 segments = 2 .. 64 lanes), the
-    cross-wave path (K = 4096), and segment counts that do not divide a wave
-    (K = 96, 192: several rows per thread in the cross-wave reduction)."""
+    cross-wave path (K = 4096, and K = 8192, the longest row the GEMV
+    takes), and segment counts that do not divide a wave (K = 96, 192:
+    several rows per thread in the cross-wave reduction)."""
     if fmt == "nf4" and K % 64:
         pytest.skip("NF4 needs K % 64 == 0")
     dev = device()
@@ -88,6 +89,28 @@ def test_shared_experts_dropped_and_flatten(fmt):
     out = _run(fmt, xp, bank, fl, dev)
     ref = oracle.grouped_gemm(xp, W, fl, E)
     assert_slices(bf16_to_host_f32(out), ref, fl, E)
+
+
+@pytest.mark.parametrize("fmt", ["nf4", "mx"])
+def test_most_pairs(fmt):
+    """The largest routing the GEMV takes: 256 pairs (32 tokens x top-8 in
+    gather mode, and the same 256 pairs flattened), experts repeated across
+    tokens, a ragged N."""
+    dev = device()
+    g = np.random.default_rng(11)
+    E, N, K = 40, 96 + 32, 256
+    bank = packed_nf4_bank(g, E, N, K) if fmt == "nf4" else packed_mx_bank(g, E, N, K)
+    W = LazyDecoded(fmt, *bank)
+    ids = wl.route_uniform(g, 32, E, 8)
+    x = wl.draw_bf16(g, (32, K))
+    say("gemv 256 pairs gather", fmt)
+    out = _run(fmt, x, bank, ids, dev)
+    assert_slices(bf16_to_host_f32(out), oracle.grouped_gemm(x, W, ids, E), ids, E)
+    fl = ids.reshape(-1, 1)
+    xp = wl.draw_bf16(g, (fl.shape[0], K))
+    say("gemv 256 pairs flatten", fmt)
+    out = _run(fmt, xp, bank, fl, dev)
+    assert_slices(bf16_to_host_f32(out), oracle.grouped_gemm(xp, W, fl, E), fl, E)
 
 
 @pytest.mark.parametrize("fmt", ["nf4", "mx"])
