@@ -3,11 +3,18 @@
     python -m bit_grouped_moe_amd.profile_summary trace DIR --cmd "..." --out FILE.md
     python -m bit_grouped_moe_amd.profile_summary traffic FETCH_DIR WRITE_DIR \
         --control-bytes B --cmd "..." --out FILE.md --json profiles/traffic_counters.json
+    python -m bit_grouped_moe_amd.profile_summary counters DIR [DIR ...] --cmd "..." --out FILE.md
 
 ``trace`` reads the kernel trace (``*_kernel_trace.csv``) of a
 ``rocprofv3 --kernel-trace --stats --output-format csv`` run and tabulates
 every libgq / probe kernel per launch shape (grid size in threads): calls,
 median, mean, min and max device time.
+
+``counters`` reads one or more ``rocprofv3 --pmc <SQ counters>`` runs of
+``bench.py`` and tabulates, for the decode gate_up GEMV and the prefill
+gate_up GEMM launches of the Qwen3 workload, the median per dispatch of
+every counter collected, plus ratios formed from counters of the same
+dispatch (no normalisation by unit counts or clocks).
 
 ``traffic`` reads two ``rocprofv3 --pmc FETCH_SIZE`` / ``--pmc WRITE_SIZE``
 runs of ``bench.py``.  The counters report KiB per dispatch; the factor that
@@ -134,6 +141,55 @@ def traffic(args):
     open(args.out, "w").write("\n".join(lines) + "\n")
 
 
+_RATIOS = (
+    ("VALU instructions per MFMA instruction", "SQ_INSTS_VALU", "SQ_INSTS_MFMA"),
+    ("LDS instructions per MFMA instruction", "SQ_INSTS_LDS", "SQ_INSTS_MFMA"),
+    ("LDS bank-conflict cycles per LDS instruction", "SQ_LDS_BANK_CONFLICT", "SQ_INSTS_LDS"),
+    ("cycles waves wait on LDS / wave cycles", "SQ_WAIT_INST_LDS", "SQ_WAVE_CYCLES"),
+    ("cycles waves wait on anything / wave cycles", "SQ_WAIT_ANY", "SQ_WAVE_CYCLES"),
+    ("VALU+MFMA co-issue cycles / MFMA busy cycles", "SQ_VALU_MFMA_COEXEC_CYCLES",
+     "SQ_VALU_MFMA_BUSY_CYCLES"),
+)
+
+
+def counters(args):
+    per = {}                                                 # (record, counter) -> [values]
+    for d in args.dirs:
+        for f in glob.glob(os.path.join(d, "**", "*_counter_collection.csv"), recursive=True):
+            disp = {}
+            for r in csv.DictReader(open(f)):
+                k = _short(r["Kernel_Name"])
+                if not k:
+                    continue
+                key = (k, int(r["Grid_Size"]), int(r["Dispatch_Id"]), r["Counter_Name"])
+                disp[key] = disp.get(key, 0.0) + float(r["Counter_Value"])
+            for (k, grid, _, cname), v in disp.items():
+                for rec, (kern, kgrid) in (("gemv_nf4_gate_up_m1", GATE_UP_GEMV),
+                                           ("gemm_nf4_gate_up_prefill", GATE_UP_GEMM)):
+                    if k.startswith(kern) and grid == kgrid:
+                        per.setdefault((rec, cname), []).append(v)
+    recs = ("gemv_nf4_gate_up_m1", "gemm_nf4_gate_up_prefill")
+    names = sorted({c for (_, c) in per})
+    med = {key: statistics.median(v) for key, v in per.items()}
+    lines = ["# SQ counters per launch from rocprofv3: " + args.title, "",
+             "Commands (run from the repository root):", "", "```", args.cmd, "```", "",
+             "Median over the launches of each kernel (counter values summed over the "
+             "device for one dispatch).", "",
+             "| counter | " + " | ".join(recs) + " |", "|---|" + "---|" * len(recs)]
+    for c in names:
+        lines.append(f"| {c} | " + " | ".join(
+            f"{med[(r, c)]:,.0f}" if (r, c) in med else "-" for r in recs) + " |")
+    lines += ["", "| ratio (same dispatch, medians) | " + " | ".join(recs) + " |",
+              "|---|" + "---|" * len(recs)]
+    for label, num, den in _RATIOS:
+        vals = []
+        for r in recs:
+            a, b = med.get((r, num)), med.get((r, den))
+            vals.append(f"{a / b:.3f}" if a is not None and b else "-")
+        lines.append(f"| {label} | " + " | ".join(vals) + " |")
+    open(args.out, "w").write("\n".join(lines) + "\n")
+
+
 def main():
     ap = argparse.ArgumentParser()
     sub = ap.add_subparsers(dest="mode", required=True)
@@ -150,8 +206,13 @@ def main():
     c.add_argument("--title", default="bench.py")
     c.add_argument("--out", required=True)
     c.add_argument("--json", required=True)
+    k = sub.add_parser("counters")
+    k.add_argument("dirs", nargs="+")
+    k.add_argument("--cmd", required=True)
+    k.add_argument("--title", default="bench.py")
+    k.add_argument("--out", required=True)
     args = ap.parse_args()
-    trace(args) if args.mode == "trace" else traffic(args)
+    {"trace": trace, "traffic": traffic, "counters": counters}[args.mode](args)
 
 
 if __name__ == "__main__":
