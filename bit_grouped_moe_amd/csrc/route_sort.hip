@@ -12,9 +12,10 @@
 //      segment start and tile base,
 //   3. compacts its pairs in ascending pair order: wave w owns a contiguous
 //      range of 2048 ids, lane l takes ids range + 64j + l (conflict-free LDS
-//      reads), and a pair's place is the workgroup's cursor + the earlier
-//      waves' counts + the wave's running count + its rank among the
-//      matching lanes (ballot bit count), and
+//      reads) and the wave keeps the 32 match ballots in scalar registers;
+//      a pair's place is the workgroup's cursor + the earlier waves' counts
+//      + the wave's running count + its rank among the matching lanes
+//      (ballot bit count), and
 //   4. writes its offsets entry and its tiles.
 // No global atomics, no workspace; the result is the unique stable order.
 #include "gq_device.hpp"
@@ -98,12 +99,14 @@ __global__ __launch_bounds__(kSortThreads) void route_sort_kernel(
       __syncthreads();
     }
     const int wbase = wave * (kChunkIds / kSortWaves);     // the wave's 2048 ids
+    uint64_t bal[kPerLane];                                // the wave's matches, kept for pass 2
     int mine = 0;
-#pragma unroll 8
+#pragma unroll
     for (int j = 0; j < kPerLane; ++j) {
       const int v = s_ids[wbase + j * kWave + lane];
       const bool hit = (b < E) ? (v == b) : (v != kPastEnd && (unsigned)v >= uE);
-      mine += __popcll(__ballot(hit));
+      bal[j] = __ballot(hit);
+      mine += __popcll(bal[j]);
     }
     if (lane == 0) wcount[wave] = mine;
     __syncthreads();
@@ -116,15 +119,12 @@ __global__ __launch_bounds__(kSortThreads) void route_sort_kernel(
     }
     int pos = cursor + before;
     const int64_t pbase = (int64_t)ch * kChunkIds + wbase;
-#pragma unroll 8
+#pragma unroll
     for (int j = 0; j < kPerLane; ++j) {
-      const int v = s_ids[wbase + j * kWave + lane];
-      const bool hit = (b < E) ? (v == b) : (v != kPastEnd && (unsigned)v >= uE);
-      const uint64_t bal = __ballot(hit);
-      if (hit)
-        sorted_pairs[pos + __popcll(bal & ((1ull << lane) - 1ull))] =
-            (int)(pbase + j * kWave + lane);
-      pos += __popcll(bal);
+      const uint64_t m = bal[j];
+      if ((m >> lane) & 1ull)
+        sorted_pairs[pos + __popcll(m & ((1ull << lane) - 1ull))] = (int)(pbase + j * kWave + lane);
+      pos += __popcll(m);
     }
     cursor += total;
     __syncthreads();                                       // wcount reused
