@@ -202,7 +202,29 @@ __global__ __launch_bounds__(kGemvMaxThreads) void grouped_gemv_kernel(
         red[i * kStride + tid] = active ? segment_dot<kMx>(lut, cw[i], am[i], sb[i], xf) : 0.f;
       lds_barrier();
       vals[0] = 0.f;
-      if (tid < R) {                                           // R <= NT (host check)
+      if (8 * R <= NT) {
+        // eight threads per row (segments part, part + 8, ...), then an
+        // 8-lane DPP sum; the total goes through LDS to thread r
+        const int rr = tid >> 3, part = tid & 7;
+        float v = 0.f;
+        if (rr < R) {
+          const int gg = rr % G, ii = rr / G;                  // weight row wrow(gg, ii)
+          const float* src = red + ii * kStride + gg * S;
+          float s0 = 0.f, s1 = 0.f;
+          int j = part;
+          for (; j + 8 < S; j += 16) {
+            s0 += src[j];
+            s1 += src[j + 8];
+          }
+          if (j < S) s0 += src[j];
+          v = s0 + s1;
+        }
+        v = group_sum_last(v, 8);                              // on the lane with part == 7
+        lds_barrier();                                         // every partial read
+        if (rr < R && part == 7) red[rr] = v;
+        lds_barrier();
+        if (tid < R) vals[0] = red[tid];
+      } else if (tid < R) {                                    // R <= NT (host check)
         const int gg = tid % G, ii = tid / G;                  // weight row wrow(gg, ii)
         const float* src = red + ii * kStride + gg * S;
         float s0 = 0.f, s1 = 0.f, s2 = 0.f, s3 = 0.f;          // fixed order, 4 chains
