@@ -74,6 +74,27 @@ def test_ragged_multi_tile(fmt, N, K):
     assert_slices(bf16_to_host_f32(out), ref, ids, E)
 
 
+@pytest.mark.parametrize("fmt,K", [("nf4", 768), ("mx", 544), ("nf4", 1088), ("mx", 1056)])
+def test_tile_boundaries(fmt, K):
+    """Expert segments on and next to the 256-row tile edges, in flatten mode
+    (one row per pair): 512 rows (two full tiles), 256, 257 (a one-row
+    tail tile), 1, 255, an empty expert, and dropped pairs scattered among
+    them; both forward kernels (K < 1024 and K >= 1024)."""
+    dev = device()
+    g = np.random.default_rng(K + 17)
+    E, N = 7, 192
+    sizes = [512, 256, 257, 1, 0, 255, 0]
+    ids = np.concatenate([np.full(n, e, dtype=np.int32) for e, n in enumerate(sizes)]
+                         + [np.full(9, -1, dtype=np.int32)])
+    ids = g.permutation(ids).reshape(-1, 1)
+    bank = packed_nf4_bank(g, E, N, K) if fmt == "nf4" else packed_mx_bank(g, E, N, K)
+    W = LazyDecoded(fmt, *bank)
+    x = wl.draw_bf16(g, (ids.shape[0], K))
+    say("gemm tile boundaries", fmt, K)
+    out = _gemm(fmt, x, to_dev(bank[0], dev), to_dev(bank[1], dev), ids, E, dev)
+    assert_slices(bf16_to_host_f32(out), oracle.grouped_gemm(x, W, ids, E), ids, E)
+
+
 @pytest.mark.parametrize("fmt,K", [("nf4", 256), ("mx", 256), ("nf4", 1088), ("mx", 1056)])
 def test_one_hot_probe_is_bit_exact(fmt, K):
     """A one-hot activation row picks one weight column: the output is the
