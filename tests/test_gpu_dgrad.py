@@ -43,6 +43,24 @@ def test_small_and_ragged(E, N, K, P):
     assert_slices(bf16_to_host_f32(out), ref, pe, E)
 
 
+def test_tile_boundaries():
+    """Expert segments on and next to the 256-row tile edges (512, 256, 257,
+    255 and 1 pairs), an empty expert and dropped pairs."""
+    dev = device()
+    g = np.random.default_rng(23)
+    E, N, K = 7, 192, 320
+    sizes = [512, 256, 257, 1, 0, 255, 0]
+    pe = np.concatenate([np.full(n, e, dtype=np.int32) for e, n in enumerate(sizes)]
+                        + [np.full(9, -1, dtype=np.int32)])
+    pe = g.permutation(pe)
+    codes, absmax = packed_nf4_bank(g, E, N, K)
+    W = LazyDecoded("nf4", codes, absmax)
+    dy = wl.draw_bf16(g, (pe.shape[0], N))
+    say("dgrad tile boundaries")
+    out = _dgrad(dy, to_dev(codes, dev), to_dev(absmax, dev), pe, E, dev)
+    assert_slices(bf16_to_host_f32(out), oracle.grouped_dgrad(dy, W, pe, E), pe, E)
+
+
 @pytest.mark.parametrize("N,K", [(128, 256), (1024, 320)])
 def test_one_hot_probe_is_bit_exact(N, K):
     """dY = e_n makes dX row p the decoded weight row W[n, :] rounded once
