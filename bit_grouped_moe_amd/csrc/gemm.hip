@@ -385,31 +385,35 @@ __device__ __forceinline__ void grouped_gemm_body(const GemmArgs& g) {
   // them into its own LDS area with the chunk slot XOR-swizzled by
   // (row >> 1) & 7 and reads MFMA fragments (row lr, chunk lh*4 + sl) back;
   // both directions are free of bank conflicts, and no other wave touches the
-  // area, so no barrier.  Loads are unconditional (rows of inactive sub-tiles
-  // are valid rows; chunks past a K tail re-read the last valid chunk and are
-  // zeroed when read), see the note at fwd_load.
+  // area, so no barrier.  Loads are unconditional within a wave's loop
+  // variant (chunks past a K tail re-read the last valid chunk and are zeroed
+  // when read), see the note at fwd_load; a wave loads the rows of sub-tile
+  // ms1 only in the variants where ms1 is active (kNa = 8 loads) and none in
+  // the variant for a wave without active rows.
   uint16_t* aw = &Aw[kDg ? 0 : wave][0];
-  // The lane's 8 row offsets are re-read from LDS at every step (registers
+  // The lane's row offsets are re-read from LDS at every step (registers
   // are short); element offsets fit 32 bits (host check).
-  auto load_a = [&](int ks, u32x4 (&Ar)[8]) {
+  auto load_a = [&](auto na_c, int ks, u32x4 (&Ar)[8]) {
+    constexpr int kNa = decltype(na_c)::value;
     const int k = min(ks * kTK + (lane & 7) * 8, g.Kc - 8);
 #pragma unroll
-    for (int i = 0; i < 8; ++i) {
+    for (int i = 0; i < kNa; ++i) {
       const int off = row_s[(i < 4 ? ms0 : ms1) * 32 + (i & 3) * 8 + (lane >> 3)] * (int)g.x_stride;
       Ar[i] = *reinterpret_cast<const u32x4*>(g.x + off + k);
     }
   };
-  auto stage_a = [&](const u32x4 (&Ar)[8]) {
+  auto stage_a = [&](auto na_c, const u32x4 (&Ar)[8]) {
+    constexpr int kNa = decltype(na_c)::value;
 #pragma unroll
-    for (int i = 0; i < 8; ++i) {
+    for (int i = 0; i < kNa; ++i) {
       const int r = (i >> 2) * 32 + (i & 3) * 8 + (lane >> 3);
       const int slot = (lane & 7) ^ ((r >> 1) & 7);
       *reinterpret_cast<u32x4*>(aw + r * kTK + slot * 8) = Ar[i];
     }
   };
-  auto read_a = [&](int sl, u32x4 (&a)[2], bool zero_hi) {
+  auto read_a = [&](int nj, int sl, u32x4 (&a)[2], bool zero_hi) {
 #pragma unroll
-    for (int j = 0; j < 2; ++j) {
+    for (int j = 0; j < nj; ++j) {
       const int r = j * 32 + lr;
       const int slot = (lh * 4 + sl) ^ ((r >> 1) & 7);
       a[j] = *reinterpret_cast<const u32x4*>(aw + r * kTK + slot * 8);
@@ -424,10 +428,11 @@ __device__ __forceinline__ void grouped_gemm_body(const GemmArgs& g) {
   // ahead.  Rows are the pairs; the contraction (N) is a multiple of 64.
   const uint16_t* ad0 = g.x + (int64_t)row_s[ms0 * 32 + lr] * g.x_stride + lh * 32;
   const uint16_t* ad1 = g.x + (int64_t)row_s[ms1 * 32 + lr] * g.x_stride + lh * 32;
-  auto load_a_direct = [&](int ks, int sl, u32x4 (&Ad)[2][4]) {
+  auto load_a_direct = [&](auto na_c, int ks, int sl, u32x4 (&Ad)[2][4]) {
+    constexpr int kNa = decltype(na_c)::value;             // 8: both sub-tiles, 4: ms0 only
     const int koff = ks * kTK;
     Ad[0][sl] = *reinterpret_cast<const u32x4*>(ad0 + koff + sl * 8);
-    Ad[1][sl] = *reinterpret_cast<const u32x4*>(ad1 + koff + sl * 8);
+    if constexpr (kNa == 8) Ad[1][sl] = *reinterpret_cast<const u32x4*>(ad1 + koff + sl * 8);
   };
   auto load_b_slice = [&](const uint16_t* B, int sl, bf16x8 (&b)[4]) {
 #pragma unroll
@@ -437,6 +442,7 @@ __device__ __forceinline__ void grouped_gemm_body(const GemmArgs& g) {
   };
   // kRows = number of active 32-row sub-tiles of this wave (1 or 2) with all
   // 128 columns valid: unguarded MFMAs.  kRows == 0: generic guarded path.
+  // kRows == -1 (no active sub-tile): the wave only decodes its share of B.
   auto mfma_slice = [&](auto rows_c, const u32x4 (&a)[2], const bf16x8 (&b)[4]) {
     constexpr int kRows = decltype(rows_c)::value;
 #pragma unroll
@@ -467,16 +473,31 @@ __device__ __forceinline__ void grouped_gemm_body(const GemmArgs& g) {
   DgLoad D{};
   DgCodes R{};
 
+  // Loop variant of the wave (uniform): rows of activations it loads per
+  // step (8 loads: both sub-tiles, 4: sub-tile ms0, 0: none).
+  using I2 = std::integral_constant<int, 2>;
+  using I1 = std::integral_constant<int, 1>;
+  using I0 = std::integral_constant<int, 0>;
+  using Im = std::integral_constant<int, -1>;
+  const int variant = !act0 ? -1 : (ncols == kTN ? (act1 ? 2 : 1) : 0);
+  const int na = variant == -1 ? 0 : (variant == 1 ? 4 : 8);
+
   // ---- prologue: step 0 decoded into Bs[0] and staged in Aw; step 1's
   // activations and codes in flight ----
-  if constexpr (kDg) {
+  auto prologue_a = [&](auto na_c) {
+    if constexpr (decltype(na_c)::value > 0) {
+      if constexpr (kDg) {
 #pragma unroll
-    for (int sl = 0; sl < 4; ++sl) load_a_direct(0, sl, Ad);
-  } else {
-    load_a(0, Ar);
-    stage_a(Ar);
-    load_a(min(1, nsteps - 1), Ar);
-  }
+        for (int sl = 0; sl < 4; ++sl) load_a_direct(na_c, 0, sl, Ad);
+      } else {
+        load_a(na_c, 0, Ar);
+        stage_a(na_c, Ar);
+        load_a(na_c, min(1, nsteps - 1), Ar);
+      }
+    }
+  };
+  if (na == 8) prologue_a(std::integral_constant<int, 8>{});
+  else if (na == 4) prologue_a(std::integral_constant<int, 4>{});
   if constexpr (kDg) {
     D = dg_load<kMode>(g, e, n0, 0, tid);
     dg_stage<kMode>(D, Cs[0], As[0], tid);
@@ -503,6 +524,9 @@ __device__ __forceinline__ void grouped_gemm_body(const GemmArgs& g) {
   // step): loads under a branch make the compiler wait for them early.
   // Unrolled by two so the two code register sets swap roles without copies. ----
   auto run_loop = [&](auto rows_c) {
+    constexpr int kRows = decltype(rows_c)::value;
+    constexpr int kNa = kRows < 0 ? 0 : (kRows == 1 ? 4 : 8);
+    using NaC = std::integral_constant<int, kNa>;
     auto step = [&](int ks, FwdLoad& F_dec, FwdLoad& F_fill) {
       const uint16_t* B = Bs[ks & 1];
       uint16_t* Bn = Bs[(ks + 1) & 1];
@@ -514,13 +538,16 @@ __device__ __forceinline__ void grouped_gemm_body(const GemmArgs& g) {
       bf16x8 b0[4], b1[4];
       auto slice = [&](int sl, const bf16x8 (&bc)[4], bf16x8 (&bn)[4]) {
         u32x4 ac[2];
-        if constexpr (kDg) {
-          ac[0] = Ad[0][sl];
-          ac[1] = Ad[1][sl];
-        } else {
-          read_a(sl, ac, zero_hi);
+        if constexpr (kRows >= 0) {
+          constexpr int kNj = kRows == 1 ? 1 : 2;          // sub-tiles with operands
+          if constexpr (kDg) {
+            ac[0] = Ad[0][sl];
+            if constexpr (kNj == 2) ac[1] = Ad[1][sl];
+          } else {
+            read_a(kNj, sl, ac, zero_hi);
+          }
+          if (sl < 3) load_b_slice(B, sl + 1, bn);
         }
-        if (sl < 3) load_b_slice(B, sl + 1, bn);
         if constexpr (kDg) {
           if (sl == 0) dg_read_codes<kMode>(Cs[(ks + 1) & 1], As[(ks + 1) & 1], tid, R);
           dg_decode_chunk<kMode>(R, As[(ks + 1) & 1], sl, lut, Bn, tid);
@@ -531,17 +558,17 @@ __device__ __forceinline__ void grouped_gemm_body(const GemmArgs& g) {
         } else {
           fwd_decode_chunk<kMode>(F_dec, sl, lut, Bn, tid);
         }
-        mfma_slice(rows_c, ac, bc);
-        if constexpr (kDg) load_a_direct(min(ks + 1, nsteps - 1), sl, Ad);
+        if constexpr (kRows >= 0) mfma_slice(rows_c, ac, bc);
+        if constexpr (kDg && kNa > 0) load_a_direct(NaC{}, min(ks + 1, nsteps - 1), sl, Ad);
       };
-      load_b_slice(B, 0, b0);
+      if constexpr (kRows >= 0) load_b_slice(B, 0, b0);
       slice(0, b0, b1);
       slice(1, b1, b0);
       slice(2, b0, b1);
       slice(3, b1, b0);
-      if constexpr (!kDg) {
-        stage_a(Ar);                                     // step ks+1 (own area: no barrier)
-        load_a(min(ks + 2, nsteps - 1), Ar);
+      if constexpr (!kDg && kNa > 0) {
+        stage_a(NaC{}, Ar);                              // step ks+1 (own area: no barrier)
+        load_a(NaC{}, min(ks + 2, nsteps - 1), Ar);
       }
       lds_barrier();
     };
@@ -550,9 +577,10 @@ __device__ __forceinline__ void grouped_gemm_body(const GemmArgs& g) {
       if (ks + 1 < nsteps) step(ks + 1, F0, F1);
     }
   };
-  if (ncols == kTN && act1) run_loop(std::integral_constant<int, 2>{});
-  else if (ncols == kTN && act0) run_loop(std::integral_constant<int, 1>{});
-  else run_loop(std::integral_constant<int, 0>{});
+  if (variant == 2) run_loop(I2{});
+  else if (variant == 1) run_loop(I1{});
+  else if (variant == 0) run_loop(I0{});
+  else run_loop(Im{});
 
   // ---- epilogue: one output row per lane, written from registers ----
   store_rows_t<kGlu, kTNo>(acc, act0, act1, ms0, ms1, valid, pair_s, g, n0, lr, lh);
@@ -850,7 +878,8 @@ __global__ __launch_bounds__(kGemmThreads, 1) void grouped_gemm_fwd_kernel(GemmA
   lds_barrier();
 
   auto run_loop = [&](auto rows_c) {
-    constexpr int kRows = decltype(rows_c)::value;         // -1: guarded generic path
+    // -1: guarded generic path; 0: no active sub-tile (the wave only decodes)
+    constexpr int kRows = decltype(rows_c)::value;
     auto step = [&](int ks, const uint16_t* Ac, uint16_t* An, const uint16_t* Bc, uint16_t* Bn,
                     XLoad& Ldec, XLoad& Lfill) {
       dma_a(min(ks + 1, nsteps - 1), An);
@@ -863,8 +892,10 @@ __global__ __launch_bounds__(kGemmThreads, 1) void grouped_gemm_fwd_kernel(GemmA
         for (int i = 0; i < 4; ++i) {
           if (kRows >= 0 ? i < kRows : true) a[i] = read_a(Ac, i, sl);
         }
+        if constexpr (kRows != 0) {
 #pragma unroll
-        for (int c = 0; c < 4; ++c) b[c] = read_b(Bc, c, sl);
+          for (int c = 0; c < 4; ++c) b[c] = read_b(Bc, c, sl);
+        }
       };
       auto mfmas = [&](const u32x4 (&a)[4], const bf16x8 (&b)[4]) {
 #pragma unroll
@@ -918,6 +949,7 @@ __global__ __launch_bounds__(kGemmThreads, 1) void grouped_gemm_fwd_kernel(GemmA
   else if (allcols && nrows == 3) run_loop(std::integral_constant<int, 3>{});
   else if (allcols && nrows == 2) run_loop(std::integral_constant<int, 2>{});
   else if (allcols && nrows == 1) run_loop(std::integral_constant<int, 1>{});
+  else if (nrows == 0) run_loop(std::integral_constant<int, 0>{});
   else run_loop(std::integral_constant<int, -1>{});
 
   // ---- epilogue: one output row per lane (see store_block_t) ----
