@@ -20,7 +20,9 @@
 //    prologue and epilogue overlap the other's matrix work.
 // In both, the B tile (weights x 64 K) is decoded ONCE per workgroup from
 // packed codes into bf16 in LDS (double-buffered, one barrier per step) and
-// shared by the waves; the K order inside a step is permuted identically
+// shared by the waves -- except on tiles of at most 128 rows in the first
+// kernel, where each wave owns 64 columns for all rows and decodes them
+// straight into MFMA operand registers; the K order inside a step is permuted identically
 // for A and B (lane half h takes k in [32h, 32h+32)), so every operand load
 // is a contiguous 16-byte piece; the weights are the first MFMA operand, so
 // a lane accumulates one output row and the epilogue writes rows from
@@ -730,6 +732,242 @@ __device__ __forceinline__ void sched_slice() {
   sched_slice_seq<kM, kDs, kValu, kDsw>(std::make_integer_sequence<int, kM>{});
 }
 
+// ---- narrow tiles (at most 128 rows) of the 256-column kernel ----
+// Under skewed routing most experts end in a partial tile, and a tile of few
+// rows spends its steps decoding B and moving it through LDS rather than in
+// the matrix cores.  Such tiles use another wave layout: wave w owns the B
+// columns 64 w + [0, 64) for ALL of the tile's (at most four) 32-row
+// sub-tiles, so each B column feeds exactly one wave, which decodes it
+// straight into MFMA operand registers -- no B tile in LDS, no B fragment
+// reads.  Lane (lr, lh) of column block cb holds column 64 w + 32 cb + lr
+// (SwiGLU: block 0 is gate row j = 32 w + lr of the tile's outputs, block 1
+// the matching up row) and, in slice sl, k = 32 lh + 8 sl + [0, 8): the K
+// order of the A fragments, so the lane's operand for the whole step is the
+// 16 code bytes at byte 16 lh of the column's 32-byte step chunk (one NF4
+// absmax block / one MXFP4 scale block per lane half).  The activation tile
+// (<= 128 rows) is still loaded straight into LDS, double-buffered, one
+// barrier per step.
+constexpr int kNarrowRows = 128;
+
+struct NLoad {
+  u32x4 c[2];      // 32 codes of column blocks 0 and 1
+  float a[2];      // NF4 absmax
+  uint32_t s[2];   // MXFP4 scale bytes
+};
+
+template <int kMode>
+__device__ __forceinline__ NLoad n_load(const GemmArgs& g, int e, int jcol, int ks, int half) {
+  NLoad L;
+  const int k0 = ks * kTK;
+#pragma unroll
+  for (int cb = 0; cb < 2; ++cb) {
+    int n;
+    if constexpr (kMode == kFwdNF4Glu) n = min(jcol, g.Nout - 1) + (cb ? g.Nout : 0);
+    else n = min(jcol + 32 * cb, g.Nw - 1);
+    const size_t row = (size_t)e * g.Nw + n;
+    L.c[cb] = *reinterpret_cast<const u32x4*>(g.codes + row * (size_t)(g.Kw / 2) + k0 / 2 +
+                                              16 * half);
+    if constexpr (kMode == kFwdMX) {
+      L.s[cb] = static_cast<const uint8_t*>(g.scl)[row * (size_t)(g.Kw / 32) + k0 / 32 + half];
+      L.a[cb] = 0.f;
+    } else {
+      L.a[cb] = static_cast<const float*>(g.scl)[row * (size_t)(g.Kw / 64) + ks];
+      L.s[cb] = 0u;
+    }
+  }
+  return L;
+}
+
+template <int kMode>
+__device__ __forceinline__ void fwd_narrow(const GemmArgs& g, int e, int n0, int start, int valid,
+                                           int tid, uint16_t* A0, uint16_t* A1, f32x2* lut2,
+                                           int* pair_s, int* row_s, float* scale_s) {
+  constexpr bool kGlu = kMode == kFwdNF4Glu;
+  constexpr bool kMx = kMode == kFwdMX;
+  const int nsteps = (g.Kc + kTK - 1) / kTK;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6), lane = tid & 63;
+  const int lr = lane & 31, lh = lane >> 5;
+  const bool ktail = kMx && (g.Kc % kTK) != 0;             // MXFP4: last step half full
+  // this lane's column (SwiGLU: its output column) and whether it exists
+  const int jcol = kGlu ? n0 + 32 * wave + lr : n0 + 64 * wave + lr;
+  bool cok[2];
+#pragma unroll
+  for (int cb = 0; cb < 2; ++cb) cok[cb] = kGlu ? jcol < g.Nout : jcol + 32 * cb < g.Nw;
+  // K tail: lane half 1 has no weights in the last step; it re-reads half 0
+  // (in bounds) and decodes with a zero factor.
+  auto load = [&](int ks) {
+    const bool full = ks * kTK + kTK <= g.Kw;
+    return n_load<kMode>(g, e, jcol, ks, full ? lh : 0);
+  };
+  NLoad X = load(0);
+  NLoad Y = load(min(1, nsteps - 1));
+  {
+    int p = g.sorted_pairs[start + min(tid, valid - 1)];
+    p = ((unsigned)p < (unsigned)g.P) ? p : 0;
+    pair_s[tid] = p;
+    row_s[tid] = p / g.topk;
+    scale_s[tid] = g.pair_scale ? g.pair_scale[p] : 1.f;
+  }
+  if constexpr (!kMx) nf4_pairs_init(lut2, tid);
+  lds_barrier();
+
+  // LDS-direct activation loads: instruction j of wave w fills rows
+  // 32 w + 8 j + [0, 8) (same slot swizzle as the 256-row tiles).
+  uint32_t voff[4];
+  uint32_t tailbits = 0;
+#pragma unroll
+  for (int j = 0; j < 4; ++j) {
+    const int R = 32 * wave + 8 * j + (lane >> 3);
+    const int c = (lane & 7) ^ ((R >> 1) & 7);
+    voff[j] = (uint32_t)row_s[R] * (uint32_t)(g.x_stride * 2) + 16u * (uint32_t)c;
+    tailbits |= (c >= 4 ? 1u : 0u) << j;
+  }
+  auto dma_a = [&](int ks, uint16_t* Adst) {
+    const char* xb = reinterpret_cast<const char*>(g.x) + (size_t)ks * (kTK * 2);
+    const bool tail = ktail && ks == nsteps - 1;
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      if (32 * wave + 8 * j < valid) {
+        uint16_t* dst = Adst + (32 * wave + 8 * j) * kTK;
+        if (kMx && tail && ((tailbits >> j) & 1u)) {
+          *reinterpret_cast<u32x4*>(dst + lane * 8) = u32x4{0u, 0u, 0u, 0u};
+        } else {
+          __builtin_amdgcn_global_load_lds((glb_void_t*)(xb + voff[j]), (lds_void_t*)dst, 16, 0,
+                                           0);
+        }
+      }
+    }
+  };
+  const int aslot_x = (lr >> 1) & 7;
+  auto read_a = [&](const uint16_t* A, int i, int sl) -> u32x4 {
+    const int R = 32 * i + lr;
+    return *reinterpret_cast<const u32x4*>(A + R * kTK + (((lh * 4 + sl) ^ aslot_x) * 8));
+  };
+  // B operand of slice sl, column block cb, for the step whose codes are L
+  auto decode = [&](const NLoad& L, int ks, int cb, int sl) -> bf16x8 {
+    const uint32_t cw = L.c[cb][sl];
+    uint32_t w[4];
+    if constexpr (kMx) {
+      const bool live = cok[cb] && (!(ktail && ks == nsteps - 1) || lh == 0);
+      const float f = live ? e8m0_to_f32(L.s[cb]) : 0.f;
+#pragma unroll
+      for (int b = 0; b < 4; ++b) w[b] = e2m1_pair_bf16_scaled(cw, b, f);
+    } else {
+      float q[8];
+      nf4_pairs8(lut2, cw, q);
+      const float a = cok[cb] ? L.a[cb] : 0.f;
+#pragma unroll
+      for (int b = 0; b < 4; ++b) w[b] = pack_bf16x2(q[2 * b] * a, q[2 * b + 1] * a);
+    }
+    return as_bf16x8(u32x4{w[0], w[1], w[2], w[3]});
+  };
+
+  f32x16 acc[4][2];
+#pragma unroll
+  for (int i = 0; i < 4; ++i)
+#pragma unroll
+    for (int c = 0; c < 2; ++c)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) acc[i][c][r] = 0.f;
+  const int nrows = (valid + 31) / 32;                     // active sub-tiles (all waves)
+  // A column block (32 columns from a multiple of 32; the matrix width is a
+  // multiple of 32) is valid for all lanes or for none: wave-uniform flags.
+  const bool allcols = __builtin_amdgcn_readfirstlane((cok[0] && cok[1]) ? 1 : 0) != 0;
+  const bool anycol = __builtin_amdgcn_readfirstlane((cok[0] || cok[1]) ? 1 : 0) != 0;
+
+  // ---- prologue: step 0's activations staged, its B decoded; step 1's
+  // codes in flight ----
+  bf16x8 B0[2][4], B1[2][4];
+  dma_a(0, A0);
+#pragma unroll
+  for (int sl = 0; sl < 4; ++sl)
+#pragma unroll
+    for (int cb = 0; cb < 2; ++cb) B0[cb][sl] = decode(X, 0, cb, sl);
+  __builtin_amdgcn_s_waitcnt(0);
+  lds_barrier();
+
+  auto run_loop = [&](auto rows_c) {
+    constexpr int kRows = decltype(rows_c)::value;         // -1: guarded generic path
+    auto step = [&](int ks, const uint16_t* Ac, uint16_t* An, const bf16x8 (&Bc)[2][4],
+                    bf16x8 (&Bn)[2][4], const NLoad& Ldec, NLoad& Lfill) {
+      dma_a(min(ks + 1, nsteps - 1), An);
+      Lfill = load(min(ks + 2, nsteps - 1));
+      __builtin_amdgcn_sched_barrier(0);                   // keep the loads at the step start
+      u32x4 fa[2][4];
+      auto frags = [&](int sl, u32x4 (&a)[4]) {
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          if (kRows >= 0 ? i < kRows : true) a[i] = read_a(Ac, i, sl);
+        }
+      };
+      frags(0, fa[0]);
+#pragma unroll
+      for (int sl = 0; sl < 4; ++sl) {
+        if (sl < 3) frags(sl + 1, fa[(sl + 1) & 1]);
+#pragma unroll
+        for (int cb = 0; cb < 2; ++cb) Bn[cb][sl] = decode(Ldec, min(ks + 1, nsteps - 1), cb, sl);
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+#pragma unroll
+          for (int cb = 0; cb < 2; ++cb) {
+            if constexpr (kRows >= 0) {
+              if (i < kRows)
+                acc[i][cb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(
+                    Bc[cb][sl], as_bf16x8(fa[sl & 1][i]), acc[i][cb], 0, 0, 0);
+            } else {
+              if (i < nrows && anycol)
+                acc[i][cb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(
+                    Bc[cb][sl], as_bf16x8(fa[sl & 1][i]), acc[i][cb], 0, 0, 0);
+            }
+          }
+        // NF4: interleave the slice's MFMAs with its fragment reads, table
+        // reads and decode VALU work (one wave per SIMD)
+        if constexpr (kRows > 0 && !kMx) sched_slice<2 * kRows, kRows + 8, 36, 0>();
+      }
+      __builtin_amdgcn_s_waitcnt(0x0F70);                  // vmcnt(0): this step's loads landed
+      lds_barrier();
+    };
+    for (int ks = 0; ks < nsteps; ks += 2) {
+      step(ks, A0, A1, B0, B1, Y, X);
+      if (ks + 1 < nsteps) step(ks + 1, A1, A0, B1, B0, X, Y);
+    }
+  };
+  if (allcols && nrows == 4) run_loop(std::integral_constant<int, 4>{});
+  else if (allcols && nrows == 3) run_loop(std::integral_constant<int, 3>{});
+  else if (allcols && nrows == 2) run_loop(std::integral_constant<int, 2>{});
+  else if (allcols && nrows == 1) run_loop(std::integral_constant<int, 1>{});
+  else run_loop(std::integral_constant<int, -1>{});
+
+  // ---- epilogue: one output row per lane ----
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    if (i >= nrows) continue;
+    const int m = 32 * i + lr;
+    const int p = pair_s[m];
+    const float sc = scale_s[m];
+    if constexpr (kGlu) {
+      const int col = n0 + 32 * wave;
+      if (m < valid && col < g.Nout) {
+        float v[16];
+#pragma unroll
+        for (int r = 0; r < 16; ++r) v[r] = silu_f32(acc[i][0][r]) * acc[i][1][r] * sc;
+        store_block_t(v, g.out + (int64_t)p * g.Nout + col, lh);
+      }
+    } else {
+#pragma unroll
+      for (int cb = 0; cb < 2; ++cb) {
+        const int col = n0 + 64 * wave + 32 * cb;
+        if (m < valid && col < g.Nout) {
+          float v[16];
+#pragma unroll
+          for (int r = 0; r < 16; ++r) v[r] = acc[i][cb][r] * sc;
+          store_block_t(v, g.out + (int64_t)p * g.Nout + col, lh);
+        }
+      }
+    }
+  }
+}
+
 template <int kMode>
 __global__ __launch_bounds__(kGemmThreads, 1) void grouped_gemm_fwd_kernel(GemmArgs g) {
   constexpr bool kGlu = kMode == kFwdNF4Glu;
@@ -778,6 +1016,10 @@ __global__ __launch_bounds__(kGemmThreads, 1) void grouped_gemm_fwd_kernel(GemmA
   if ((unsigned)e >= (unsigned)g.E || (unsigned)start >= (unsigned)g.P) return;
   const int valid = min(kTM, min(g.offsets[e + 1], g.P) - start);
   if (valid <= 0) return;
+  if (valid <= kNarrowRows) {
+    fwd_narrow<kMode>(g, e, n0, start, valid, tid, A0, A1, lut2, pair_s, row_s, scale_s);
+    return;
+  }
   const int nsteps = (g.Kc + kTK - 1) / kTK;
   // The codes of steps 0 and 1 depend on the tile only: their loads go out
   // first, alongside the pair ids (fewer dependent round trips before the

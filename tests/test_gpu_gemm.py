@@ -95,6 +95,30 @@ def test_tile_boundaries(fmt, K):
     assert_slices(bf16_to_host_f32(out), oracle.grouped_gemm(x, W, ids, E), ids, E)
 
 
+@pytest.mark.parametrize("fmt,K,N", [("nf4", 1088, 320), ("mx", 1056, 288), ("nf4", 2048, 512)])
+def test_narrow_tile_edges(fmt, K, N):
+    """K >= 1024: tiles of at most 128 rows take the column-per-wave layout,
+    longer ones the 2 x 2 layout.  Segments of 128 and 129 rows, 384 and 385
+    (a full tile then 128 or 129 rows), 32, 33, 97 and 1, an empty expert,
+    dropped pairs; N ends inside a 256-column tile (a column tile whose
+    last waves own no columns)."""
+    dev = device()
+    g = np.random.default_rng(K + N)
+    E = 10
+    sizes = [128, 129, 384, 385, 32, 33, 97, 1, 0, 64]
+    ids = np.concatenate([np.full(n, e, dtype=np.int32) for e, n in enumerate(sizes)]
+                         + [np.full(5, -1, dtype=np.int32)])
+    ids = g.permutation(ids).reshape(-1, 1)
+    bank = packed_nf4_bank(g, E, N, K) if fmt == "nf4" else packed_mx_bank(g, E, N, K)
+    W = LazyDecoded(fmt, *bank)
+    x = wl.draw_bf16(g, (ids.shape[0], K))
+    sc = g.uniform(0.5, 1.5, size=ids.shape).astype(np.float32)
+    say("gemm narrow tile edges", fmt, K, N)
+    out = _gemm(fmt, x, to_dev(bank[0], dev), to_dev(bank[1], dev), ids, E, dev, sc)
+    ref = oracle.grouped_gemm(x, W, ids, E, pair_scale=sc)
+    assert_slices(bf16_to_host_f32(out), ref, ids, E)
+
+
 @pytest.mark.parametrize("fmt,K", [("nf4", 256), ("mx", 256), ("nf4", 1088), ("mx", 1056)])
 def test_one_hot_probe_is_bit_exact(fmt, K):
     """A one-hot activation row picks one weight column: the output is the
