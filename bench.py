@@ -29,6 +29,9 @@ The same line carries
     (M = 2048, top-4), NF4 dgrad (M = 2048, top-8), the NF4 M = 4 decode, and
     the whole NF4 MoE layer (SwiGLU and router-weighted combine fused) at
     decode (M = 1) and prefill (M = 4096).
+The prefill and dgrad steps run eagerly (their kernels are long): the step
+time comes from a loop without any events; the per-kernel times from a
+second loop with events around each launch.
 All inputs are synthetic and resident in HBM before timing starts.
 """
 
@@ -114,6 +117,23 @@ class Timer:
 
     def avg_us(self):
         return 1e3 * float(np.mean([a.elapsed_time(b) for a, b in self.pairs]))
+
+
+def eager_steps(run, steps, warmup):
+    """Warmup, then ``steps`` steps with events around each launch (the
+    per-kernel times), then ``steps`` steps without events, timed as a whole
+    between two synchronizations: the step time.  Returns seconds per step."""
+    for _ in range(warmup):
+        run(False)
+    torch.cuda.synchronize()
+    for _ in range(steps):
+        run(True)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for _ in range(steps):
+        run(False)
+    torch.cuda.synchronize()
+    return (time.perf_counter() - t0) / steps
 
 
 # --------------------------------------------------------------------------
@@ -340,14 +360,7 @@ def prefill_layer_nf4(dev, steps, warmup):
         if timed:
             tc.stop(ev)
 
-    for _ in range(warmup):
-        run(False)
-    torch.cuda.synchronize()
-    t0 = time.perf_counter()
-    for _ in range(steps):
-        run(True)
-    torch.cuda.synchronize()
-    dt = time.perf_counter() - t0
+    dt = eager_steps(run, steps, warmup) * steps
     flops = 2.0 * P * (Ng * Kg + Nd * Kd)
     return {"workload": "qwen3-30b-a3b nf4 moe layer prefill M=4096 top-8 Zipf(1.1): route sort "
                         "+ swiglu gate_up gemm + down gemm (router-weight scale) + combine",
@@ -397,14 +410,7 @@ def prefill(dev, steps, warmup, fmt):
         if timed:
             td.stop(ev)
 
-    for _ in range(warmup):
-        run(False)
-    torch.cuda.synchronize()
-    t0 = time.perf_counter()
-    for _ in range(steps):
-        run(True)
-    torch.cuda.synchronize()
-    dt = time.perf_counter() - t0
+    dt = eager_steps(run, steps, warmup) * steps
     fg, fd = 2.0 * P * Ng * Kg, 2.0 * P * Nd * Kd
     ug, ud, us = tg.avg_us(), td.avg_us(), ts.avg_us()
     counts = np.bincount(route.reshape(-1), minlength=E)
@@ -423,7 +429,7 @@ def prefill(dev, steps, warmup, fmt):
 
 def dgrad(dev, steps, warmup, fmt="nf4"):
     """Input gradient of both projections: Qwen3 NF4 (M=2048 top-8) or
-    gpt-oss MXFP4 (M=2048 top-4), eager with per-launch events."""
+    gpt-oss MXFP4 (M=2048 top-4), eager."""
     if fmt == "nf4":
         cfgd, cfg, bank, fn = wl.QWEN, wl.CFG_QWEN_DGRAD, wl.random_nf4_bank, gq.gq_nf4_grouped_dgrad
     else:
@@ -451,14 +457,7 @@ def dgrad(dev, steps, warmup, fmt="nf4"):
         if timed:
             td.stop(ev)
 
-    for _ in range(warmup):
-        run(False)
-    torch.cuda.synchronize()
-    t0 = time.perf_counter()
-    for _ in range(steps):
-        run(True)
-    torch.cuda.synchronize()
-    dt = time.perf_counter() - t0
+    dt = eager_steps(run, steps, warmup) * steps
     fg, fd = 2.0 * P * Ng * Kg, 2.0 * P * Nd * Kd
     ug, ud = tg.avg_us(), td.avg_us()
     name = ("qwen3-30b-a3b nf4 dgrad M=2048 top-8 (16384 pairs)" if fmt == "nf4" else
