@@ -1,5 +1,5 @@
-"""Seeded random shapes through the prefill GEMM (NF4, MXFP4, SwiGLU) and
-the input gradient against the float64 oracle: expert counts, row counts
+"""Seeded random shapes through the prefill GEMM (NF4, MXFP4, SwiGLU), the
+input gradient and the decode launches against the float64 oracle: expert counts, row counts
 per expert (so tiles of every size class: <= 128 rows, 129..255, full,
 several), column counts ending inside a tile, K on both sides of the
 kernel switch (MXFP4 with a half step), dropped ids, pair scales and
@@ -81,3 +81,71 @@ def test_random_dgrad(seed):
     dx = fn(to_dev_bf16(dy, dev), to_dev(bank[0], dev), to_dev(bank[1], dev), route)
     torch.cuda.synchronize()
     assert_slices(bf16_to_host_f32(dx), oracle.grouped_dgrad(dy, W, pe, E), pe, E)
+
+
+def _wide_bits(g, rows, cols, dev):
+    """bf16 [rows, cols] device view with a random row padding, and its host bits."""
+    pad = 8 * int(g.integers(0, 3))
+    full = wl.draw_bf16(g, (rows, cols + pad))
+    return to_dev_bf16(full, dev)[:, :cols], np.ascontiguousarray(full[:, :cols])
+
+
+def _rows_close(got, ref, tol=oracle.REL_L2_TOL):
+    for i in range(ref.shape[0]):
+        nr = np.linalg.norm(ref[i])
+        if nr == 0.0:
+            assert not np.any(got[i]), i
+        else:
+            assert np.linalg.norm(got[i] - ref[i]) / nr <= tol, i
+
+
+@pytest.mark.parametrize("seed", range(N_CASES))
+def test_random_decode(seed):
+    """Decode launches: NF4 / MXFP4 GEMV (gather or flatten mode, pair
+    scales), the SwiGLU GEMV and the down GEMV with the combine fused."""
+    dev = device()
+    g = np.random.default_rng(9800 + seed)
+    kind = ["nf4", "mx", "glu", "down"][seed % 4]
+    E = int(g.integers(1, 10))
+    rows = int(g.integers(1, 9))
+    topk = int(g.integers(1, min(E, 8) + 1))
+    if kind == "down":
+        topk = min(topk, 64 // rows)
+        K = 64 * int(g.integers(1, 33))                    # I <= 2048
+    elif kind == "mx":
+        K = 32 * int(g.integers(1, 257))                   # <= 8192
+    else:
+        K = 64 * int(g.integers(1, 129))
+    N = 2 * int(g.integers(1, 400)) if kind == "glu" else int(g.integers(1, 700))
+    bank = packed_mx_bank(g, E, N, K) if kind == "mx" else packed_nf4_bank(g, E, N, K)
+    W = LazyDecoded("mx" if kind == "mx" else "nf4", *bank)
+    a, b = to_dev(bank[0], dev), to_dev(bank[1], dev)
+    ids = wl.route_uniform(g, rows, E, topk) if g.random() < 0.5 else \
+        g.integers(0, E, size=(rows, topk)).astype(np.int32)  # repeated experts too
+    ids[g.random(ids.shape) < 0.1] = -1
+    say("sweep decode", seed, kind, E, N, K, rows, topk)
+    if kind == "down":
+        act, acth = _wide_bits(g, rows * topk, K, dev)
+        w = wl.router_weights(g, rows, topk) if g.random() < 0.5 else None
+        y = gq.gq_nf4_grouped_gemv_down_combine(act, a, b, to_dev(ids, dev),
+                                                None if w is None else to_dev(w, dev))
+        torch.cuda.synchronize()
+        _rows_close(bf16_to_host_f32(y), oracle.down_combine(acth, W, ids, E, w))
+        return
+    flatten = kind != "glu" and g.random() < 0.3
+    if flatten:                                            # one input row per pair
+        x, xh = _wide_bits(g, rows * topk, K, dev)
+        ids = ids.reshape(-1, 1)
+    else:
+        x, xh = _wide_bits(g, rows, K, dev)
+    if kind == "glu":
+        out = gq.gq_nf4_grouped_gemv_swiglu(x, a, b, to_dev(ids, dev))
+        ref = oracle.gate_up_swiglu(xh, W, ids, E)
+    else:
+        sc = wl.router_weights(g, ids.shape[0], ids.shape[1]) if g.random() < 0.5 else None
+        fn = gq.gq_nf4_grouped_gemv if kind == "nf4" else gq.gq_mxfp4_grouped_gemv
+        out = fn(x, a, b, to_dev(ids, dev),
+                 pair_scale=None if sc is None else to_dev(sc.reshape(-1), dev))
+        ref = oracle.grouped_gemm(xh, W, ids, E, pair_scale=sc)
+    torch.cuda.synchronize()
+    assert_slices(bf16_to_host_f32(out), ref, ids, E)
