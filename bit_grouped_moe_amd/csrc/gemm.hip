@@ -743,8 +743,9 @@ __device__ __forceinline__ void sched_slice() {
 // (SwiGLU: block 0 is gate row j = 32 w + lr of the tile's outputs, block 1
 // the matching up row) and, in slice sl, k = 32 lh + 8 sl + [0, 8): the K
 // order of the A fragments, so the lane's operand for the whole step is the
-// 16 code bytes at byte 16 lh of the column's 32-byte step chunk (one NF4
-// absmax block / one MXFP4 scale block per lane half).  The activation tile
+// 16 code bytes at byte 16 lh of the column's 32-byte step chunk (the
+// step's 64 K are one NF4 absmax block; each lane half's 32 K one MXFP4
+// scale block).  The activation tile
 // (<= 128 rows) is still loaded straight into LDS, double-buffered, one
 // barrier per step.
 constexpr int kNarrowRows = 128;
