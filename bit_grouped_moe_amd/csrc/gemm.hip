@@ -18,12 +18,12 @@
 //  * shorter contractions and the input gradient (grouped_gemm_body): 128
 //    columns per tile, two workgroups per CU so that one workgroup's
 //    prologue and epilogue overlap the other's matrix work.
-// In both, the B tile (weights x 64 K) is decoded ONCE per workgroup from
-// packed codes into bf16 in LDS (double-buffered, one barrier per step) and
-// shared by the waves -- except on tiles of at most 128 rows in the first
-// kernel, where each wave owns 64 columns for all rows and decodes them
-// straight into MFMA operand registers; the K order inside a step is permuted identically
-// for A and B (lane half h takes k in [32h, 32h+32)), so every operand load
+// The B tile (weights x 64 K) is decoded ONCE per workgroup from packed
+// codes into bf16: in the first kernel each wave owns 64 of the 256 columns
+// for all rows and decodes them straight into MFMA operand registers; in the
+// second B goes through LDS (double-buffered, one barrier per step), shared
+// by the waves.  The K order inside a step is permuted identically for A and
+// B (lane half h takes k in [32h, 32h+32)), so every operand load
 // is a contiguous 16-byte piece; the weights are the first MFMA operand, so
 // a lane accumulates one output row and the epilogue writes rows from
 // registers.  Block index -> tile is XCD-aware: the hardware deals blocks
@@ -603,112 +603,12 @@ __global__ __launch_bounds__(kGemmThreads, 2) void grouped_gemm_fwd_shortk_kerne
 }
 
 // ---- forward kernel: 256 x 256 output tile, one wave per SIMD ----
-// Workgroup = 4 waves on one CU (one workgroup per CU: ~141 KB of LDS).
-//  * A (gathered activation rows, 256 x 64 per K step) goes from global
-//    memory straight into LDS with LDS-direct loads (no register round trip),
-//    double-buffered; rows are 128 bytes with the 16-byte chunk slot
-//    XOR-swizzled by (row >> 1) & 7 (conflict-free fragment reads).  Lane L
-//    of a load instruction fills slot L % 8 of row L / 8 of an 8-row group,
-//    so it fetches the global chunk (L % 8) ^ swizzle(row).
-//  * B (256 weight rows x 64 K per step) is decoded once per workgroup: thread
-//    t decodes the 64 codes of B column t (one NF4 absmax block or two MXFP4
-//    scale blocks) into bf16 in LDS (double-buffered, padded rows).  NF4
-//    goes through the code-byte pair table (nf4_pairs8) at LDS address 0,
-//    its reads one slice ahead of their use.
-//  * wave w owns the 32-row sub-tiles (w & 1) + 2i, i < 4 (interleaved so
-//    that short expert segments keep all four SIMDs busy) times the 128
-//    columns 128 * (w >> 1) + [0, 128): 4 x 4 v_mfma_f32_32x32x16_bf16 per
-//    16-wide K slice, accumulators in AGPRs.
-//  * K step ks: issue the LDS-direct loads of step ks+1's activations and the
-//    code loads of step ks+2; per slice, read the next slice's fragments,
-//    decode an eighth of step ks+1's B tile into the other buffer and run
-//    the slice's 16 MFMAs (NF4: interleaved with the LDS reads and the
-//    decode's VALU work, sched_slice); wait for the step's loads, one
-//    barrier.
-// For the SwiGLU variant the 256 B columns are gate rows j0 + [0, 64), the
-// matching up rows, gate rows j0 + [64, 128), their up rows: each wave holds
-// the gate and up values of the same 64 outputs.
+// Workgroup = 4 waves on one CU (256 accumulator registers per lane, ~70 KB
+// of LDS); the tile loop is fwd_columns below.
 constexpr int kXN = 256;                                  // B columns per tile
 
 typedef __attribute__((address_space(3))) void lds_void_t;
 typedef __attribute__((address_space(1))) const void glb_void_t;
-
-struct XLoad {
-  u32x4 c0, c1;    // codes of chunks 0-3 and 4-7 (8 weights each)
-  float a;         // NF4 absmax
-  uint32_t s0, s1; // MXFP4 scale bytes of the two 32-weight blocks
-  bool ok, ok1;    // column inside the matrix; second MXFP4 block inside K
-};
-
-template <int kMode>
-__device__ __forceinline__ XLoad x_load(const GemmArgs& g, int e, int n0, int ks, int t) {
-  XLoad L;
-  int n;
-  if constexpr (kMode == kFwdNF4Glu) {
-    const int j = n0 + (t & 63) + ((t >> 7) << 6);         // output column
-    L.ok = j < g.Nout;
-    n = min(j, g.Nout - 1) + (((t >> 6) & 1) ? g.Nout : 0);
-  } else {
-    n = n0 + t;
-    L.ok = n < g.Nw;
-    n = min(n, g.Nw - 1);
-  }
-  const int k0 = ks * kTK;                                  // < Kw
-  const bool full = k0 + kTK <= g.Kw;                       // MXFP4 K tail: half a step
-  const size_t row = (size_t)e * g.Nw + n;
-  const uint8_t* p = g.codes + row * (size_t)(g.Kw / 2) + k0 / 2;
-  L.c0 = *reinterpret_cast<const u32x4*>(p);
-  L.c1 = *reinterpret_cast<const u32x4*>(full ? p + 16 : p);
-  if constexpr (kMode == kFwdMX) {
-    const uint8_t* sp = static_cast<const uint8_t*>(g.scl) + row * (size_t)(g.Kw / 32) + k0 / 32;
-    L.s0 = sp[0];
-    L.s1 = sp[full ? 1 : 0];
-    L.ok1 = L.ok && full;
-    L.a = 0.f;
-  } else {
-    L.a = static_cast<const float*>(g.scl)[row * (size_t)(g.Kw / 64) + ks];
-    L.s0 = L.s1 = 0u;
-    L.ok1 = L.ok;
-  }
-  return L;
-}
-
-template <int kMode>
-__device__ __forceinline__ void x_decode_chunk(const XLoad& L, int q, const float* lut,
-                                               uint16_t* B, int t) {
-  const uint32_t cw = q < 4 ? L.c0[q & 3] : L.c1[q & 3];
-  uint32_t p[4];
-  if constexpr (kMode == kFwdMX) {
-    const float sc = q < 4 ? (L.ok ? e8m0_to_f32(L.s0) : 0.f) : (L.ok1 ? e8m0_to_f32(L.s1) : 0.f);
-#pragma unroll
-    for (int b = 0; b < 4; ++b) p[b] = e2m1_pair_bf16_scaled(cw, b, sc);
-  } else {
-    nf4_decode8_bf16(lut, cw, L.ok ? L.a : 0.f, p);
-  }
-  *reinterpret_cast<u32x4*>(B + t * kBStride + 8 * q) = u32x4{p[0], p[1], p[2], p[3]};
-}
-
-// NF4 decode split in two so the table reads can run a slice ahead of their
-// use: fetch the codebook values of chunks q, q+1, then scale, round and
-// store them.
-__device__ __forceinline__ uint32_t x_chunk_word(const XLoad& L, int q) {
-  return q < 4 ? L.c0[q & 3] : L.c1[q & 3];
-}
-__device__ __forceinline__ void x_fetch2(const XLoad& L, int q, const f32x2* tab, float (&v)[16]) {
-  nf4_pairs8(tab, x_chunk_word(L, q), v);
-  nf4_pairs8(tab, x_chunk_word(L, q + 1), v + 8);
-}
-__device__ __forceinline__ void x_finish2(const XLoad& L, int q, const float (&v)[16], uint16_t* B,
-                                          int t) {
-  const float a = L.ok ? L.a : 0.f;
-#pragma unroll
-  for (int c = 0; c < 2; ++c) {
-    uint32_t p[4];
-#pragma unroll
-    for (int b = 0; b < 4; ++b) p[b] = pack_bf16x2(v[8 * c + 2 * b] * a, v[8 * c + 2 * b + 1] * a);
-    *reinterpret_cast<u32x4*>(B + t * kBStride + 8 * (q + c)) = u32x4{p[0], p[1], p[2], p[3]};
-  }
-}
 
 // Instruction interleave for one K slice of kM MFMAs: after each MFMA, an
 // even share of the slice's LDS reads, VALU ops and LDS writes, so that the
@@ -732,23 +632,27 @@ __device__ __forceinline__ void sched_slice() {
   sched_slice_seq<kM, kDs, kValu, kDsw>(std::make_integer_sequence<int, kM>{});
 }
 
-// ---- narrow tiles (at most 128 rows) of the 256-column kernel ----
-// Under skewed routing most experts end in a partial tile, and a tile of few
-// rows spends its steps decoding B and moving it through LDS rather than in
-// the matrix cores.  Such tiles use another wave layout: wave w owns the B
-// columns 64 w + [0, 64) for ALL of the tile's (at most four) 32-row
-// sub-tiles, so each B column feeds exactly one wave, which decodes it
-// straight into MFMA operand registers -- no B tile in LDS, no B fragment
-// reads.  Lane (lr, lh) of column block cb holds column 64 w + 32 cb + lr
+// ---- the 256-column tile loop: one B column per wave, decoded in registers ----
+// Wave w owns the B columns 64 w + [0, 64) for ALL of the tile's 32-row
+// sub-tiles (up to 4 on tiles of at most 128 rows, up to 8 otherwise: 8 x 2
+// blocks of 32 x 32 accumulators fill the 256 AGPRs), so each B column feeds
+// exactly one wave, which decodes it straight into MFMA operand registers:
+// no B tile in LDS, no B fragment reads, no B barrier traffic.  (A 2 x 2
+// layout with B decoded once into LDS and read by two waves each was 2-4%
+// slower on every workload measured, 8-10% on tiles of at most 64 rows.)
+// Lane (lr, lh) of column block cb holds column 64 w + 32 cb + lr
 // (SwiGLU: block 0 is gate row j = 32 w + lr of the tile's outputs, block 1
 // the matching up row) and, in slice sl, k = 32 lh + 8 sl + [0, 8): the K
 // order of the A fragments, so the lane's operand for the whole step is the
 // 16 code bytes at byte 16 lh of the column's 32-byte step chunk (the
 // step's 64 K are one NF4 absmax block; each lane half's 32 K one MXFP4
-// scale block).  The activation tile
-// (<= 128 rows) is still loaded straight into LDS, double-buffered, one
-// barrier per step.
-constexpr int kNarrowRows = 128;
+// scale block).  The activation tile goes from global memory straight into
+// LDS (LDS-direct loads, double-buffered, one barrier per step); each wave
+// reads the A fragments of every active sub-tile.  Per 16-wide K slice a
+// wave runs (active sub-tiles) x 2 v_mfma_f32_32x32x16_bf16, interleaved
+// (NF4) with its fragment reads, table reads and decode VALU work.
+// The SwiGLU epilogue combines blocks 0 and 1, which sit in the same lanes.
+constexpr int kNarrowRows = 128;                           // tiles up to here: 4 sub-tiles
 
 struct NLoad {
   u32x4 c[2];      // 32 codes of column blocks 0 and 1
@@ -779,8 +683,8 @@ __device__ __forceinline__ NLoad n_load(const GemmArgs& g, int e, int jcol, int 
   return L;
 }
 
-template <int kMode>
-__device__ __forceinline__ void fwd_narrow(const GemmArgs& g, int e, int n0, int start, int valid,
+template <int kMode, int kSub>
+__device__ __forceinline__ void fwd_columns(const GemmArgs& g, int e, int n0, int start, int valid,
                                            int tid, uint16_t* A0, uint16_t* A1, f32x2* lut2,
                                            int* pair_s, int* row_s, float* scale_s) {
   constexpr bool kGlu = kMode == kFwdNF4Glu;
@@ -812,13 +716,18 @@ __device__ __forceinline__ void fwd_narrow(const GemmArgs& g, int e, int n0, int
   if constexpr (!kMx) nf4_pairs_init(lut2, tid);
   lds_barrier();
 
-  // LDS-direct activation loads: instruction j of wave w fills rows
-  // 32 w + 8 j + [0, 8) (same slot swizzle as the 256-row tiles).
-  uint32_t voff[4];
+  // LDS-direct activation loads: instruction j of wave w fills the 8-row
+  // group arow(j) (128-row tiles: the wave's own 32 rows; 256-row tiles:
+  // groups dealt round-robin to the waves).  Rows are 128 bytes with the
+  // 16-byte chunk slot XOR-swizzled by (row >> 1) & 7 (conflict-free
+  // fragment reads): lane L fills slot L % 8 of row L / 8 of the group, so it
+  // fetches the global chunk (L % 8) ^ swizzle(row).
+  auto arow = [&](int j) { return kSub == 4 ? 32 * wave + 8 * j : 8 * (4 * j + wave); };
+  uint32_t voff[kSub];
   uint32_t tailbits = 0;
 #pragma unroll
-  for (int j = 0; j < 4; ++j) {
-    const int R = 32 * wave + 8 * j + (lane >> 3);
+  for (int j = 0; j < kSub; ++j) {
+    const int R = arow(j) + (lane >> 3);
     const int c = (lane & 7) ^ ((R >> 1) & 7);
     voff[j] = (uint32_t)row_s[R] * (uint32_t)(g.x_stride * 2) + 16u * (uint32_t)c;
     tailbits |= (c >= 4 ? 1u : 0u) << j;
@@ -827,9 +736,9 @@ __device__ __forceinline__ void fwd_narrow(const GemmArgs& g, int e, int n0, int
     const char* xb = reinterpret_cast<const char*>(g.x) + (size_t)ks * (kTK * 2);
     const bool tail = ktail && ks == nsteps - 1;
 #pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      if (32 * wave + 8 * j < valid) {
-        uint16_t* dst = Adst + (32 * wave + 8 * j) * kTK;
+    for (int j = 0; j < kSub; ++j) {
+      if (arow(j) < valid) {                               // groups past the segment: skipped
+        uint16_t* dst = Adst + arow(j) * kTK;
         if (kMx && tail && ((tailbits >> j) & 1u)) {
           *reinterpret_cast<u32x4*>(dst + lane * 8) = u32x4{0u, 0u, 0u, 0u};
         } else {
@@ -863,9 +772,9 @@ __device__ __forceinline__ void fwd_narrow(const GemmArgs& g, int e, int n0, int
     return as_bf16x8(u32x4{w[0], w[1], w[2], w[3]});
   };
 
-  f32x16 acc[4][2];
+  f32x16 acc[kSub][2];
 #pragma unroll
-  for (int i = 0; i < 4; ++i)
+  for (int i = 0; i < kSub; ++i)
 #pragma unroll
     for (int c = 0; c < 2; ++c)
 #pragma unroll
@@ -894,10 +803,10 @@ __device__ __forceinline__ void fwd_narrow(const GemmArgs& g, int e, int n0, int
       dma_a(min(ks + 1, nsteps - 1), An);
       Lfill = load(min(ks + 2, nsteps - 1));
       __builtin_amdgcn_sched_barrier(0);                   // keep the loads at the step start
-      u32x4 fa[2][4];
-      auto frags = [&](int sl, u32x4 (&a)[4]) {
+      u32x4 fa[2][kSub];
+      auto frags = [&](int sl, u32x4 (&a)[kSub]) {
 #pragma unroll
-        for (int i = 0; i < 4; ++i) {
+        for (int i = 0; i < kSub; ++i) {
           if (kRows >= 0 ? i < kRows : true) a[i] = read_a(Ac, i, sl);
         }
       };
@@ -908,7 +817,7 @@ __device__ __forceinline__ void fwd_narrow(const GemmArgs& g, int e, int n0, int
 #pragma unroll
         for (int cb = 0; cb < 2; ++cb) Bn[cb][sl] = decode(Ldec, min(ks + 1, nsteps - 1), cb, sl);
 #pragma unroll
-        for (int i = 0; i < 4; ++i)
+        for (int i = 0; i < kSub; ++i)
 #pragma unroll
           for (int cb = 0; cb < 2; ++cb) {
             if constexpr (kRows >= 0) {
@@ -933,15 +842,21 @@ __device__ __forceinline__ void fwd_narrow(const GemmArgs& g, int e, int n0, int
       if (ks + 1 < nsteps) step(ks + 1, A1, A0, B1, B0, X, Y);
     }
   };
-  if (allcols && nrows == 4) run_loop(std::integral_constant<int, 4>{});
-  else if (allcols && nrows == 3) run_loop(std::integral_constant<int, 3>{});
-  else if (allcols && nrows == 2) run_loop(std::integral_constant<int, 2>{});
-  else if (allcols && nrows == 1) run_loop(std::integral_constant<int, 1>{});
+  // loop variants by active sub-tiles (1..4 on 128-row tiles, 5..8 on
+  // 256-row tiles), all columns valid; else the guarded generic loop
+  using I8 = std::integral_constant<int, kSub == 8 ? 8 : 4>;
+  using I7 = std::integral_constant<int, kSub == 8 ? 7 : 3>;
+  using I6 = std::integral_constant<int, kSub == 8 ? 6 : 2>;
+  using I5 = std::integral_constant<int, kSub == 8 ? 5 : 1>;
+  if (allcols && nrows == I8::value) run_loop(I8{});
+  else if (allcols && nrows == I7::value) run_loop(I7{});
+  else if (allcols && nrows == I6::value) run_loop(I6{});
+  else if (allcols && nrows == I5::value) run_loop(I5{});
   else run_loop(std::integral_constant<int, -1>{});
 
   // ---- epilogue: one output row per lane ----
 #pragma unroll
-  for (int i = 0; i < 4; ++i) {
+  for (int i = 0; i < kSub; ++i) {
     if (i >= nrows) continue;
     const int m = 32 * i + lr;
     const int p = pair_s[m];
@@ -972,18 +887,14 @@ __device__ __forceinline__ void fwd_narrow(const GemmArgs& g, int e, int n0, int
 template <int kMode>
 __global__ __launch_bounds__(kGemmThreads, 1) void grouped_gemm_fwd_kernel(GemmArgs g) {
   constexpr bool kGlu = kMode == kFwdNF4Glu;
-  constexpr bool kMx = kMode == kFwdMX;
   constexpr int kTNo = kGlu ? kXN / 2 : kXN;               // output columns per tile
   // Separate arrays: the compiler then knows that an LDS-direct load into one
   // buffer does not alias reads of the other (no extra waits).
   __shared__ __attribute__((aligned(16))) uint16_t A0[kTM * kTK];
   __shared__ __attribute__((aligned(16))) uint16_t A1[kTM * kTK];
-  __shared__ __attribute__((aligned(16))) uint16_t B0[kXN * kBStride];
-  __shared__ __attribute__((aligned(16))) uint16_t B1[kXN * kBStride];
   __shared__ int pair_s[kTM];                              // pair of each tile row
   __shared__ int row_s[kTM];                               // its activation row (pair / topk)
   __shared__ float scale_s[kTM];                           // its pair weight (1 if none)
-  __shared__ float lut[16];
   // NF4 code-byte pair table; the alignment places it at LDS address 0
   __shared__ __attribute__((aligned(4096))) f32x2 lut2[256];
 
@@ -1017,205 +928,10 @@ __global__ __launch_bounds__(kGemmThreads, 1) void grouped_gemm_fwd_kernel(GemmA
   if ((unsigned)e >= (unsigned)g.E || (unsigned)start >= (unsigned)g.P) return;
   const int valid = min(kTM, min(g.offsets[e + 1], g.P) - start);
   if (valid <= 0) return;
-  if (valid <= kNarrowRows) {
-    fwd_narrow<kMode>(g, e, n0, start, valid, tid, A0, A1, lut2, pair_s, row_s, scale_s);
-    return;
-  }
-  const int nsteps = (g.Kc + kTK - 1) / kTK;
-  // The codes of steps 0 and 1 depend on the tile only: their loads go out
-  // first, alongside the pair ids (fewer dependent round trips before the
-  // first MFMA).
-  XLoad X = x_load<kMode>(g, e, n0, 0, tid);
-  XLoad Y = x_load<kMode>(g, e, n0, min(1, nsteps - 1), tid);
-  float sc_t;                                              // pair weight of tile row tid
-  {
-    int p = g.sorted_pairs[start + min(tid, valid - 1)];
-    p = ((unsigned)p < (unsigned)g.P) ? p : 0;
-    pair_s[tid] = p;
-    row_s[tid] = p / g.topk;
-    sc_t = g.pair_scale ? g.pair_scale[p] : 1.f;
-  }
-  if constexpr (!kMx) {
-    nf4_lut_init(lut, tid);
-    nf4_pairs_init(lut2, tid);
-  }
-  lds_barrier();
-
-  // wave index as a scalar: per-wave branches stay scalar branches
-  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6), lane = tid & 63;
-  const int lr = lane & 31, lh = lane >> 5;
-  const int rg = wave & 1, hc = wave >> 1;
-  const bool ktail = kMx && (g.Kc % kTK) != 0;             // MXFP4: last step half full
-  const int ovalid = g.Nout - n0;                          // output columns left (multiple of 32)
-
-  // LDS-direct activation loads: instruction j of wave w fills rows
-  // 64w + 8j + [0, 8).  Byte offsets of the lane's 8 source chunks; they
-  // fit 32 bits (host check on rows * stride).
-  uint32_t voff[8];
-  uint32_t tailbits = 0;                                   // chunk >= 4 (MXFP4 K tail)
-#pragma unroll
-  for (int j = 0; j < 8; ++j) {
-    const int R = 64 * wave + 8 * j + (lane >> 3);
-    const int c = (lane & 7) ^ ((R >> 1) & 7);
-    voff[j] = (uint32_t)row_s[R] * (uint32_t)(g.x_stride * 2) + 16u * (uint32_t)c;
-    tailbits |= (c >= 4 ? 1u : 0u) << j;
-  }
-  // MXFP4 K tail (last step half full): lanes whose chunk lies past K write
-  // zeros to their LDS slot instead of loading, so no operand needs masking.
-  auto dma_a = [&](int ks, uint16_t* Adst) {
-    const char* xb = reinterpret_cast<const char*>(g.x) + (size_t)ks * (kTK * 2);
-    const bool tail = ktail && ks == nsteps - 1;
-#pragma unroll
-    for (int j = 0; j < 8; ++j) {
-      if (64 * wave + 8 * j < valid) {                     // rows past the segment: skipped
-        uint16_t* dst = Adst + (64 * wave + 8 * j) * kTK;
-        if (kMx && tail && ((tailbits >> j) & 1u)) {
-          *reinterpret_cast<u32x4*>(dst + lane * 8) = u32x4{0u, 0u, 0u, 0u};
-        } else {
-          __builtin_amdgcn_global_load_lds((glb_void_t*)(xb + voff[j]), (lds_void_t*)dst, 16, 0,
-                                           0);
-        }
-      }
-    }
-  };
-  // Fragment reads: A rows 32 * (2i + rg) + lr, B columns 128 hc + 32 cb + lr;
-  // lane half lh takes K chunk 4 lh + sl of slice sl.
-  const int aslot_x = (lr >> 1) & 7;
-  auto read_a = [&](const uint16_t* A, int i, int sl) -> u32x4 {
-    const int R = 32 * (2 * i + rg) + lr;
-    return *reinterpret_cast<const u32x4*>(A + R * kTK + (((lh * 4 + sl) ^ aslot_x) * 8));
-  };
-  auto read_b = [&](const uint16_t* B, int cb, int sl) -> bf16x8 {
-    return as_bf16x8(*reinterpret_cast<const u32x4*>(
-        B + (128 * hc + 32 * cb + lr) * kBStride + (lh * 4 + sl) * 8));
-  };
-
-  f32x16 acc[4][4];
-#pragma unroll
-  for (int i = 0; i < 4; ++i)
-#pragma unroll
-    for (int c = 0; c < 4; ++c)
-#pragma unroll
-      for (int r = 0; r < 16; ++r) acc[i][c][r] = 0.f;
-
-  bool act[4], cok[4];
-#pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    act[i] = 32 * (2 * i + rg) < valid;
-    // SwiGLU: column blocks 0, 1 hold gate, 2, 3 the up values of outputs 64 hc + 32 (i & 1)
-    cok[i] = kGlu ? 64 * hc + 32 * (i & 1) < ovalid : 128 * hc + 32 * i < ovalid;
-  }
-  int nrows = 0;
-#pragma unroll
-  for (int i = 0; i < 4; ++i) nrows += act[i] ? 1 : 0;
-  const bool allcols = kGlu ? 64 * hc + 64 <= ovalid : 128 * hc + 128 <= ovalid;
-
-  // ---- prologue: step 0 staged and decoded; step 1's codes in flight ----
-  dma_a(0, A0);
-#pragma unroll
-  for (int q = 0; q < 8; ++q) x_decode_chunk<kMode>(X, q, lut, B0, tid);
-  float qn[16];                                             // NF4: fetched table values in flight
-  if constexpr (!kMx) x_fetch2(Y, 0, lut2, qn);
-  scale_s[tid] = sc_t;                                      // read in the epilogue
-  __builtin_amdgcn_s_waitcnt(0);                            // everything, incl. the LDS-direct loads
-  lds_barrier();
-
-  auto run_loop = [&](auto rows_c) {
-    // -1: guarded generic path; 0: no active sub-tile (the wave only decodes)
-    constexpr int kRows = decltype(rows_c)::value;
-    auto step = [&](int ks, const uint16_t* Ac, uint16_t* An, const uint16_t* Bc, uint16_t* Bn,
-                    XLoad& Ldec, XLoad& Lfill) {
-      dma_a(min(ks + 1, nsteps - 1), An);
-      Lfill = x_load<kMode>(g, e, n0, min(ks + 2, nsteps - 1), tid);
-      __builtin_amdgcn_sched_barrier(0);                   // keep the loads at the step start
-      u32x4 fa[2][4];
-      bf16x8 fb[2][4];
-      auto frags = [&](int sl, u32x4 (&a)[4], bf16x8 (&b)[4]) {
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          if (kRows >= 0 ? i < kRows : true) a[i] = read_a(Ac, i, sl);
-        }
-        if constexpr (kRows != 0) {
-#pragma unroll
-          for (int c = 0; c < 4; ++c) b[c] = read_b(Bc, c, sl);
-        }
-      };
-      auto mfmas = [&](const u32x4 (&a)[4], const bf16x8 (&b)[4]) {
-#pragma unroll
-        for (int i = 0; i < 4; ++i)
-#pragma unroll
-          for (int c = 0; c < 4; ++c) {
-            // weights as the first operand: the accumulator holds the
-            // transposed tile, one output row per lane
-            if constexpr (kRows >= 0) {
-              if (i < kRows)
-                acc[i][c] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(b[c], as_bf16x8(a[i]),
-                                                                    acc[i][c], 0, 0, 0);
-            } else {
-              if (act[i] && cok[c])
-                acc[i][c] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(b[c], as_bf16x8(a[i]),
-                                                                    acc[i][c], 0, 0, 0);
-            }
-          }
-      };
-      frags(0, fa[0], fb[0]);
-#pragma unroll
-      for (int sl = 0; sl < 4; ++sl) {
-        if (sl < 3) frags(sl + 1, fa[(sl + 1) & 1], fb[(sl + 1) & 1]);
-        if constexpr (kMx) {
-          x_decode_chunk<kMode>(Ldec, 2 * sl, lut, Bn, tid);
-          x_decode_chunk<kMode>(Ldec, 2 * sl + 1, lut, Bn, tid);
-        } else {
-          // table values of the next slice's chunks (the next step's first
-          // two after the last slice), then finish this slice's two chunks
-          float qf[16];
-          if (sl < 3) x_fetch2(Ldec, 2 * sl + 2, lut2, qf);
-          else x_fetch2(Lfill, 0, lut2, qf);
-          x_finish2(Ldec, 2 * sl, qn, Bn, tid);
-#pragma unroll
-          for (int u = 0; u < 16; ++u) qn[u] = qf[u];
-        }
-        mfmas(fa[sl & 1], fb[sl & 1]);
-        // (the MXFP4 decode is light enough that the default order is
-        // faster than this interleave)
-        if constexpr (kRows > 0 && !kMx) sched_slice<4 * kRows, 12 + kRows, 32, 2>();
-      }
-      __builtin_amdgcn_s_waitcnt(0x0F70);                  // vmcnt(0): this step's loads landed
-      lds_barrier();
-    };
-    for (int ks = 0; ks < nsteps; ks += 2) {
-      step(ks, A0, A1, B0, B1, Y, X);
-      if (ks + 1 < nsteps) step(ks + 1, A1, A0, B1, B0, X, Y);
-    }
-  };
-  if (allcols && nrows == 4) run_loop(std::integral_constant<int, 4>{});
-  else if (allcols && nrows == 3) run_loop(std::integral_constant<int, 3>{});
-  else if (allcols && nrows == 2) run_loop(std::integral_constant<int, 2>{});
-  else if (allcols && nrows == 1) run_loop(std::integral_constant<int, 1>{});
-  else if (nrows == 0) run_loop(std::integral_constant<int, 0>{});
-  else run_loop(std::integral_constant<int, -1>{});
-
-  // ---- epilogue: one output row per lane (see store_block_t) ----
-  constexpr int kWo = kGlu ? 64 : 128;                     // output columns per wave
-  const int c0 = n0 + hc * kWo;                             // first output column of the wave
-#pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    if (!act[i]) continue;
-    const int m = 32 * (2 * i + rg) + lr;
-    const int p = pair_s[m];
-    const float sc = scale_s[m];
-#pragma unroll
-    for (int c = 0; c < kWo / 32; ++c) {
-      const int col = c0 + 32 * c;
-      if (m < valid && col < g.Nout) {
-        float v[16];
-#pragma unroll
-        for (int r = 0; r < 16; ++r)
-          v[r] = kGlu ? silu_f32(acc[i][c][r]) * acc[i][c + 2][r] * sc : acc[i][c][r] * sc;
-        store_block_t(v, g.out + (int64_t)p * g.Nout + col, lh);
-      }
-    }
-  }
+  if (valid <= kNarrowRows)
+    fwd_columns<kMode, 4>(g, e, n0, start, valid, tid, A0, A1, lut2, pair_s, row_s, scale_s);
+  else
+    fwd_columns<kMode, 8>(g, e, n0, start, valid, tid, A0, A1, lut2, pair_s, row_s, scale_s);
 }
 
 // Contractions of at least this many elements use the 256 x 256 kernel
