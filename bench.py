@@ -168,8 +168,10 @@ def decode_nf4(dev, steps, warmup, M=1):
         step(i)
     g_steps = capture(step, steps)
     g_gate = capture(gate, steps)
+    g_down = capture(down, steps)
     g_steps.replay()                                   # first replay uploads the graph
     g_gate.replay()
+    g_down.replay()
     torch.cuda.synchronize()
 
     t0 = time.perf_counter()
@@ -177,6 +179,7 @@ def decode_nf4(dev, steps, warmup, M=1):
     torch.cuda.synchronize()
     dt = time.perf_counter() - t0
     gate_ms = event_ms(g_gate.replay)
+    down_ms = event_ms(g_down.replay)
 
     def step_bytes(i):
         d = len(set(ids[i].reshape(-1).tolist()))
@@ -187,7 +190,9 @@ def decode_nf4(dev, steps, warmup, M=1):
     byts = [step_bytes(i) for i in range(steps)]
     total = sum(a + b for a, b in byts)
     gate_bytes = float(np.mean([a for a, _ in byts]))
+    down_bytes = float(np.mean([b for _, b in byts]))
     gate_us = 1e3 * gate_ms / steps
+    down_us = 1e3 * down_ms / steps
     sample = {"ids": ids[:steps], "banks_g": banks_g, "banks_d": banks_d, "x": x, "xd": xd}
     return {
         "ms_per_step": 1e3 * dt / steps,
@@ -196,49 +201,115 @@ def decode_nf4(dev, steps, warmup, M=1):
         "gate_up_bytes_per_launch": gate_bytes,
         "gate_up_us": gate_us,
         "gate_up_gbs": gate_bytes / (gate_us * 1e-6) / 1e9,
+        "down_bytes_per_launch": down_bytes,
+        "down_us": down_us,
+        "down_gbs": down_bytes / (down_us * 1e-6) / 1e9,
     }, sample
 
 
-def controls(dev, nbytes, n=64):
-    """Empty-launch floor and a cold streaming read of nbytes, graph-replayed."""
+def probes_lib():
     lib = ctypes.CDLL(os.path.join(ROOT, "bit_grouped_moe_amd", "libgq_probes.so"))
     lib.gq_probe_empty.argtypes = [ctypes.c_void_p]
-    lib.gq_probe_stream_read.argtypes = [ctypes.c_void_p, ctypes.c_int64, ctypes.c_void_p,
-                                         ctypes.c_void_p]
+    lib.gq_probe_stream_read.argtypes = [ctypes.c_void_p, ctypes.c_int64, ctypes.c_int32,
+                                         ctypes.c_void_p, ctypes.c_void_p]
     lib.gq_probe_copy.argtypes = [ctypes.c_void_p, ctypes.c_void_p, ctypes.c_int64,
                                   ctypes.c_void_p]
-    nb = (nbytes + 15) // 16 * 16
-    nbuf = 40                                          # 40 x 14 MB >> the 256 MB cache
-    bufs = [torch.randint(0, 255, (nb,), dtype=torch.uint8, device=dev) for _ in range(nbuf)]
-    sink = torch.zeros(4, dtype=torch.int32, device=dev)
+    lib.gq_probe_mfma.argtypes = [ctypes.c_int32, ctypes.c_int64, ctypes.c_int32,
+                                  ctypes.c_void_p, ctypes.c_void_p]
+    lib.gq_probe_mfma_flops.argtypes = [ctypes.c_int32]
+    lib.gq_probe_mfma_flops.restype = ctypes.c_int64
+    lib.gq_probe_mfma_per_wave_iter.restype = ctypes.c_int32
+    return lib
 
-    def stream(i):
-        st = lib.gq_probe_stream_read(ctypes.c_void_p(bufs[i % nbuf].data_ptr()), nb,
-                                      ctypes.c_void_p(sink.data_ptr()),
-                                      ctypes.c_void_p(torch.cuda.current_stream().cuda_stream))
-        assert st == 0
+
+def _stream():
+    return ctypes.c_void_p(torch.cuda.current_stream().cuda_stream)
+
+
+def fit_line(xs, ys):
+    """Least-squares t = t0 + bytes / bw over the points (bytes, us):
+    returns (t0_us, bw_gbs)."""
+    A = np.stack([np.ones(len(xs)), np.asarray(xs, dtype=np.float64)], axis=1)
+    (t0, slope), *_ = np.linalg.lstsq(A, np.asarray(ys, dtype=np.float64), rcond=None)
+    return float(t0), float(1e-3 / slope) if slope > 0 else float("inf")
+
+
+def controls(dev, sizes, n=64):
+    """Same-run controls, graph-replayed: the empty-launch floor, a plain copy
+    of sizes[0] bytes, and a cold streaming read of every size in ``sizes``
+    (each at 1, 4 and 16 loads per thread; the fastest shape is the control
+    for that size), plus the fit t = t0 + bytes/bw over the stream sizes."""
+    lib = probes_lib()
+    sink = torch.zeros(4, dtype=torch.int32, device=dev)
+    out = {"stream": []}
+    for nbytes in sizes:
+        nb = (int(nbytes) + 15) // 16 * 16
+        nbuf = max(4, -(-600_000_000 // nb))           # > 2x the 256 MB last-level cache
+        bufs = [torch.randint(0, 255, (nb,), dtype=torch.uint8, device=dev) for _ in range(nbuf)]
+        best = None
+        for L in (1, 4, 16):
+            def stream(i, L=L):
+                assert lib.gq_probe_stream_read(ctypes.c_void_p(bufs[i % nbuf].data_ptr()), nb, L,
+                                                ctypes.c_void_p(sink.data_ptr()), _stream()) == 0
+            gs = capture(stream, n)
+            gs.replay()
+            us = 1e3 * event_ms(gs.replay) / n
+            if best is None or us < best[1]:
+                best = (L, us)
+        out["stream"].append({"bytes": nb, "us": best[1], "gbs": nb / (best[1] * 1e-6) / 1e9,
+                              "loads_per_thread": best[0]})
+        if nbytes == sizes[0]:
+            dst = torch.empty(nb, dtype=torch.uint8, device=dev)
+
+            def copy(i):
+                assert lib.gq_probe_copy(ctypes.c_void_p(bufs[i % nbuf].data_ptr()),
+                                         ctypes.c_void_p(dst.data_ptr()), nb, _stream()) == 0
+            gc = capture(copy, n)
+            gc.replay()
+            us_copy = 1e3 * event_ms(gc.replay) / n
+            out["copy_us"] = us_copy
+            out["copy_gbs"] = 2 * nb / (us_copy * 1e-6) / 1e9
+            del dst
+        del bufs
 
     def empty(i):
-        assert lib.gq_probe_empty(ctypes.c_void_p(torch.cuda.current_stream().cuda_stream)) == 0
+        assert lib.gq_probe_empty(_stream()) == 0
 
-    dst = torch.empty(nb, dtype=torch.uint8, device=dev)
-
-    def copy(i):
-        st = lib.gq_probe_copy(ctypes.c_void_p(bufs[i % nbuf].data_ptr()),
-                               ctypes.c_void_p(dst.data_ptr()), nb,
-                               ctypes.c_void_p(torch.cuda.current_stream().cuda_stream))
-        assert st == 0
-
-    gs, ge, gc = capture(stream, n), capture(empty, n), capture(copy, n)
-    gs.replay()
+    ge = capture(empty, n)
     ge.replay()
-    gc.replay()
-    us_stream = 1e3 * event_ms(gs.replay) / n
-    us_empty = 1e3 * event_ms(ge.replay) / n
-    us_copy = 1e3 * event_ms(gc.replay) / n
-    return {"empty_launch_us": us_empty, "stream_read_us": us_stream,
-            "stream_read_gbs": nb / (us_stream * 1e-6) / 1e9, "stream_read_bytes": nb,
-            "copy_us": us_copy, "copy_gbs": 2 * nb / (us_copy * 1e-6) / 1e9}
+    out["empty_launch_us"] = 1e3 * event_ms(ge.replay) / n
+    t0, bw = fit_line([s["bytes"] for s in out["stream"]], [s["us"] for s in out["stream"]])
+    out["stream_fit"] = {"t0_us": t0, "bw_gbs": bw, "bw_frac_hbm": bw / HBM_PEAK_GBS}
+    return out
+
+
+def mfma_rates(dev, iters=4096, blocks=1024, launches=12):
+    """Dense matrix-instruction rates on this GPU (random operands, four
+    waves per SIMD): bf16 32x32x16 and the block-scaled 32x32x64 f8f6f4
+    instruction with e4m3 x e2m1, e2m1 x e2m1 and e4m3 x e4m3 operands.
+    Each kind runs ``launches`` launches back to back; the rate is taken
+    over the last half (the clock settles under sustained load)."""
+    lib = probes_lib()
+    sink = torch.zeros(4, dtype=torch.int32, device=dev)
+    per_iter = lib.gq_probe_mfma_per_wave_iter()
+    names = {0: "bf16_32x32x16", 1: "scale_e4m3_x_e2m1_32x32x64",
+             2: "scale_e2m1_x_e2m1_32x32x64", 3: "scale_e4m3_x_e4m3_32x32x64"}
+    res = {}
+    for kind, name in names.items():
+        flops = lib.gq_probe_mfma_flops(kind) * per_iter * iters * blocks * 4
+        times = []
+        for _ in range(launches):
+            times.append(event_ms(lambda: lib.gq_probe_mfma(kind, iters, blocks,
+                                                             ctypes.c_void_p(sink.data_ptr()),
+                                                             _stream())))
+        ms = float(np.median(times[launches // 2:]))
+        insts = per_iter * iters * blocks * 4
+        res[name] = {"tflops": flops / (ms * 1e-3) / 1e12,
+                     "ns_per_inst_per_simd": ms * 1e6 / (insts / 1024)}
+    bf = res["bf16_32x32x16"]["tflops"]
+    for name in names.values():
+        res[name]["vs_bf16_flop_rate"] = res[name]["tflops"] / bf
+    return res
 
 
 def decode_mx(dev, steps, warmup):
@@ -260,29 +331,36 @@ def decode_mx(dev, steps, warmup):
         b, s = banks_g[i % copies]
         gq.gq_mxfp4_grouped_gemv(x, b, s, ids_g[i], out=out_g)
 
-    def step(i):
-        gate(i)
+    def down(i):
         b, s = banks_d[i % copies]
         gq.gq_mxfp4_grouped_gemv(xd, b, s, ids_d[i], out=out_d)
 
+    def step(i):
+        gate(i)
+        down(i)
+
     for i in range(steps, steps + warmup):
         step(i)
-    g_steps, g_gate = capture(step, steps), capture(gate, steps)
+    g_steps, g_gate, g_down = capture(step, steps), capture(gate, steps), capture(down, steps)
     g_steps.replay()
     g_gate.replay()
+    g_down.replay()
     torch.cuda.synchronize()
     t0 = time.perf_counter()
     g_steps.replay()
     torch.cuda.synchronize()
     dt = time.perf_counter() - t0
     us = 1e3 * event_ms(g_gate.replay) / steps
+    us_d = 1e3 * event_ms(g_down.replay) / steps
     bg = topk * mx_expert_bytes(Ng, Kg) + Kg * 2 + topk * Ng * 2
     bd = topk * mx_expert_bytes(Nd, Kd) + topk * Kd * 2 + topk * Nd * 2
     return {"workload": "gpt-oss-20b mxfp4 decode gemv M=1 (gate_up [5760,2880] + down "
                         "[2880,2880], E=32, top-4)",
             "ms_per_step": 1e3 * dt / steps, "gbs": (bg + bd) * steps / dt / 1e9,
+            "gate_up_bytes_per_launch": bg, "down_bytes_per_launch": bd,
             "gate_up_us": us, "gate_up_gbs": bg / (us * 1e-6) / 1e9,
-            "gate_up_frac_hbm": bg / (us * 1e-6) / 1e9 / HBM_PEAK_GBS}
+            "gate_up_frac_hbm": bg / (us * 1e-6) / 1e9 / HBM_PEAK_GBS,
+            "down_us": us_d, "down_gbs": bd / (us_d * 1e-6) / 1e9}
 
 
 def decode_layer_nf4(dev, steps, warmup, M=1):
@@ -469,49 +547,80 @@ def dgrad(dev, steps, warmup, fmt="nf4"):
 
 
 # --------------------------------------------------------------------------
-def cpu_baseline(sample, budget_s):
-    """The oracle as it stands: decode of the active experts + float64
-    grouped matmul, for as many decode steps as fit in the time budget
-    (at least one).  BLAS is held to one thread, so ``cores`` is exact."""
-    import oracle
+def cpu_info():
+    model = "unknown"
     try:
-        from threadpoolctl import threadpool_limits
-    except ImportError:                      # pragma: no cover
-        threadpool_limits = None
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    model = line.split(":", 1)[1].strip()
+                    break
+    except OSError:
+        pass
+    return model
+
+
+def cpu_baseline(sample, budget_s, runs=3):
+    """The oracle as it stands: decode of the active experts + float64
+    grouped matmul over the timed decode steps, ``runs`` runs of about
+    budget_s / runs seconds each; the rate is the median over the runs.
+    BLAS gets every core this process may run on (capped by OMP_NUM_THREADS
+    where that is set: the host's CPU share); the oracle's decode itself is
+    NumPy element-wise work on one thread."""
+    import oracle
+    from threadpoolctl import threadpool_info, threadpool_limits
     E, topk = wl.QWEN["E"], wl.QWEN["topk"]
     (Ng, Kg), (Nd, Kd) = wl.QWEN["gate_up"], wl.QWEN["down"]
     x_bits = sample["x"].view(torch.int16).cpu().numpy().view(np.uint16)
     xd_bits = sample["xd"].view(torch.int16).cpu().numpy().view(np.uint16)
-    ctx = threadpool_limits(limits=1) if threadpool_limits else None
-    if ctx:
-        ctx.__enter__()
-    done, total_bytes, elapsed = 0, 0, 0.0
-    try:
-        for i, ids in enumerate(sample["ids"]):
+    affinity = len(os.sched_getaffinity(0))
+    share = int(os.environ.get("OMP_NUM_THREADS", affinity) or affinity)
+    threads = max(1, min(affinity, share))
+    host = {}                                # host copies of active experts (untimed)
+
+    def fetch(i, e):
+        key = (i % COPIES, e)
+        if key not in host:
             cg, ag = sample["banks_g"][i % COPIES]
             cd, ad = sample["banks_d"][i % COPIES]
-            active = sorted(set(ids.reshape(-1).tolist()))
-            host = {e: (cg[e].cpu().numpy(), ag[e].cpu().numpy(), cd[e].cpu().numpy(),
-                        ad[e].cpu().numpy()) for e in active}          # untimed host copy
-            t0 = time.perf_counter()
-            wg = {e: oracle.nf4_decode(host[e][0], host[e][1]) for e in active}
-            wd = {e: oracle.nf4_decode(host[e][2], host[e][3]) for e in active}
-            oracle.grouped_gemm(x_bits, lambda e: wg[e], ids, E)
-            oracle.grouped_gemm(xd_bits, lambda e: wd[e], ids.reshape(-1, 1), E)
-            elapsed += time.perf_counter() - t0
-            done += 1
-            d = len(active)
-            total_bytes += (d * (nf4_expert_bytes(Ng, Kg) + nf4_expert_bytes(Nd, Kd))
-                            + Kg * 2 + topk * Ng * 2 + topk * Kd * 2 + topk * Nd * 2)
-            if elapsed >= budget_s:
-                break
-    finally:
-        if ctx:
-            ctx.__exit__(None, None, None)
-    return {"value": total_bytes / elapsed / 1e9, "unit": "GB/s", "cores": 1, "kind": "oracle",
-            "sample": f"{done} of the timed decode steps (M=1, gate_up + down, 8 experts each): "
-                      f"NumPy NF4 decode of the active experts + float64 grouped matmul, "
-                      f"{elapsed:.1f} s on 1 core (BLAS limited to 1 thread)"}
+            host[key] = (cg[e].cpu().numpy(), ag[e].cpu().numpy(), cd[e].cpu().numpy(),
+                         ad[e].cpu().numpy())
+        return host[key]
+
+    steps = range(len(sample["ids"]))
+    rates, done_all, blas = [], 0, []
+    with threadpool_limits(limits=threads):
+        blas = [{k: d.get(k) for k in ("internal_api", "version", "num_threads",
+                                        "threading_layer")}
+                for d in threadpool_info() if d.get("user_api") == "blas"]
+        for _ in range(runs):
+            done, nbytes, elapsed = 0, 0, 0.0
+            for i in steps:
+                ids = sample["ids"][i]
+                active = sorted(set(ids.reshape(-1).tolist()))
+                h = {e: fetch(i, e) for e in active}
+                t0 = time.perf_counter()
+                wg = {e: oracle.nf4_decode(h[e][0], h[e][1]) for e in active}
+                wd = {e: oracle.nf4_decode(h[e][2], h[e][3]) for e in active}
+                oracle.grouped_gemm(x_bits, lambda e: wg[e], ids, E)
+                oracle.grouped_gemm(xd_bits, lambda e: wd[e], ids.reshape(-1, 1), E)
+                elapsed += time.perf_counter() - t0
+                done += 1
+                d = len(active)
+                nbytes += (d * (nf4_expert_bytes(Ng, Kg) + nf4_expert_bytes(Nd, Kd))
+                           + Kg * 2 + topk * Ng * 2 + topk * Kd * 2 + topk * Nd * 2)
+                if elapsed >= budget_s / runs:
+                    break
+            rates.append(nbytes / elapsed / 1e9)
+            done_all += done
+    used = max([b["num_threads"] or 1 for b in blas] + [1])
+    return {"value": float(np.median(rates)), "unit": "GB/s", "cores": used, "kind": "oracle",
+            "runs_gbs": [round(r, 4) for r in rates],
+            "cpu_model": cpu_info(), "affinity_cpus": affinity, "blas": blas,
+            "sample": f"median of {runs} runs over {done_all} timed decode steps in all (M=1, "
+                      f"gate_up + down, 8 experts each, about {budget_s / runs:.0f} s per run): "
+                      f"NumPy NF4 decode of the active experts + float64 grouped matmul, BLAS "
+                      f"on {used} threads"}
 
 
 def measured_traffic(kernel_key, algorithmic):
@@ -535,7 +644,14 @@ def traffic_bytes(t):
 
 
 def r4(d):
-    return {k: (round(v, 4) if isinstance(v, float) else v) for k, v in d.items()}
+    """Floats rounded to 4 decimals, recursively."""
+    if isinstance(d, float):
+        return round(d, 4)
+    if isinstance(d, dict):
+        return {k: r4(v) for k, v in d.items()}
+    if isinstance(d, (list, tuple)):
+        return [r4(v) for v in d]
+    return d
 
 
 def main():
@@ -563,8 +679,29 @@ def main():
     log("[bench] nf4 decode M=1")
     dec, sample = decode_nf4(dev, args.steps, args.warmup, M=1)
     log("[bench]", r4(dec))
-    ctl = controls(dev, int(dec["gate_up_bytes_per_launch"]))
-    log("[bench] controls", r4(ctl))
+    log("[bench] mxfp4 decode M=1")
+    dmx = decode_mx(dev, args.steps, args.warmup)
+    log("[bench]", r4(dmx))
+    # the four one-token launches: (name, algorithmic bytes, device us)
+    launches = [("nf4_gate_up", dec["gate_up_bytes_per_launch"], dec["gate_up_us"]),
+                ("nf4_down", dec["down_bytes_per_launch"], dec["down_us"]),
+                ("mxfp4_gate_up", dmx["gate_up_bytes_per_launch"], dmx["gate_up_us"]),
+                ("mxfp4_down", dmx["down_bytes_per_launch"], dmx["down_us"])]
+    log("[bench] controls")
+    ctl = controls(dev, [int(b) for _, b, _ in launches] + [140_000_000])
+    log("[bench] controls", ctl)
+    t0, bw = fit_line([b for _, b, _ in launches], [u for _, _, u in launches])
+    decode_fit = {
+        "model": "t = t0 + bytes / bw_eff, least squares over the four one-token GEMV launches",
+        "t0_us": t0, "bw_eff_gbs": bw, "bw_eff_frac_hbm": bw / HBM_PEAK_GBS,
+        "launches": [{"kernel": n, "bytes": round(b), "us": u,
+                      "gbs": b / (u * 1e-6) / 1e9, "frac_hbm": b / (u * 1e-6) / 1e9 / HBM_PEAK_GBS,
+                      "control_us": c["us"], "frac_of_control": c["us"] / u}
+                     for (n, b, u), c in zip(launches, ctl["stream"])]}
+    log("[bench] decode fit", decode_fit)
+    log("[bench] mfma rates")
+    rates = mfma_rates(dev)
+    log("[bench] mfma rates", rates)
     log("[bench] nf4 prefill M=4096")
     pre = prefill(dev, args.prefill_steps, args.prefill_warmup, "nf4")
     log("[bench]", r4(pre))
@@ -574,8 +711,7 @@ def main():
         d4, _ = decode_nf4(dev, args.steps, args.warmup, M=4)
         extra["nf4_decode_m4"] = {"workload": "qwen3-30b-a3b nf4 decode gemv M=4", **d4,
                                   "gate_up_frac_hbm": d4["gate_up_gbs"] / HBM_PEAK_GBS}
-        log("[bench] mxfp4 decode M=1")
-        extra["mxfp4_decode_m1"] = decode_mx(dev, args.steps, args.warmup)
+        extra["mxfp4_decode_m1"] = dmx
         log("[bench] mxfp4 prefill M=2048")
         mp = prefill(dev, args.prefill_steps, args.prefill_warmup, "mx")
         mp["workload"] = "gpt-oss-20b mxfp4 prefill M=2048 top-4 (bf16 MFMA on exact decode)"
@@ -624,7 +760,9 @@ def main():
                      "kernel": "grouped_gemv_kernel (NF4, gate_up, M=1)",
                      "bytes_per_launch": round(dec["gate_up_bytes_per_launch"]),
                      "avg_launch_us": round(dec["gate_up_us"], 3),
-                     "controls": r4(ctl)},
+                     "controls": ctl,
+                     "decode_fit": decode_fit},
+        "mfma_rates": rates,
         "cpu_baseline": r4(cpu),
         "prefill": {"workload": "qwen3-30b-a3b-shaped nf4 prefill, M=4096 tokens, top-8 Zipf(1.1) "
                                 "of E=128, router-weight scales: route sort + gate_up GEMM + "
@@ -644,7 +782,7 @@ def main():
                     "expert_rows_max_median_min": pre["expert_rows_max_median_min"]},
         "extra": extra,
     }
-    print(json.dumps(line), flush=True)
+    print(json.dumps(r4(line)), flush=True)
 
 
 if __name__ == "__main__":

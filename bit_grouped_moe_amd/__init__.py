@@ -239,6 +239,15 @@ def _scale(pair_scale, P):
     return pair_scale
 
 
+def _gemv_pairs(topk_ids, rows):
+    """Pair count of a decode GEMV call: ``topk_ids`` must be [rows, topk]
+    for the ``rows`` activation rows of x (the kernel reads pair p's row
+    p / topk and writes rows*topk output rows)."""
+    if topk_ids.dim() != 2 or topk_ids.shape[0] != rows:
+        raise ValueError(f"topk_ids must be [rows={rows}, topk] (got {tuple(topk_ids.shape)})")
+    return topk_ids.shape[0] * topk_ids.shape[1]
+
+
 def gq_nf4_grouped_gemv(x, codes, absmax, topk_ids, pair_scale=None, out=None):
     """Decode-time grouped GEMV (<= 256 pairs) on NF4 experts; returns bf16 [rows*topk, N]."""
     lib = load_library()
@@ -247,7 +256,7 @@ def gq_nf4_grouped_gemv(x, codes, absmax, topk_ids, pair_scale=None, out=None):
     if Kw != K:
         raise ValueError("x and codes disagree on K")
     _dev(topk_ids, "topk_ids", torch.int32, 2)
-    P = topk_ids.numel()
+    P = _gemv_pairs(topk_ids, rows)
     out = _out(out, P, N, x.device)
     st = lib.gq_nf4_grouped_gemv(_ptr(x), rows, K, xs, _ptr(codes), _ptr(absmax), E, N,
                                  _ptr(topk_ids), topk_ids.shape[1], _ptr(_scale(pair_scale, P)),
@@ -264,7 +273,7 @@ def gq_mxfp4_grouped_gemv(x, blocks, scales, topk_ids, pair_scale=None, out=None
     if Kw != K:
         raise ValueError("x and blocks disagree on K")
     _dev(topk_ids, "topk_ids", torch.int32, 2)
-    P = topk_ids.numel()
+    P = _gemv_pairs(topk_ids, rows)
     out = _out(out, P, N, x.device)
     st = lib.gq_mxfp4_grouped_gemv(_ptr(x), rows, K, xs, _ptr(blocks), _ptr(scales), E, N,
                                    _ptr(topk_ids), topk_ids.shape[1], _ptr(_scale(pair_scale, P)),
@@ -348,7 +357,7 @@ def gq_nf4_grouped_gemv_swiglu(x, codes, absmax, topk_ids, out=None):
     if Kw != K or N2 % 2:
         raise ValueError("x and codes disagree on K, or the gate_up width is odd")
     _dev(topk_ids, "topk_ids", torch.int32, 2)
-    P = topk_ids.numel()
+    P = _gemv_pairs(topk_ids, rows)
     out = _out(out, P, N2 // 2, x.device)
     st = lib.gq_nf4_grouped_gemv_swiglu(_ptr(x), rows, K, xs, _ptr(codes), _ptr(absmax), E, N2,
                                         _ptr(topk_ids), topk_ids.shape[1], _ptr(out), _stream(x))

@@ -30,8 +30,8 @@ identities, a library routine for bf16 rounding).  No function here is
 """
 
 from .bf16 import f32_to_bf16_rne, bf16_to_f32  # noqa: F401
-from .nf4 import NF4_CODEBOOK, nf4_pack, nf4_decode, nf4_decode_rows  # noqa: F401
-from .mxfp4 import E2M1_VALUES, e2m1_value, mxfp4_pack, mxfp4_decode, mxfp4_decode_rows  # noqa: F401
+from .nf4 import NF4_CODEBOOK, nf4_pack, nf4_decode  # noqa: F401
+from .mxfp4 import E2M1_VALUES, e2m1_value, mxfp4_pack, mxfp4_decode  # noqa: F401
 from .route import route_sort  # noqa: F401
 from .grouped import (  # noqa: F401
     grouped_gemm,

@@ -33,7 +33,7 @@ specification v1.0 supplies the format definitions):
 
 import numpy as np
 
-__all__ = ["E2M1_VALUES", "e2m1_value", "mxfp4_pack", "mxfp4_decode", "mxfp4_decode_rows",
+__all__ = ["E2M1_VALUES", "e2m1_value", "mxfp4_pack", "mxfp4_decode",
            "MX_BLOCK"]
 
 MX_BLOCK = 32
@@ -116,8 +116,3 @@ def mxfp4_decode(blocks, scales):
         out32 = out.astype(np.float32)
     return out32.reshape(blocks.shape[:-2] + (blocks.shape[-2] * 32,))
 
-
-def mxfp4_decode_rows(blocks, scales, rows):
-    """Decode only the listed rows (for sampled checks at large sizes)."""
-    rows = np.asarray(rows)
-    return mxfp4_decode(blocks[rows], scales[rows])

@@ -32,7 +32,7 @@ Readings taken where the pages are silent:
 
 import numpy as np
 
-__all__ = ["NF4_CODEBOOK", "NF4_BLOCK", "nf4_pack", "nf4_decode", "nf4_decode_rows"]
+__all__ = ["NF4_CODEBOOK", "NF4_BLOCK", "nf4_pack", "nf4_decode"]
 
 NF4_BLOCK = 64
 
@@ -107,8 +107,3 @@ def nf4_decode(packed, absmax):
     a = np.repeat(absmax, NF4_BLOCK, axis=1)                          # float32
     return (q * a).astype(np.float32)                                 # fp32 RNE multiply
 
-
-def nf4_decode_rows(packed, absmax, rows):
-    """Decode only the listed rows (for sampled checks at large sizes)."""
-    rows = np.asarray(rows)
-    return nf4_decode(packed[rows], absmax[rows])

@@ -86,6 +86,25 @@ def assert_slices(y_gpu_f32, y_ref, pair_expert, E, experts=None):
     return worst
 
 
+def assert_rows(y_gpu_f32, y_ref, tol=None, what=""):
+    """Per-row relative L2 <= tol (default: the per-slice tolerance) for
+    every row of a checked set; a row whose reference is exactly zero must
+    be exactly zero.  A single wrong row in a large expert slice barely
+    moves the slice error; this catches it."""
+    tol = oracle.REL_L2_TOL if tol is None else tol
+    y_ref = np.asarray(y_ref, dtype=np.float64)
+    d = np.asarray(y_gpu_f32, dtype=np.float64) - y_ref
+    nr = np.linalg.norm(y_ref, axis=1)
+    nd = np.linalg.norm(d, axis=1)
+    zero = nr == 0.0
+    assert not np.any(nd[zero]), f"{what}: rows {np.nonzero(zero & (nd > 0))[0][:8]} should be 0"
+    err = nd[~zero] / nr[~zero]
+    worst = float(err.max()) if err.size else 0.0
+    assert worst <= tol, (f"{what}: per-row rel-L2 {worst} above {tol} "
+                          f"(row {np.nonzero(~zero)[0][int(err.argmax())]})")
+    return worst
+
+
 def plus_zero(bits):
     """bf16 bit patterns with -0 mapped to +0.  A one-hot probe multiplies a
     decoded weight by 1 and adds zero products: IEEE round-to-nearest gives

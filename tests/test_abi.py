@@ -175,7 +175,8 @@ def test_probe_library_exports_its_header():
     text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
     names = sorted(set(re.findall(r"\b(gq_probe_[a-z0-9_]+)\s*\(", text)))
     plib = ctypes.CDLL(path)
-    assert names == ["gq_probe_copy", "gq_probe_empty", "gq_probe_stream_read"]
+    assert names == ["gq_probe_copy", "gq_probe_empty", "gq_probe_mfma", "gq_probe_mfma_flops",
+                     "gq_probe_mfma_per_wave_iter", "gq_probe_stream_read"]
     for n in names:
         assert hasattr(plib, n), n
     plib.gq_probe_copy.argtypes = [ctypes.c_void_p, ctypes.c_void_p, ctypes.c_int64,
@@ -215,3 +216,14 @@ def test_epilogue_entry_points_reject(lib):
     assert lib.gq_moe_combine(F, 4, 8, 2048, 2040, NULL, F, None) == INVALID
     assert lib.gq_moe_combine(F2, 4, 8, 2048, 2048, NULL, F, None) == INVALID
     assert lib.gq_moe_combine(NULL, 0, 8, 2048, 2048, NULL, NULL, None) == 0
+
+
+def test_gemv_pair_count_requires_matching_rows():
+    """The decode GEMV wrappers take the pair count from topk_ids [rows, topk]
+    and reject a topk_ids whose row count differs from x's (checked on the
+    host, before any launch)."""
+    import torch
+    assert gq._gemv_pairs(torch.zeros((4, 8), dtype=torch.int32), 4) == 32
+    for shape in ((3, 8), (5, 8), (32,), (4, 8, 1)):
+        with pytest.raises(ValueError):
+            gq._gemv_pairs(torch.zeros(shape, dtype=torch.int32), 4)

@@ -11,7 +11,7 @@ import torch
 import bit_grouped_moe_amd as gq
 import oracle
 import workloads as wl
-from tests.gpu_common import (LazyDecoded, plus_zero,
+from tests.gpu_common import (LazyDecoded, plus_zero, assert_rows,
                               assert_slices, bf16_bits, bf16_to_host_f32, device,
                               packed_mx_bank, packed_nf4_bank, say, to_dev, to_dev_bf16)
 
@@ -97,15 +97,18 @@ def test_tile_boundaries(fmt, K):
 
 @pytest.mark.parametrize("fmt,K,N", [("nf4", 1088, 320), ("mx", 1056, 288), ("nf4", 2048, 512)])
 def test_narrow_tile_edges(fmt, K, N):
-    """K >= 1024: tiles of at most 128 rows take the column-per-wave layout,
-    longer ones the 2 x 2 layout.  Segments of 128 and 129 rows, 384 and 385
-    (a full tile then 128 or 129 rows), 32, 33, 97 and 1, an empty expert,
-    dropped pairs; N ends inside a 256-column tile (a column tile whose
-    last waves own no columns)."""
+    """K >= 1024: the 256-column kernel runs tiles of at most 128 rows with
+    4 sub-tiles per wave (each wave loads its own 32 rows) and longer tiles
+    with 8 (8-row groups dealt round-robin to the waves), each specialised
+    per count of active 32-row sub-tiles.  Segments of 128 and 129 rows, 384
+    and 385 (a full tile then 128 or 129 rows), 161, 192 and 224 (6 and 7
+    active sub-tiles), 32, 33, 97 and 1, an empty expert, dropped pairs; N
+    ends inside a 256-column tile (a column tile whose last waves own no
+    columns)."""
     dev = device()
     g = np.random.default_rng(K + N)
-    E = 10
-    sizes = [128, 129, 384, 385, 32, 33, 97, 1, 0, 64]
+    E = 13
+    sizes = [128, 129, 384, 385, 32, 33, 97, 1, 0, 64, 161, 192, 224]
     ids = np.concatenate([np.full(n, e, dtype=np.int32) for e, n in enumerate(sizes)]
                          + [np.full(5, -1, dtype=np.int32)])
     ids = g.permutation(ids).reshape(-1, 1)
@@ -173,23 +176,44 @@ def test_qwen_prefill_full_shapes(proj):
             sc.reshape(-1)[rows].astype(np.float64)[:, None]
         err = np.linalg.norm(yg[rows] - ref) / np.linalg.norm(ref)
         assert err <= oracle.REL_L2_TOL, (e, err)
+        assert_rows(yg[rows], ref, what=f"expert {e}")
 
 
-def test_gptoss_prefill_full_shapes():
+@pytest.mark.parametrize("proj", ["gate_up", "down"])
+def test_gptoss_prefill_full_shapes(proj):
+    """gpt-oss-20b MXFP4 at M = 2048 tokens, top-4 uniform over 32 experts:
+    gate_up [5760, 2880] in gather mode and down [2880, 2880] in flatten
+    mode (8192 pairs, router-weight scales; its last 64-column tile is the
+    guarded one), as the bench launches them.  Three sampled experts are
+    checked per slice and per row, and a few dropped pairs must give zero
+    rows."""
     dev = device()
     E, topk = wl.GPTOSS["E"], wl.GPTOSS["topk"]
-    N, K = wl.GPTOSS["gate_up"]
+    N, K = wl.GPTOSS[proj]
     M = 2048
-    blocks, scales = wl.random_mxfp4_bank(E, N, K, dev, seed=4000)
+    blocks, scales = wl.random_mxfp4_bank(E, N, K, dev, seed=4000 if proj == "gate_up" else 4001)
     ids = wl.route_uniform(wl.rng(wl.CFG_GPTOSS, wl.S_ROUTE), M, E, topk)
-    x = wl.draw_bf16(wl.rng(wl.CFG_GPTOSS, wl.S_X), (M, K))
-    say("gemm gpt-oss prefill")
-    out = _gemm("mx", x, blocks, scales, ids, E, dev)
+    sc = None
+    if proj == "down":
+        sc = wl.router_weights(wl.rng(wl.CFG_GPTOSS, wl.S_LOGITS), M, topk).reshape(-1, 1)
+        ids = ids.reshape(-1, 1)
+    ids = ids.copy()
+    drop = np.random.default_rng(41).choice(ids.size, 37, replace=False)
+    ids.reshape(-1)[drop] = -1
+    x = wl.draw_bf16(wl.rng(wl.CFG_GPTOSS, wl.S_X if proj == "gate_up" else wl.S_DOWN_IN),
+                     (ids.shape[0], K))
+    say("gemm gpt-oss prefill", proj)
+    out = _gemm("mx", x, blocks, scales, ids, E, dev, sc)
     W = LazyDecoded("mx", blocks.cpu().numpy(), scales.cpu().numpy())
     check = [0, 17, 31]
-    ref = oracle.grouped_gemm(x, lambda e: W(e) if e in check else np.zeros((N, K), np.float32),
-                              ids, E)
-    assert_slices(bf16_to_host_f32(out), ref, ids, E, experts=check)
+    # the oracle on the sampled experts only (other pairs dropped there)
+    ref = oracle.grouped_gemm(x, W, np.where(np.isin(ids, check), ids, -1), E, pair_scale=sc)
+    yg = bf16_to_host_f32(out)
+    assert_slices(yg, ref, ids, E, experts=check)
+    flat = ids.reshape(-1)
+    rows = np.nonzero(np.isin(flat, check))[0]
+    assert_rows(yg[rows], ref[rows], what="sampled experts")
+    assert not np.any(yg[drop]), "dropped pairs must give zero rows"
 
 
 def test_deterministic_and_route_reuse():

@@ -46,15 +46,14 @@ def test_tiny_gather(fmt, rows):
         assert_slices(bf16_to_host_f32(out), ref, ids, E)
 
 
-@pytest.mark.parametrize("fmt", ["nf4", "mx"])
-@pytest.mark.parametrize("K", [64, 128, 256, 1024, 4096, 8192, 192, 96])
+@pytest.mark.parametrize("fmt,K", [(f, k) for f in ("nf4", "mx")
+                                   for k in (64, 128, 256, 1024, 4096, 8192, 192, 96)
+                                   if f == "mx" or k % 64 == 0])
 def test_k_sweep(fmt, K):
     """Every in-wave reduction width (K/32 segments = 2 .. 64 lanes), the
     cross-wave path (K = 4096, and K = 8192, the longest row the GEMV
     takes), and segment counts that do not divide a wave (K = 96, 192:
     several rows per thread in the cross-wave reduction)."""
-    if fmt == "nf4" and K % 64:
-        pytest.skip("NF4 needs K % 64 == 0")
     dev = device()
     g = wl.rng(wl.CFG_TINY, 300 + K)
     E, N, topk, rows = 3, 160, 2, 2
@@ -189,3 +188,25 @@ def test_deterministic():
     b = gq.gq_nf4_grouped_gemv(x, codes, absmax, ids)
     torch.cuda.synchronize()
     assert torch.equal(a.view(torch.int16), b.view(torch.int16))
+
+
+@pytest.mark.parametrize("fmt", ["nf4", "mx"])
+def test_rows_of_x_and_topk_ids_must_agree(fmt):
+    """x with more (or fewer) rows than topk_ids is rejected before any
+    launch: the kernel would read topk_ids past its end (or leave output
+    rows unwritten)."""
+    dev = device()
+    g = wl.rng(wl.CFG_TINY, 900)
+    E, N, K = 4, 64, 128
+    bank = packed_nf4_bank(g, E, N, K) if fmt == "nf4" else packed_mx_bank(g, E, N, K)
+    a, b = to_dev(bank[0], dev), to_dev(bank[1], dev)
+    fn = gq.gq_nf4_grouped_gemv if fmt == "nf4" else gq.gq_mxfp4_grouped_gemv
+    ids = to_dev(wl.route_uniform(g, 2, E, 2), dev)
+    for rows in (1, 3):
+        x = to_dev_bf16(wl.draw_bf16(g, (rows, K)), dev)
+        with pytest.raises(ValueError):
+            fn(x, a, b, ids)
+    if fmt == "nf4":
+        x = to_dev_bf16(wl.draw_bf16(g, (3, K)), dev)
+        with pytest.raises(ValueError):
+            gq.gq_nf4_grouped_gemv_swiglu(x, a, b, ids)
