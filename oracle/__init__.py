@@ -19,6 +19,10 @@ Each function cites the web page (by title) and the section it follows:
 * "flashrt/grouped-moe-gemv" -- section "Functions" (routing tensor and
   output layout conventions).
 
+``fp8`` holds the e4m3 element format and the two-term activation split
+that the block-scaled fp4 matmul path uses (a reading: the pages keep the
+activations in bf16; see that module's docstring).
+
 Where the pages are silent the reading taken is stated in the docstring of
 the function concerned.
 
@@ -32,6 +36,8 @@ identities, a library routine for bf16 rounding).  No function here is
 from .bf16 import f32_to_bf16_rne, bf16_to_f32  # noqa: F401
 from .nf4 import NF4_CODEBOOK, nf4_pack, nf4_decode  # noqa: F401
 from .mxfp4 import E2M1_VALUES, e2m1_value, mxfp4_pack, mxfp4_decode  # noqa: F401
+from .fp8 import (E4M3_VALUES, e4m3_value, e4m3_rne, block_scale_exponent,  # noqa: F401
+                  act_split_e4m3, act_split_value)
 from .route import route_sort  # noqa: F401
 from .grouped import (  # noqa: F401
     grouped_gemm,
