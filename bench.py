@@ -53,6 +53,7 @@ import workloads as wl  # noqa: E402
 
 HBM_PEAK_GBS = 8000.0            # MI355X HBM3E
 BF16_PEAK_TFLOPS = 2516.6        # MI355X dense bf16 MFMA
+FP8_PEAK_TFLOPS = 5033.0         # MI355X dense fp8 MFMA
 FP4_PEAK_TFLOPS = 10066.0        # MI355X dense fp4 MFMA
 COPIES = 16                      # independent bank copies rotated per step
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic_counters.json")
@@ -505,6 +506,66 @@ def prefill(dev, steps, warmup, fmt):
     }
 
 
+def prefill_mx_scaled(dev, steps, warmup):
+    """gpt-oss MXFP4 prefill (M=2048 uniform top-4) on the block-scaled fp4
+    matrix instruction: route sort + activation split + gate_up GEMM +
+    split of the down input + down GEMM per step (eager)."""
+    cfgd, M, cfg = wl.GPTOSS, 2048, wl.CFG_GPTOSS
+    E, topk = cfgd["E"], cfgd["topk"]
+    (Ng, Kg), (Nd, Kd) = cfgd["gate_up"], cfgd["down"]
+    P = M * topk
+    route = wl.route_uniform(wl.rng(cfg, wl.S_ROUTE), M, E, topk)
+    a_g, b_g = wl.random_mxfp4_bank(E, Ng, Kg, dev, seed=30)
+    a_d, b_d = wl.random_mxfp4_bank(E, Nd, Kd, dev, seed=300)
+    ids = torch.from_numpy(route).to(dev)
+    sc = torch.from_numpy(wl.router_weights(wl.rng(cfg, wl.S_LOGITS), M, topk)).to(dev)
+    x = bf16_dev(wl.draw_bf16(wl.rng(cfg, wl.S_X), (M, Kg)), dev)
+    xd = bf16_dev(wl.draw_bf16(wl.rng(cfg, wl.S_DOWN_IN), (P, Kd)), dev)
+    out_g = torch.empty((P, Ng), dtype=torch.bfloat16, device=dev)
+    out_d = torch.empty((P, Nd), dtype=torch.bfloat16, device=dev)
+    cs, ss = gq.split_sizes(M, Kg)
+    sx = (torch.empty(cs, dtype=torch.uint8, device=dev), torch.empty(ss, dtype=torch.uint8, device=dev))
+    cs, ss = gq.split_sizes(P, Kd)
+    sxd = (torch.empty(cs, dtype=torch.uint8, device=dev), torch.empty(ss, dtype=torch.uint8, device=dev))
+    t_sg, t_g, t_sd, t_d = Timer(), Timer(), Timer(), Timer()
+
+    def run(timed):
+        r = gq.gq_route_sort(ids, E)
+        rd = r._replace(rows=P, topk=1)
+        ev = t_sg.start() if timed else None
+        gq.gq_act_split_e4m3(x, *sx)
+        if timed:
+            t_sg.stop(ev)
+            ev = t_g.start()
+        gq.gq_mxfp4_grouped_gemm_scaled(sx, a_g, b_g, r, pair_scale=sc, out=out_g)
+        if timed:
+            t_g.stop(ev)
+            ev = t_sd.start()
+        gq.gq_act_split_e4m3(xd, *sxd)
+        if timed:
+            t_sd.stop(ev)
+            ev = t_d.start()
+        gq.gq_mxfp4_grouped_gemm_scaled(sxd, a_d, b_d, rd, pair_scale=sc, out=out_d)
+        if timed:
+            t_d.stop(ev)
+
+    dt = eager_steps(run, steps, warmup) * steps
+    fg, fd = 2.0 * P * Ng * Kg, 2.0 * P * Nd * Kd
+    ug, ud = t_g.avg_us(), t_d.avg_us()
+    return {"workload": "gpt-oss-20b mxfp4 prefill M=2048 top-4 on the block-scaled fp4 matrix "
+                        "instruction (e2m1 weights as stored x two-term e4m3 split of the "
+                        "activations): route sort + split + gate_up + split + down",
+            "ms_per_step": 1e3 * dt / steps, "tflops": (fg + fd) * steps / dt / 1e12,
+            "gate_up_us": ug, "down_us": ud, "split_gate_up_us": t_sg.avg_us(),
+            "split_down_us": t_sd.avg_us(),
+            "gate_up_tflops": fg / (ug * 1e-6) / 1e12, "down_tflops": fd / (ud * 1e-6) / 1e12,
+            "gate_up_frac_bf16_peak": fg / (ug * 1e-6) / 1e12 / BF16_PEAK_TFLOPS,
+            # two e4m3 x e2m1 instructions per useful product: issued flops are twice the
+            # useful ones, against the fp8 x fp4 (fp8-rate) peak
+            "gate_up_issued_frac_fp8_peak": 2 * fg / (ug * 1e-6) / 1e12 / FP8_PEAK_TFLOPS,
+            "gate_up_frac_fp4_peak": fg / (ug * 1e-6) / 1e12 / FP4_PEAK_TFLOPS}
+
+
 def dgrad(dev, steps, warmup, fmt="nf4"):
     """Input gradient of both projections: Qwen3 NF4 (M=2048 top-8) or
     gpt-oss MXFP4 (M=2048 top-4), eager."""
@@ -718,6 +779,10 @@ def main():
         mp["gate_up_frac_bf16_peak"] = mp["gate_up_tflops"] / BF16_PEAK_TFLOPS
         mp["gate_up_frac_fp4_peak"] = mp["gate_up_tflops"] / FP4_PEAK_TFLOPS
         extra["mxfp4_prefill_m2048"] = mp
+        log("[bench] mxfp4 prefill M=2048 (block-scaled fp4 instruction)")
+        extra["mxfp4_prefill_m2048_scaled"] = prefill_mx_scaled(dev, args.prefill_steps,
+                                                                args.prefill_warmup)
+        log("[bench]", r4(extra["mxfp4_prefill_m2048_scaled"]))
         log("[bench] nf4 moe layer decode M=1")
         extra["nf4_moe_layer_decode_m1"] = decode_layer_nf4(dev, args.steps, args.warmup)
         log("[bench] nf4 moe layer prefill M=4096")

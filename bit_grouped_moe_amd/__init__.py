@@ -22,7 +22,7 @@ __all__ = [
     "gq_nf4_grouped_gemv", "gq_mxfp4_grouped_gemv", "gq_nf4_grouped_gemm",
     "gq_mxfp4_grouped_gemm", "gq_nf4_grouped_dgrad", "gq_mxfp4_grouped_dgrad",
     "gq_nf4_grouped_gemv_swiglu", "gq_nf4_grouped_gemm_swiglu", "gq_nf4_grouped_gemv_down_combine",
-    "gq_moe_combine", "Route",
+    "gq_moe_combine", "gq_act_split_e4m3", "gq_mxfp4_grouped_gemm_scaled", "Route",
 ]
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
@@ -33,7 +33,7 @@ EXPORTED_SYMBOLS = (
     "gq_mxfp4_decode", "gq_nf4_grouped_gemv", "gq_mxfp4_grouped_gemv", "gq_nf4_grouped_gemm",
     "gq_mxfp4_grouped_gemm", "gq_nf4_grouped_dgrad", "gq_mxfp4_grouped_dgrad",
     "gq_nf4_grouped_gemv_swiglu", "gq_nf4_grouped_gemm_swiglu", "gq_nf4_grouped_gemv_down_combine",
-    "gq_moe_combine",
+    "gq_moe_combine", "gq_act_split_e4m3", "gq_mxfp4_grouped_gemm_scaled",
 )
 
 _i32, _i64, _p = ctypes.c_int32, ctypes.c_int64, ctypes.c_void_p
@@ -62,6 +62,9 @@ _SIGNATURES = {
     "gq_nf4_grouped_gemv_down_combine": (ctypes.c_int, [_p, _i32, _i32, _i64, _p, _p, _i32, _i32,
                                                         _p, _i32, _p, _p, _p]),
     "gq_moe_combine": (ctypes.c_int, [_p, _i32, _i32, _i32, _i64, _p, _p, _p]),
+    "gq_act_split_e4m3": (ctypes.c_int, [_p, _i32, _i32, _i64, _p, _p, _p]),
+    "gq_mxfp4_grouped_gemm_scaled": (ctypes.c_int, [_p, _p, _i32, _i32, _p, _p, _i32, _i32, _i32,
+                                                    _p, _p, _p, _p, _p, _i32, _i32, _p, _p]),
 }
 
 _lib = None
@@ -420,4 +423,55 @@ def gq_moe_combine(y_pairs, topk, topk_weights=None, out=None):
     st = lib.gq_moe_combine(_ptr(y_pairs), rows, topk, H, ys,
                             _ptr(_weights(topk_weights, rows, topk)), _ptr(out), _stream(y_pairs))
     _check(st, "gq_moe_combine")
+    return out
+
+
+# ---- MXFP4 on the block-scaled fp4 matrix instruction ------------------------
+def split_sizes(rows, K):
+    """Byte shapes of gq_act_split_e4m3's outputs for x [rows, K]:
+    (codes [rows, 2*Kp], scales [rows, Kp/16]) with Kp = K rounded up to 64."""
+    kp = (K + 63) // 64 * 64
+    return (rows, 2 * kp), (rows, kp // 16)
+
+
+def gq_act_split_e4m3(x, codes=None, scales=None):
+    """Two-term e4m3 split of bf16 activations x [rows, K]; returns the
+    (codes, scales) uint8 tensors gq_mxfp4_grouped_gemm_scaled takes."""
+    lib = load_library()
+    rows, K, xs = _x_args(x)
+    cshape, sshape = split_sizes(rows, K)
+    if codes is None:
+        codes = torch.empty(cshape, dtype=torch.uint8, device=x.device)
+    if scales is None:
+        scales = torch.empty(sshape, dtype=torch.uint8, device=x.device)
+    _dev(codes, "codes", torch.uint8)
+    _dev(scales, "scales", torch.uint8)
+    if tuple(codes.shape) != cshape or tuple(scales.shape) != sshape:
+        raise ValueError(f"split buffers must be {cshape} and {sshape}")
+    st = lib.gq_act_split_e4m3(_ptr(x), rows, K, xs, _ptr(codes), _ptr(scales), _stream(x))
+    _check(st, "gq_act_split_e4m3")
+    return codes, scales
+
+
+def gq_mxfp4_grouped_gemm_scaled(x_split, blocks, scales, route, pair_scale=None, out=None):
+    """Prefill grouped GEMM on MXFP4 experts through the block-scaled fp4
+    instruction; ``x_split`` = gq_act_split_e4m3(x) for x [rows, K]."""
+    lib = load_library()
+    xq, xsc = x_split
+    _dev(xq, "x_split codes", torch.uint8, 2)
+    _dev(xsc, "x_split scales", torch.uint8, 2)
+    E, N, K = _mx_bank(blocks, scales)
+    rows = xq.shape[0]
+    cshape, sshape = split_sizes(rows, K)
+    if tuple(xq.shape) != cshape or tuple(xsc.shape) != sshape:
+        raise ValueError("x_split does not match the weights' K")
+    if route.rows != rows or route.num_experts != E:
+        raise ValueError("x_split and route disagree")
+    P = rows * route.topk
+    out = _out(out, P, N, xq.device)
+    st = lib.gq_mxfp4_grouped_gemm_scaled(_ptr(xq), _ptr(xsc), rows, K, _ptr(blocks),
+                                          _ptr(scales), E, N, route.topk,
+                                          _ptr(_scale(pair_scale, P)), *_route_ptrs(route),
+                                          _ptr(out), _stream(xq))
+    _check(st, "gq_mxfp4_grouped_gemm_scaled")
     return out

@@ -35,43 +35,16 @@
 #include <type_traits>
 #include <utility>
 
+#include "gemm_common.hpp"
 #include "gq_device.hpp"
 #include "gq_host.hpp"
 #include "../../include/gq.h"
 
 namespace gq {
 
-constexpr int kTM = 256;          // tile rows (routed pairs)
 constexpr int kTN = 128;          // tile columns (output features)
-constexpr int kTK = 64;           // contraction per step
-constexpr int kGemmThreads = 256;
 constexpr int kBStride = 72;      // bf16 per LDS row of B (64 + 8 pad: conflict-free 16-B reads)
 constexpr int kCStride = 64;      // bytes per LDS row of raw codes (dgrad staging)
-
-// kFwdNF4Glu: NF4 forward on a fused gate_up weight (gate rows [0, I), up
-// rows [I, 2I)) whose epilogue writes SwiGLU(gate, up) = silu(gate) * up.
-enum BMode { kFwdNF4 = 0, kFwdMX = 1, kDgradNF4 = 2, kDgradMX = 3, kFwdNF4Glu = 4 };
-
-struct GemmArgs {
-  const uint16_t* x;           // activations (forward) or output gradient (dgrad)
-  int64_t x_stride;            // elements
-  const uint8_t* codes;        // [E, Nw, Kw/2]
-  const void* scl;             // NF4 absmax float [E, Nw, Kw/64] / MXFP4 e8m0 [E, Nw, Kw/32]
-  int Nw, Kw;                  // expert weight shape [Nw, Kw]
-  int Kc;                      // contraction length (Kw forward, Nw dgrad)
-  int Nout;                    // output columns (Nw forward, Kw dgrad)
-  int E, topk, P;
-  const float* pair_scale;
-  const int32_t* offsets;
-  const int32_t* sorted_pairs;
-  const int32_t* tiles;
-  const int32_t* num_tiles;
-  int n_col_tiles;             // ceil(Nout / kTN)
-  int n_logical;               // max_tiles * n_col_tiles
-  uint16_t* out;               // [P, Nout]
-};
-
-__device__ __forceinline__ bf16x8 as_bf16x8(u32x4 v) { return __builtin_bit_cast(bf16x8, v); }
 
 // ---- B producers: fill Bs[col][k] (bf16, row stride kBStride) for step ks ----
 
@@ -239,30 +212,6 @@ __device__ __forceinline__ void dg_decode_chunk(const DgCodes& R, const float* A
   *reinterpret_cast<u32x4*>(Bs + (j4 * 4 + c) * kBStride + r8 * 8) = v;
 }
 
-// Epilogue shared by the forward and dgrad kernels.  A transposed
-// accumulator block (32 columns x 32 rows, weights as the first MFMA
-// operand) gives lane (lr, lh) the row lr of the sub-tile at columns
-// 8q + 4 lh + [0, 4), q = r / 4.  The lane scales by its row's pair weight,
-// rounds to bf16 and swaps half of its words with the partner lane 32 away
-// (v_permlane32_swap), after which each lane holds 8 consecutive columns and
-// writes them as one 16-byte piece of the output row.
-__device__ __forceinline__ void store_block_t(const float (&v)[16], uint16_t* orow, int lh) {
-  uint32_t w[4][2];                                        // columns 8q + 4 lh + [0, 4)
-#pragma unroll
-  for (int q = 0; q < 4; ++q) {
-    w[q][0] = pack_bf16x2(v[4 * q], v[4 * q + 1]);
-    w[q][1] = pack_bf16x2(v[4 * q + 2], v[4 * q + 3]);
-  }
-#pragma unroll
-  for (int jp = 0; jp < 2; ++jp) {
-    // after the swap: lane half 0 holds columns 16 jp + [0, 8), half 1
-    // columns 16 jp + [8, 16)
-    const auto s0 = __builtin_amdgcn_permlane32_swap(w[2 * jp][0], w[2 * jp + 1][0], false, false);
-    const auto s1 = __builtin_amdgcn_permlane32_swap(w[2 * jp][1], w[2 * jp + 1][1], false, false);
-    *reinterpret_cast<u32x4*>(orow + 16 * jp + 8 * lh) = u32x4{s0[0], s1[0], s0[1], s1[1]};
-  }
-}
-
 // Rows of sub-tiles ms0, ms1 (32 rows each) for the 128 B columns of a
 // 256 x 128 tile (SwiGLU: 64 outputs from gate blocks 0, 1 and up blocks 2, 3).
 template <bool kGlu, int kTNo>
@@ -317,40 +266,9 @@ __device__ __forceinline__ void grouped_gemm_body(const GemmArgs& g) {
   __shared__ float lut[16];
 
   const int tid = threadIdx.x;
-  // XCD-aware block -> logical tile mapping (see file comment).
-  const int C = g.n_col_tiles;
-  const int bid = blockIdx.x;
-  const int q = bid >> 3, xcd = bid & 7;
-  const int logical = (q / C) * (8 * C) + xcd * C + (q % C);
-  if (logical >= g.n_logical) return;
-  const int tile = logical / C;
-  const int n0 = (logical % C) * kTNo;
-  const int T = *g.num_tiles;
-
-  if (tile >= T) {
-    // Zero the rows of dropped pairs (ids outside [0, E)), columns [n0, n0+128).
-    const int dstart = g.offsets[g.E] + (tile - T) * kTM;
-    if (dstart >= g.P) return;
-    if (dstart < 0) return;
-    const int dvalid = min(kTM, g.P - dstart);
-    for (int idx = tid; idx < dvalid * (kTNo / 8); idx += kGemmThreads) {
-      const int r = idx / (kTNo / 8), c8 = idx % (kTNo / 8);
-      const int col = n0 + c8 * 8;
-      const int p = g.sorted_pairs[dstart + r];
-      if (col < g.Nout && (unsigned)p < (unsigned)g.P) {
-        *reinterpret_cast<u32x4*>(g.out + (int64_t)p * g.Nout + col) = u32x4{0u, 0u, 0u, 0u};
-      }
-    }
-    return;
-  }
-
-  const int e = g.tiles[2 * tile];
-  const int start = g.tiles[2 * tile + 1];
-  // A tile list that does not come from gq_route_sort must not make the
-  // kernel read outside its buffers: reject entries that cannot be valid.
-  if ((unsigned)e >= (unsigned)g.E || (unsigned)start >= (unsigned)g.P) return;
-  const int valid = min(kTM, min(g.offsets[e + 1], g.P) - start);
-  if (valid <= 0) return;
+  TileInfo ti;
+  if (!tile_head<kTNo>(g, tid, ti)) return;
+  const int e = ti.e, start = ti.start, valid = ti.valid, n0 = ti.n0;
   for (int r = tid; r < kTM; r += kGemmThreads) {
     int p = g.sorted_pairs[start + min(r, valid - 1)];
     p = ((unsigned)p < (unsigned)g.P) ? p : 0;
@@ -605,10 +523,6 @@ __global__ __launch_bounds__(kGemmThreads, 2) void grouped_gemm_fwd_shortk_kerne
 // ---- forward kernel: 256 x 256 output tile, one wave per SIMD ----
 // Workgroup = 4 waves on one CU (256 accumulator registers per lane, ~70 KB
 // of LDS); the tile loop is fwd_columns below.
-constexpr int kXN = 256;                                  // B columns per tile
-
-typedef __attribute__((address_space(3))) void lds_void_t;
-typedef __attribute__((address_space(1))) const void glb_void_t;
 
 // Instruction interleave for one K slice of kM MFMAs: after each MFMA, an
 // even share of the slice's LDS reads, VALU ops and LDS writes, so that the
@@ -652,37 +566,6 @@ __device__ __forceinline__ void sched_slice() {
 // wave runs (active sub-tiles) x 2 v_mfma_f32_32x32x16_bf16, interleaved
 // (NF4) with its fragment reads, table reads and decode VALU work.
 // The SwiGLU epilogue combines blocks 0 and 1, which sit in the same lanes.
-constexpr int kNarrowRows = 128;                           // tiles up to here: 4 sub-tiles
-
-struct NLoad {
-  u32x4 c[2];      // 32 codes of column blocks 0 and 1
-  float a[2];      // NF4 absmax
-  uint32_t s[2];   // MXFP4 scale bytes
-};
-
-template <int kMode>
-__device__ __forceinline__ NLoad n_load(const GemmArgs& g, int e, int jcol, int ks, int half) {
-  NLoad L;
-  const int k0 = ks * kTK;
-#pragma unroll
-  for (int cb = 0; cb < 2; ++cb) {
-    int n;
-    if constexpr (kMode == kFwdNF4Glu) n = min(jcol, g.Nout - 1) + (cb ? g.Nout : 0);
-    else n = min(jcol + 32 * cb, g.Nw - 1);
-    const size_t row = (size_t)e * g.Nw + n;
-    L.c[cb] = *reinterpret_cast<const u32x4*>(g.codes + row * (size_t)(g.Kw / 2) + k0 / 2 +
-                                              16 * half);
-    if constexpr (kMode == kFwdMX) {
-      L.s[cb] = static_cast<const uint8_t*>(g.scl)[row * (size_t)(g.Kw / 32) + k0 / 32 + half];
-      L.a[cb] = 0.f;
-    } else {
-      L.a[cb] = static_cast<const float*>(g.scl)[row * (size_t)(g.Kw / 64) + ks];
-      L.s[cb] = 0u;
-    }
-  }
-  return L;
-}
-
 template <int kMode, int kSub>
 __device__ __forceinline__ void fwd_columns(const GemmArgs& g, int e, int n0, int start, int valid,
                                            int tid, uint16_t* A0, uint16_t* A1, f32x2* lut2,
@@ -855,13 +738,13 @@ __device__ __forceinline__ void fwd_columns(const GemmArgs& g, int e, int n0, in
   else run_loop(std::integral_constant<int, -1>{});
 
   // ---- epilogue: one output row per lane ----
+  if constexpr (kGlu) {
 #pragma unroll
-  for (int i = 0; i < kSub; ++i) {
-    if (i >= nrows) continue;
-    const int m = 32 * i + lr;
-    const int p = pair_s[m];
-    const float sc = scale_s[m];
-    if constexpr (kGlu) {
+    for (int i = 0; i < kSub; ++i) {
+      if (i >= nrows) continue;
+      const int m = 32 * i + lr;
+      const int p = pair_s[m];
+      const float sc = scale_s[m];
       const int col = n0 + 32 * wave;
       if (m < valid && col < g.Nout) {
         float v[16];
@@ -869,18 +752,9 @@ __device__ __forceinline__ void fwd_columns(const GemmArgs& g, int e, int n0, in
         for (int r = 0; r < 16; ++r) v[r] = silu_f32(acc[i][0][r]) * acc[i][1][r] * sc;
         store_block_t(v, g.out + (int64_t)p * g.Nout + col, lh);
       }
-    } else {
-#pragma unroll
-      for (int cb = 0; cb < 2; ++cb) {
-        const int col = n0 + 64 * wave + 32 * cb;
-        if (m < valid && col < g.Nout) {
-          float v[16];
-#pragma unroll
-          for (int r = 0; r < 16; ++r) v[r] = acc[i][cb][r] * sc;
-          store_block_t(v, g.out + (int64_t)p * g.Nout + col, lh);
-        }
-      }
     }
+  } else {
+    store_wide_rows<kSub>(acc, nrows, valid, pair_s, scale_s, g, n0, wave, lr, lh);
   }
 }
 
@@ -899,39 +773,14 @@ __global__ __launch_bounds__(kGemmThreads, 1) void grouped_gemm_fwd_kernel(GemmA
   __shared__ __attribute__((aligned(4096))) f32x2 lut2[256];
 
   const int tid = threadIdx.x;
-  const int C = g.n_col_tiles;
-  const int bid = blockIdx.x;
-  const int qb = bid >> 3, xcd = bid & 7;
-  const int logical = (qb / C) * (8 * C) + xcd * C + (qb % C);
-  if (logical >= g.n_logical) return;
-  const int tile = logical / C;
-  const int n0 = (logical % C) * kTNo;
-  const int T = *g.num_tiles;
-
-  if (tile >= T) {
-    // Zero the rows of dropped pairs (ids outside [0, E)), columns [n0, n0+kTNo).
-    const int dstart = g.offsets[g.E] + (tile - T) * kTM;
-    if (dstart >= g.P || dstart < 0) return;
-    const int dvalid = min(kTM, g.P - dstart);
-    for (int idx = tid; idx < dvalid * (kTNo / 8); idx += kGemmThreads) {
-      const int r = idx / (kTNo / 8), c8 = idx % (kTNo / 8);
-      const int col = n0 + c8 * 8;
-      const int p = g.sorted_pairs[dstart + r];
-      if (col < g.Nout && (unsigned)p < (unsigned)g.P)
-        *reinterpret_cast<u32x4*>(g.out + (int64_t)p * g.Nout + col) = u32x4{0u, 0u, 0u, 0u};
-    }
-    return;
-  }
-
-  const int e = g.tiles[2 * tile];
-  const int start = g.tiles[2 * tile + 1];
-  if ((unsigned)e >= (unsigned)g.E || (unsigned)start >= (unsigned)g.P) return;
-  const int valid = min(kTM, min(g.offsets[e + 1], g.P) - start);
-  if (valid <= 0) return;
-  if (valid <= kNarrowRows)
-    fwd_columns<kMode, 4>(g, e, n0, start, valid, tid, A0, A1, lut2, pair_s, row_s, scale_s);
+  TileInfo t;
+  if (!tile_head<kTNo>(g, tid, t)) return;
+  if (t.valid <= kNarrowRows)
+    fwd_columns<kMode, 4>(g, t.e, t.n0, t.start, t.valid, tid, A0, A1, lut2, pair_s, row_s,
+                          scale_s);
   else
-    fwd_columns<kMode, 8>(g, e, n0, start, valid, tid, A0, A1, lut2, pair_s, row_s, scale_s);
+    fwd_columns<kMode, 8>(g, t.e, t.n0, t.start, t.valid, tid, A0, A1, lut2, pair_s, row_s,
+                          scale_s);
 }
 
 // Contractions of at least this many elements use the 256 x 256 kernel
@@ -963,20 +812,6 @@ static int launch_gemm(GemmArgs g, int32_t max_tiles, int32_t tile_m, hipStream_
     hipLaunchKernelGGL(grouped_gemm_fwd_shortk_kernel<kMode>, dim3((unsigned)grid),
                        dim3(kGemmThreads), 0, stream, g);
   return launch_status();
-}
-
-static int common_gemm_checks(const uint16_t* x, int64_t x_rows, int64_t x_stride, int32_t Kc,
-                              const uint8_t* codes, const void* scl, const int32_t* offsets,
-                              const int32_t* sorted_pairs, const int32_t* tiles,
-                              const int32_t* num_tiles, const uint16_t* out) {
-  if (!x || !codes || !scl || !offsets || !sorted_pairs || !tiles || !num_tiles || !out)
-    return kInvalid;
-  if (x_stride < Kc || x_stride % 8) return kInvalid;
-  if (x_rows * x_stride >= INT32_MAX) return kNotSupported;   // 32-bit activation offsets
-  if (!aligned16(x) || !aligned16(codes) || !aligned16(out)) return kInvalid;
-  if (!aligned4(offsets) || !aligned4(sorted_pairs) || !aligned4(tiles) || !aligned4(num_tiles))
-    return kInvalid;
-  return kOk;
 }
 
 template <bool kMx, bool kGlu = false>

@@ -185,6 +185,61 @@ int gq_mxfp4_grouped_gemm(const uint16_t* x, int32_t rows, int32_t K, int64_t x_
                           int32_t tile_m, uint16_t* out, hipStream_t stream);
 
 /* ------------------------------------------------------------------------
+ * MXFP4 prefill on the block-scaled fp4 matrix instruction.  [P2] summary
+ * (MXFP4 as OCP e2m1 on the checkpoint's released bytes, decoded inside the
+ * mainloop); [P3] summary (native MXFP4 expert inference); [P1] "Which
+ * entry point?" (native MXFP4 expert math).  The weights' e2m1 codes and
+ * e8m0 scales are fed to the gfx950 instruction as stored, with no decode.
+ * The pages keep activations in bf16; the instruction's other operand must
+ * be an MX format too, so the activations are first written as two e4m3
+ * terms (the reading of this library):
+ *
+ *   x[t, k] ~= hi[t, k] * 2^(s_hi[t, k/32] - 127) + lo[t, k] * 2^(s_lo[t, k/32] - 127)
+ *
+ * per 32 consecutive k: X = the smallest integer with amax * 2^-X <= 448
+ * (the largest e4m3 magnitude; -127 for an all-zero block), hi = e4m3 of
+ * x * 2^-Xh rounded to nearest even, lo the same for the exact residual
+ * x - hi * 2^Xh with its own exponent.  The two terms hold every bf16 value
+ * of a block exactly unless its magnitudes span 2^12 or more; in any case
+ * |x - split| <= 2^-8 |x| + 2^-16 amax.  Results are then within the same
+ * tolerance of the float64 W4A16 product as the bf16 path.
+ *
+ * gq_act_split_e4m3: x uint16 bf16 [rows, K] (row stride x_stride elements,
+ * a multiple of 8; K a multiple of 32) -> with Kp = K rounded up to 64:
+ *   codes  uint8 [rows, 2*Kp]: per row and 64-k step s, 128 bytes: hi codes
+ *          then lo codes, 64 bytes each; in each, bytes [32h, 32h+32) hold
+ *          elements 16h + [0, 16) of k block 2s, then of block 2s+1 (the
+ *          order the instruction's e4m3 operand takes them in)
+ *   scales uint8 [rows, Kp/16]: per step s_hi(2s), s_lo(2s), s_hi(2s+1),
+ *          s_lo(2s+1)
+ * A block past K (K % 64 == 32) is written as zeros with scale byte 0.
+ * codes 16-byte aligned, scales 4-byte aligned.
+ * InvalidValue: null pointer, rows < 0, K not a positive multiple of 32,
+ *   bad stride or alignment.  NotSupported: grid beyond 2^31 blocks.
+ *
+ * gq_mxfp4_grouped_gemm_scaled: as gq_mxfp4_grouped_gemm with the
+ * activations given as gq_act_split_e4m3's output for x [rows, K]:
+ *
+ *   out[p, n] = bf16( pair_scale[p] * sum_k split(x)[p/topk, k] * W_{ids[p]}[n, k] )
+ *
+ * float32 accumulation.  Same grouping, pair_scale and out conventions.
+ * InvalidValue: null pointer (pair_scale may be NULL), rows < 0, topk < 1,
+ *   E < 1, N < 1 or N % 32, K not a positive multiple of 32, bad alignment,
+ *   max_tiles below the bound.
+ * NotSupported: tile_m != 256, rows*topk >= 2^31, rows*2*Kp >= 2^31, grid
+ *   beyond 2^31 blocks.  rows == 0 enqueues nothing.
+ */
+int gq_act_split_e4m3(const uint16_t* x, int32_t rows, int32_t K, int64_t x_stride,
+                      uint8_t* codes, uint8_t* scales, hipStream_t stream);
+int gq_mxfp4_grouped_gemm_scaled(const uint8_t* x_codes, const uint8_t* x_scales, int32_t rows,
+                                 int32_t K, const uint8_t* blocks, const uint8_t* scales,
+                                 int32_t num_experts, int32_t N, int32_t topk,
+                                 const float* pair_scale, const int32_t* expert_offsets,
+                                 const int32_t* sorted_pairs, const int32_t* tiles,
+                                 const int32_t* num_tiles, int32_t max_tiles, int32_t tile_m,
+                                 uint16_t* out, hipStream_t stream);
+
+/* ------------------------------------------------------------------------
  * NF4 input gradient.  [P1] "Which entry point?" (grouped NF4 backward);
  * [P2] summary (the NF4 path is differentiable, fine-tuning stays packed).
  *

@@ -227,3 +227,29 @@ def test_gemv_pair_count_requires_matching_rows():
     for shape in ((3, 8), (5, 8), (32,), (4, 8, 1)):
         with pytest.raises(ValueError):
             gq._gemv_pairs(torch.zeros(shape, dtype=torch.int32), 4)
+
+
+def test_scaled_mxfp4_entry_points_reject(lib):
+    # split: K % 32, stride, null, misaligned output, rows == 0
+    assert lib.gq_act_split_e4m3(F, 4, 48, 48, F, F, None) == INVALID
+    assert lib.gq_act_split_e4m3(F, 4, 64, 60, F, F, None) == INVALID
+    assert lib.gq_act_split_e4m3(NULL, 4, 64, 64, F, F, None) == INVALID
+    assert lib.gq_act_split_e4m3(F, 4, 64, 64, F2, F, None) == INVALID
+    assert lib.gq_act_split_e4m3(F, -1, 64, 64, F, F, None) == INVALID
+    assert lib.gq_act_split_e4m3(F, 0, 64, 64, F, F, None) == 0
+    # scaled GEMM: N % 32, K % 32, tile_m, max_tiles, null, 32-bit row offsets
+    args = [F, F, 2048, 2880, F, F, 32, 5760, 4, NULL, F, F, F, F, 32 + 33 + 1, 256, F, None]
+
+    def call(**kw):
+        a = list(args)
+        for i, v in kw.items():
+            a[int(i[1:])] = v
+        return lib.gq_mxfp4_grouped_gemm_scaled(*a)
+    assert call(a7=5750) == INVALID
+    assert call(a3=2870) == INVALID
+    assert call(a15=128) == NOT_SUPPORTED
+    assert call(a14=60) == INVALID
+    assert call(a0=NULL) == INVALID
+    assert call(a1=F2) == INVALID
+    assert call(a2=1 << 20, a14=(1 << 22) // 256 + 33 + 1) == NOT_SUPPORTED
+    assert call(a2=0) == 0
