@@ -165,13 +165,24 @@ __device__ __forceinline__ void dg_stage(const DgLoad& L, uint8_t* Cs, float* As
     float f;
     if constexpr (F::kMx) f = e8m0_to_f32(L.s);
     else f = L.a;
-    As[tid] = L.aok ? f : 0.f;
+    // factor of (row tid / kBlk, block tid % kBlk), stored block-major so a
+    // thread's 8 consecutive rows are 32 contiguous bytes
+    As[(tid % F::kBlk) * kTK + tid / F::kBlk] = L.aok ? f : 0.f;
   }
 }
 
-// Dgrad decode, in four chunks: chunk c writes column 4*j4 + c of the
-// thread's column quad (8 consecutive contraction values, 16 bytes).  The
-// thread's raw codes and absmax are read from LDS once, by chunk 0.
+// Dgrad decode.  Thread (j4, r8) = (tid % 32, tid / 32) produces rows
+// r8*8 .. +8 of the column quad 4*j4 .. +3: it reads its two code bytes of
+// each of the 8 rows from LDS once per step, the rows' factors (one scale
+// block covers the quad) as 32 contiguous bytes, and writes each column's 8
+// consecutive contraction values as one 16-byte run.
+//  * NF4: codebook values from the 16-entry LDS table; weight =
+//    float32(value * absmax), then bf16 RNE.
+//  * MXFP4, in two passes of two columns (code byte cp of each row holds
+//    columns 4*j4 + 2cp and + 2cp + 1, the even one in the low nibble): the
+//    hardware converter turns the byte into the two bf16 weights with the
+//    e8m0 factor applied, exactly; a byte permute then pairs rows i and
+//    i + 1 of one column.
 struct DgCodes {
   uint32_t two[4];   // bytes j4*2, j4*2+1 of rows r8*8 + 2i (low half) and + 2i+1 (high half)
 };
@@ -188,28 +199,62 @@ __device__ __forceinline__ void dg_read_codes(const uint8_t* Cs, const float* As
   }
 }
 
-// The LUT holds the NF4 codebook or the e2m1 values; weight = value * factor
-// in float32 (exact for e2m1 times a power of two), then bf16 RNE.
 template <int kMode>
-__device__ __forceinline__ void dg_decode_chunk(const DgCodes& R, const float* As, int c,
-                                                const float* lut, uint16_t* Bs, int tid) {
+__device__ __forceinline__ void dg_decode_pair(const DgCodes& R, const float* As, int cp,
+                                               uint16_t* Bs, int tid) {
   using F = DgFmt<kMode>;
   const int j4 = tid & 31, r8 = tid >> 5;
-  const int blk = (j4 * 4) / F::kBlkK;
-  float w[8];
-  // bytes j4*2, j4*2+1 hold columns 4*j4 .. 4*j4+3; element 2j sits in the
-  // high nibble (NF4) or the low nibble (MXFP4) of byte j
-  constexpr bool kLowFirst = DgFmt<kMode>::kMx;
+  // factors of the 8 rows for the quad's scale block (32 contiguous bytes)
+  const f32x4* fp = reinterpret_cast<const f32x4*>(As + ((j4 * 4) / F::kBlkK) * kTK + r8 * 8);
+  const f32x4 f0 = fp[0], f1 = fp[1];
+  const float f[8] = {f0[0], f0[1], f0[2], f0[3], f1[0], f1[1], f1[2], f1[3]};
+  uint32_t ce[4], co[4];                 // columns 4 j4 + 2cp (even) and + 1 (odd), rows paired
 #pragma unroll
-  for (int i = 0; i < 8; ++i) {
-    const bool lo = ((c & 1) != 0) != kLowFirst;
-    const int byte = (c >> 1) + 2 * (i & 1);
-    const float qv = lo ? nf4_q_lo(lut, R.two[i >> 1], byte) : nf4_q_hi(lut, R.two[i >> 1], byte);
-    w[i] = qv * As[(r8 * 8 + i) * F::kBlk + blk];           // factor re-read: registers are short
+  for (int h = 0; h < 4; ++h) {
+    // rows 2h (low half of two[h]) and 2h + 1 (high half): byte cp and 2 + cp
+    const uint32_t r0 = e2m1_pair_bf16_scaled(R.two[h], cp, f[2 * h]);
+    const uint32_t r1 = e2m1_pair_bf16_scaled(R.two[h], 2 + cp, f[2 * h + 1]);
+    ce[h] = __builtin_amdgcn_perm(r1, r0, 0x05040100u);     // low halves: even column
+    co[h] = __builtin_amdgcn_perm(r1, r0, 0x07060302u);     // high halves: odd column
   }
-  const u32x4 v{pack_bf16x2(w[0], w[1]), pack_bf16x2(w[2], w[3]), pack_bf16x2(w[4], w[5]),
-                pack_bf16x2(w[6], w[7])};
-  *reinterpret_cast<u32x4*>(Bs + (j4 * 4 + c) * kBStride + r8 * 8) = v;
+  uint16_t* col = Bs + (j4 * 4 + 2 * cp) * kBStride + r8 * 8;
+  *reinterpret_cast<u32x4*>(col) = u32x4{ce[0], ce[1], ce[2], ce[3]};
+  *reinterpret_cast<u32x4*>(col + kBStride) = u32x4{co[0], co[1], co[2], co[3]};
+}
+
+// NF4: all four columns of the quad per call, from the 16-entry codebook
+// table (16 distinct banks: conflict-free); code dword h holds rows 2h and
+// 2h + 1, its 8 nibbles in element order are the quad's columns of row 2h
+// then of row 2h + 1 (high nibble = even column).
+__device__ __forceinline__ void dg_decode_nf4(const DgCodes& R, const float* As, const float* lut,
+                                              uint16_t* Bs, int tid) {
+  const int j4 = tid & 31, r8 = tid >> 5;
+  const f32x4* fp = reinterpret_cast<const f32x4*>(As + (j4 / 16) * kTK + r8 * 8);
+  const f32x4 f0 = fp[0], f1 = fp[1];
+  const float f[8] = {f0[0], f0[1], f0[2], f0[3], f1[0], f1[1], f1[2], f1[3]};
+  uint32_t c[4][4];                      // [column][row pair]
+#pragma unroll
+  for (int h = 0; h < 4; ++h) {
+    float q[8];
+    nf4_lookup8(lut, R.two[h], q);
+#pragma unroll
+    for (int k = 0; k < 4; ++k) c[k][h] = pack_bf16x2(q[k] * f[2 * h], q[4 + k] * f[2 * h + 1]);
+  }
+#pragma unroll
+  for (int k = 0; k < 4; ++k)
+    *reinterpret_cast<u32x4*>(Bs + (j4 * 4 + k) * kBStride + r8 * 8) =
+        u32x4{c[k][0], c[k][1], c[k][2], c[k][3]};
+}
+
+// one step's B tile: NF4 in one pass, MXFP4 in two (slices 1 and 2)
+template <int kMode>
+__device__ __forceinline__ void dg_decode(const DgCodes& R, const float* As, int part,
+                                          const float* lut, uint16_t* Bs, int tid) {
+  if constexpr (kMode == kDgradNF4) {
+    if (part == 0) dg_decode_nf4(R, As, lut, Bs, tid);
+  } else {
+    dg_decode_pair<kMode>(R, As, part, Bs, tid);
+  }
 }
 
 // Rows of sub-tiles ms0, ms1 (32 rows each) for the 128 B columns of a
@@ -252,12 +297,20 @@ __device__ __forceinline__ void store_rows_t(const f32x16 (&acc)[2][4], bool act
 template <int kMode>
 __device__ __forceinline__ void grouped_gemm_body(const GemmArgs& g) {
   constexpr bool kDg = kMode == kDgradNF4 || kMode == kDgradMX;
+  // Activation (dY) operand of the input gradient.  MXFP4: staged like the
+  // forward operand (coalesced 128-byte row loads, per-wave swizzled LDS
+  // area); fragment-shaped loads straight into registers make every load
+  // instruction touch 32 rows and kept the address unit ~80% busy (gpt-oss
+  // dgrad gate_up 513 -> 433 us staged).  NF4: the direct loads (on the
+  // Qwen3 shapes tiles are half full, ~128 rows per expert, and the staging's
+  // extra LDS traffic costs more than the address unit saves: 220 vs 227 us).
+  constexpr bool kDirectA = kMode == kDgradNF4;
   constexpr bool kGlu = kMode == kFwdNF4Glu;
   constexpr int kTNo = kGlu ? kTN / 2 : kTN;               // output columns per tile
   __shared__ __attribute__((aligned(16))) uint16_t Bs[2][kTN * kBStride];
   __shared__ __attribute__((aligned(16))) uint8_t Cs[kDg ? 2 : 1][kDg ? kTK * kCStride : 16];
   __shared__ float As[kDg ? 2 : 1][kDg ? DgFmt<kMode>::kBlk * kTK : 1];
-  __shared__ __attribute__((aligned(16))) uint16_t Aw[kDg ? 1 : 4][kDg ? 8 : 64 * kTK];  // A staging
+  __shared__ __attribute__((aligned(16))) uint16_t Aw[kDirectA ? 1 : 4][kDirectA ? 8 : 64 * kTK];
   __shared__ int pair_s[kTM];
   // dgrad rows are the pairs themselves: row_s aliases pair_s (saves 1 KB of
   // LDS, which lets two dgrad workgroups share a CU)
@@ -275,8 +328,7 @@ __device__ __forceinline__ void grouped_gemm_body(const GemmArgs& g) {
     pair_s[r] = p;
     if constexpr (!kDg) row_s[r] = p / g.topk;
   }
-  if constexpr (kMode == kDgradMX) e2m1_lut_init(lut, tid);
-  else if constexpr (kMode != kFwdMX) nf4_lut_init(lut, tid);
+  if constexpr (kMode != kFwdMX && kMode != kDgradMX) nf4_lut_init(lut, tid);
   lds_barrier();
 
   const int wave = tid >> 6, lane = tid & 63;
@@ -310,7 +362,7 @@ __device__ __forceinline__ void grouped_gemm_body(const GemmArgs& g) {
   // when read), see the note at fwd_load; a wave loads the rows of sub-tile
   // ms1 only in the variants where ms1 is active (kNa = 8 loads) and none in
   // the variant for a wave without active rows.
-  uint16_t* aw = &Aw[kDg ? 0 : wave][0];
+  uint16_t* aw = &Aw[kDirectA ? 0 : wave][0];
   // The lane's row offsets are re-read from LDS at every step (registers
   // are short); element offsets fit 32 bits (host check).
   auto load_a = [&](auto na_c, int ks, u32x4 (&Ar)[8]) {
@@ -387,8 +439,8 @@ __device__ __forceinline__ void grouped_gemm_body(const GemmArgs& g) {
     }
   };
 
-  u32x4 Ar[kDg ? 1 : 8];                                   // forward: staged A prefetch
-  u32x4 Ad[2][kDg ? 4 : 1];                                // dgrad: direct A fragments
+  u32x4 Ar[kDirectA ? 1 : 8];                              // staged A prefetch
+  u32x4 Ad[2][kDirectA ? 4 : 1];                           // direct A fragments
   FwdLoad F0{}, F1{};
   DgLoad D{};
   DgCodes R{};
@@ -406,7 +458,7 @@ __device__ __forceinline__ void grouped_gemm_body(const GemmArgs& g) {
   // activations and codes in flight ----
   auto prologue_a = [&](auto na_c) {
     if constexpr (decltype(na_c)::value > 0) {
-      if constexpr (kDg) {
+      if constexpr (kDirectA) {
 #pragma unroll
         for (int sl = 0; sl < 4; ++sl) load_a_direct(na_c, 0, sl, Ad);
       } else {
@@ -424,8 +476,8 @@ __device__ __forceinline__ void grouped_gemm_body(const GemmArgs& g) {
     D = dg_load<kMode>(g, e, n0, min(1, nsteps - 1), tid);
     lds_barrier();
     dg_read_codes<kMode>(Cs[0], As[0], tid, R);
-#pragma unroll
-    for (int c = 0; c < 4; ++c) dg_decode_chunk<kMode>(R, As[0], c, lut, Bs[0], tid);
+    dg_decode<kMode>(R, As[0], 0, lut, Bs[0], tid);
+    dg_decode<kMode>(R, As[0], 1, lut, Bs[0], tid);
     dg_stage<kMode>(D, Cs[1], As[1], tid);
     D = dg_load<kMode>(g, e, n0, min(2, nsteps - 1), tid);
   } else {
@@ -460,7 +512,7 @@ __device__ __forceinline__ void grouped_gemm_body(const GemmArgs& g) {
         u32x4 ac[2];
         if constexpr (kRows >= 0) {
           constexpr int kNj = kRows == 1 ? 1 : 2;          // sub-tiles with operands
-          if constexpr (kDg) {
+          if constexpr (kDirectA) {
             ac[0] = Ad[0][sl];
             if constexpr (kNj == 2) ac[1] = Ad[1][sl];
           } else {
@@ -470,7 +522,7 @@ __device__ __forceinline__ void grouped_gemm_body(const GemmArgs& g) {
         }
         if constexpr (kDg) {
           if (sl == 0) dg_read_codes<kMode>(Cs[(ks + 1) & 1], As[(ks + 1) & 1], tid, R);
-          dg_decode_chunk<kMode>(R, As[(ks + 1) & 1], sl, lut, Bn, tid);
+          if (sl == 1 || sl == 2) dg_decode<kMode>(R, As[(ks + 1) & 1], sl - 1, lut, Bn, tid);
           if (sl == 3) {                                   // codes of step ks+2, then ks+3
             dg_stage<kMode>(D, Cs[ks & 1], As[ks & 1], tid);
             D = dg_load<kMode>(g, e, n0, min(ks + 3, nsteps - 1), tid);
@@ -479,14 +531,14 @@ __device__ __forceinline__ void grouped_gemm_body(const GemmArgs& g) {
           fwd_decode_chunk<kMode>(F_dec, sl, lut, Bn, tid);
         }
         if constexpr (kRows >= 0) mfma_slice(rows_c, ac, bc);
-        if constexpr (kDg && kNa > 0) load_a_direct(NaC{}, min(ks + 1, nsteps - 1), sl, Ad);
+        if constexpr (kDirectA && kNa > 0) load_a_direct(NaC{}, min(ks + 1, nsteps - 1), sl, Ad);
       };
       if constexpr (kRows >= 0) load_b_slice(B, 0, b0);
       slice(0, b0, b1);
       slice(1, b1, b0);
       slice(2, b0, b1);
       slice(3, b1, b0);
-      if constexpr (!kDg && kNa > 0) {
+      if constexpr (!kDirectA && kNa > 0) {
         stage_a(NaC{}, Ar);                              // step ks+1 (own area: no barrier)
         load_a(NaC{}, min(ks + 2, nsteps - 1), Ar);
       }
@@ -507,7 +559,7 @@ __device__ __forceinline__ void grouped_gemm_body(const GemmArgs& g) {
 }
 
 // The dgrad fits 2 waves per SIMD (2 workgroups per CU): it keeps its code
-// words two rows per register and re-reads the row factors from LDS.
+// words two rows per register.
 template <int kMode>
 __global__ __launch_bounds__(kGemmThreads, 2) void grouped_dgrad_kernel(GemmArgs g) {
   grouped_gemm_body<kMode>(g);
