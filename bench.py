@@ -715,6 +715,46 @@ def r4(d):
     return d
 
 
+LEGS = ("decode", "decode_m4", "mx_decode", "controls", "prefill", "mx_prefill",
+        "mx_prefill_scaled", "layer_decode", "layer_prefill", "dgrad", "mx_dgrad", "mfma")
+
+
+def run_legs(dev, args, legs):
+    """The named legs only (for profiler runs), one JSON object of results."""
+    out = {}
+    st, wu, ps, pw = args.steps, args.warmup, args.prefill_steps, args.prefill_warmup
+    for leg in legs:
+        log("[bench] leg", leg)
+        if leg == "decode":
+            out[leg] = decode_nf4(dev, st, wu, M=1)[0]
+        elif leg == "decode_m4":
+            out[leg] = decode_nf4(dev, st, wu, M=4)[0]
+        elif leg == "mx_decode":
+            out[leg] = decode_mx(dev, st, wu)
+        elif leg == "controls":
+            out[leg] = controls(dev, [16 << 20, 140_000_000])
+        elif leg == "prefill":
+            out[leg] = prefill(dev, ps, pw, "nf4")
+        elif leg == "mx_prefill":
+            out[leg] = prefill(dev, ps, pw, "mx")
+        elif leg == "mx_prefill_scaled":
+            out[leg] = prefill_mx_scaled(dev, ps, pw)
+        elif leg == "layer_decode":
+            out[leg] = decode_layer_nf4(dev, st, wu)
+        elif leg == "layer_prefill":
+            out[leg] = prefill_layer_nf4(dev, ps, pw)
+        elif leg == "dgrad":
+            out[leg] = dgrad(dev, ps, pw)
+        elif leg == "mx_dgrad":
+            out[leg] = dgrad(dev, ps, pw, "mx")
+        elif leg == "mfma":
+            out[leg] = mfma_rates(dev)
+        else:
+            sys.exit(f"unknown leg {leg}; choose from {','.join(LEGS)}")
+        log("[bench]", leg, r4(out[leg]))
+    print(json.dumps(r4(out)), flush=True)
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -725,6 +765,9 @@ def main():
                     help="untimed prefill/dgrad steps first (long kernels: lets the clocks settle)")
     ap.add_argument("--cpu-budget", type=float, default=12.0)
     ap.add_argument("--quick", action="store_true", help="headline + prefill only, short CPU leg")
+    ap.add_argument("--legs", default=None,
+                    help="profiling runs: comma-separated subset of " + ",".join(LEGS) +
+                         "; runs only those legs and prints their results (not the bench line)")
     args = ap.parse_args()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
         print("bench.py measures one GPU: the library has no multi-GPU path "
@@ -736,6 +779,9 @@ def main():
         sys.exit(2)
     gq.load_library()
     dev = torch.device("cuda:0")
+    if args.legs:
+        run_legs(dev, args, args.legs.split(","))
+        return
 
     log("[bench] nf4 decode M=1")
     dec, sample = decode_nf4(dev, args.steps, args.warmup, M=1)

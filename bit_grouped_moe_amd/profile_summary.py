@@ -3,7 +3,8 @@
     python -m bit_grouped_moe_amd.profile_summary trace DIR --cmd "..." --out FILE.md
     python -m bit_grouped_moe_amd.profile_summary traffic FETCH_DIR WRITE_DIR \
         --control-bytes B --cmd "..." --out FILE.md --json profiles/traffic_counters.json
-    python -m bit_grouped_moe_amd.profile_summary counters DIR [DIR ...] --cmd "..." --out FILE.md
+    python -m bit_grouped_moe_amd.profile_summary counters DIR [DIR ...] --cmd "..." --out FILE.md \
+        [--kernels all]
 
 ``trace`` reads the kernel trace (``*_kernel_trace.csv``) of a
 ``rocprofv3 --kernel-trace --stats --output-format csv`` run and tabulates
@@ -12,8 +13,9 @@ median, mean, min and max device time.
 
 ``counters`` reads one or more ``rocprofv3 --pmc <SQ counters>`` runs of
 ``bench.py`` and tabulates, for the decode gate_up GEMV and the prefill
-gate_up GEMM launches of the Qwen3 workload, the median per dispatch of
-every counter collected, plus ratios formed from counters of the same
+gate_up GEMM launches of the Qwen3 workload (or, with ``--kernels all``,
+for every libgq kernel launch shape in the runs), the median per dispatch
+of every counter collected, plus ratios formed from counters of the same
 dispatch (no normalisation by unit counts or clocks).
 
 ``traffic`` reads two ``rocprofv3 --pmc FETCH_SIZE`` / ``--pmc WRITE_SIZE``
@@ -41,7 +43,7 @@ CSRC = os.path.join(HERE, "csrc")
 GATE_UP_GEMV = ("grouped_gemv_kernel<false, 2, true, false>", 393216)  # N=1536, K=2048, M=1, top-8
 GATE_UP_GEMM = ("grouped_gemm_fwd_kernel<0>", 405504)      # M=4096 top-8, 257 x 6 tiles
 SOURCES = {"gemv_nf4_gate_up_m1": ["gemv.hip", "gq_device.hpp"],
-           "gemm_nf4_gate_up_prefill": ["gemm.hip", "gq_device.hpp"]}
+           "gemm_nf4_gate_up_prefill": ["gemm.hip", "gemm_common.hpp", "gq_device.hpp"]}
 
 
 _PROBES = ("stream_read_kernel(", "copy_kernel(", "empty_kernel(")
@@ -149,10 +151,16 @@ _RATIOS = (
     ("cycles waves wait on anything / wave cycles", "SQ_WAIT_ANY", "SQ_WAVE_CYCLES"),
     ("VALU+MFMA co-issue cycles / MFMA busy cycles", "SQ_VALU_MFMA_COEXEC_CYCLES",
      "SQ_VALU_MFMA_BUSY_CYCLES"),
+    ("cycles waves wait on an instruction's data / wave cycles", "SQ_WAIT_INST_ANY",
+     "SQ_WAVE_CYCLES"),
+    ("address-unit busy cycles / shader-engine busy cycles", "TA_TA_BUSY_sum", "SQ_BUSY_CYCLES"),
+    ("address unit stalled by the L1 / address-unit busy", "TA_ADDR_STALLED_BY_TC_CYCLES_sum",
+     "TA_TA_BUSY_sum"),
 )
 
 
 def counters(args):
+    every = getattr(args, "kernels", "bench") == "all"
     per = {}                                                 # (record, counter) -> [values]
     for d in args.dirs:
         for f in glob.glob(os.path.join(d, "**", "*_counter_collection.csv"), recursive=True):
@@ -164,11 +172,17 @@ def counters(args):
                 key = (k, int(r["Grid_Size"]), int(r["Dispatch_Id"]), r["Counter_Name"])
                 disp[key] = disp.get(key, 0.0) + float(r["Counter_Value"])
             for (k, grid, _, cname), v in disp.items():
+                if every:
+                    per.setdefault((f"{k} grid {grid}", cname), []).append(v)
+                    continue
                 for rec, (kern, kgrid) in (("gemv_nf4_gate_up_m1", GATE_UP_GEMV),
                                            ("gemm_nf4_gate_up_prefill", GATE_UP_GEMM)):
                     if k.startswith(kern) and grid == kgrid:
                         per.setdefault((rec, cname), []).append(v)
-    recs = ("gemv_nf4_gate_up_m1", "gemm_nf4_gate_up_prefill")
+    if every:
+        recs = tuple(sorted({r for (r, _) in per}))
+    else:
+        recs = ("gemv_nf4_gate_up_m1", "gemm_nf4_gate_up_prefill")
     names = sorted({c for (_, c) in per})
     med = {key: statistics.median(v) for key, v in per.items()}
     lines = ["# SQ counters per launch from rocprofv3: " + args.title, "",
@@ -211,6 +225,7 @@ def main():
     k.add_argument("--cmd", required=True)
     k.add_argument("--title", default="bench.py")
     k.add_argument("--out", required=True)
+    k.add_argument("--kernels", default="bench", choices=("bench", "all"))
     args = ap.parse_args()
     {"trace": trace, "traffic": traffic, "counters": counters}[args.mode](args)
 

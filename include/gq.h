@@ -134,8 +134,13 @@ int gq_mxfp4_decode(const uint8_t* blocks, const uint8_t* scales, int64_t n_rows
  *   topk_ids   int32 [rows, topk]; pair_scale float [rows*topk] or NULL
  *   out        uint16 bf16 [rows*topk, N]
  * Each distinct active expert's bytes are read once, whichever tokens use
- * it; no sort is needed (the kernel reads topk_ids directly).  Arithmetic:
- * exact float32 decode, float32 products and sums.
+ * it; no sort is needed (the kernel reads topk_ids directly).  Arithmetic,
+ * float32 throughout with no bf16 rounding of the weights: each group of 32
+ * consecutive k is summed as sum(codebook_value * x) (NF4) or
+ * sum(e2m1_value * x) (MXFP4), then multiplied once by the group's factor
+ * (the NF4 absmax of its 64-block; the MXFP4 2^(s-127), exact); the group
+ * partials are added in a fixed order.  A one-hot x therefore returns
+ * bf16(float32(value * factor)), the decoded weight, bit for bit.
  * InvalidValue: null pointer (pair_scale may be NULL), rows < 1,
  *   topk < 1, E < 1, N < 1, K not a positive multiple of 64 (NF4) / 32
  *   (MXFP4), bad stride or alignment.
