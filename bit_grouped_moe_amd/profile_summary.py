@@ -132,6 +132,17 @@ def traffic(args):
         rec[key] = {"source": SOURCES[key][0], "source_sha256": sources_sha(key),
                     "fetch_bytes": fb, "write_bytes": wb, "hbm_bytes_per_launch": fb + wb}
         rows.append(f"| {key} | {kern} | {grid} | {f:.1f} | {w:.1f} | {fb:,.0f} | {wb:,.0f} |")
+    if getattr(args, "kernels", "bench") == "all":
+        rows.append("")
+        rows.append("Every kernel launch shape in the runs (median per dispatch):")
+        rows.append("")
+        rows.append("| kernel | grid | FETCH_SIZE KiB | WRITE_SIZE KiB | read bytes | written bytes |")
+        rows.append("|---|---|---|---|---|---|")
+        for kern, grid in sorted({(k, g) for (k, g, _) in fetch} & {(k, g) for (k, g, _) in write}):
+            f = _median_for(fetch, kern, grid)
+            w = _median_for(write, kern, grid)
+            rows.append(f"| {kern} | {grid} | {f:.1f} | {w:.1f} | {f * 1024 * fr:,.0f} | "
+                        f"{w * 1024 * fw:,.0f} |")
     json.dump(rec, open(args.json, "w"), indent=1)
     lines = ["# HBM traffic per launch from rocprofv3 counters: " + args.title, "",
              "Commands (run from the repository root):", "", "```", args.cmd, "```", "",
@@ -153,7 +164,10 @@ _RATIOS = (
      "SQ_VALU_MFMA_BUSY_CYCLES"),
     ("cycles waves wait on an instruction's data / wave cycles", "SQ_WAIT_INST_ANY",
      "SQ_WAVE_CYCLES"),
-    ("address-unit busy cycles / shader-engine busy cycles", "TA_TA_BUSY_sum", "SQ_BUSY_CYCLES"),
+    # TA_TA_BUSY_sum adds the 256 per-CU address units, SQ_BUSY_CYCLES the 32
+    # shader engines: (TA / 256) / (SQ / 32) is the busy fraction of one unit.
+    ("address-unit busy fraction, (TA_TA_BUSY_sum / 256) / (SQ_BUSY_CYCLES / 32)",
+     "TA_TA_BUSY_sum", "SQ_BUSY_CYCLES", 32 / 256),
     ("address unit stalled by the L1 / address-unit busy", "TA_ADDR_STALLED_BY_TC_CYCLES_sum",
      "TA_TA_BUSY_sum"),
 )
@@ -181,6 +195,12 @@ def counters(args):
                         per.setdefault((rec, cname), []).append(v)
     if every:
         recs = tuple(sorted({r for (r, _) in per}))
+        match = [m for m in (getattr(args, "match", None) or "").split(",") if m]
+        if match:
+            recs = tuple(r for r in recs if any(r.startswith(m) for m in match))
+        labels = dict(x.split("=", 1) for x in (getattr(args, "label", None) or []))
+        per = {(labels.get(r, r), c): v for (r, c), v in per.items() if r in recs}
+        recs = tuple(labels.get(r, r) for r in recs)
     else:
         recs = ("gemv_nf4_gate_up_m1", "gemm_nf4_gate_up_prefill")
     names = sorted({c for (_, c) in per})
@@ -195,11 +215,11 @@ def counters(args):
             f"{med[(r, c)]:,.0f}" if (r, c) in med else "-" for r in recs) + " |")
     lines += ["", "| ratio (same dispatch, medians) | " + " | ".join(recs) + " |",
               "|---|" + "---|" * len(recs)]
-    for label, num, den in _RATIOS:
+    for label, num, den, *scale in _RATIOS:
         vals = []
         for r in recs:
             a, b = med.get((r, num)), med.get((r, den))
-            vals.append(f"{a / b:.3f}" if a is not None and b else "-")
+            vals.append(f"{a / b * (scale[0] if scale else 1.0):.3f}" if a is not None and b else "-")
         lines.append(f"| {label} | " + " | ".join(vals) + " |")
     open(args.out, "w").write("\n".join(lines) + "\n")
 
@@ -220,12 +240,17 @@ def main():
     c.add_argument("--title", default="bench.py")
     c.add_argument("--out", required=True)
     c.add_argument("--json", required=True)
+    c.add_argument("--kernels", default="bench", choices=("bench", "all"))
     k = sub.add_parser("counters")
     k.add_argument("dirs", nargs="+")
     k.add_argument("--cmd", required=True)
     k.add_argument("--title", default="bench.py")
     k.add_argument("--out", required=True)
     k.add_argument("--kernels", default="bench", choices=("bench", "all"))
+    k.add_argument("--match", default=None,
+                   help="with --kernels all: comma-separated kernel-name prefixes to keep")
+    k.add_argument("--label", action="append",
+                   help="with --kernels all: 'KERNEL grid G=column title' (repeatable)")
     args = ap.parse_args()
     {"trace": trace, "traffic": traffic, "counters": counters}[args.mode](args)
 
