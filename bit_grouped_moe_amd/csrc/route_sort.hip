@@ -5,17 +5,25 @@
 // synchronisation); the grouping itself is this library's design.
 //
 // Launch: E + 1 workgroups of 1024 threads.  Workgroup b < E owns expert b,
-// workgroup E owns the dropped pairs.  Each workgroup
-//   1. stages the ids in LDS with coalesced loads (32768 per pass),
-//   2. builds the full expert histogram in LDS (integer LDS atomics: the
-//      counts do not depend on their order) and reduces it to its own
-//      segment start and tile base,
-//   3. compacts its pairs in ascending pair order: wave w owns a contiguous
-//      range of 2048 ids, lane l takes ids range + 64j + l (conflict-free LDS
-//      reads) and the wave keeps the 32 match ballots in scalar registers;
-//      a pair's place is the workgroup's cursor + the earlier waves' counts
-//      + the wave's running count + its rank among the matching lanes
-//      (ballot bit count), and
+// workgroup E owns the dropped pairs.  The ids are taken in chunks of 32768;
+// wave w of a workgroup owns ids [chunk + 2048 w, chunk + 2048 (w + 1)) and
+// lane l holds ids chunk + 2048 w + 64 j + l, j < 32, in registers (each
+// load instruction reads 256 contiguous bytes).  Each workgroup
+//   1. builds the full expert histogram with integer LDS atomics into
+//      several copies of the histogram, lane l adding to copy l mod C (C = 64
+//      for E <= 128, fewer for larger E; at most 8192 counters): a skewed
+//      routing makes many lanes of one instruction hit the same expert, and
+//      same-address lanes of an LDS atomic serialise; the copies are summed
+//      by groups of lanes (integer counts: the order does not matter),
+//   2. lets every wave read the histogram and form its segment start, tile
+//      base and the totals itself (lane partial sums and a butterfly sum, no
+//      barrier),
+//   3. compacts its pairs in ascending pair order from the same registers:
+//      the wave's 32 match ballots are taken once to count (for the first
+//      chunk during the histogram pass, so the two share a barrier) and once
+//      to place, rows without a match skipped; a pair's place is the
+//      workgroup's cursor + the earlier waves' counts + the wave's running
+//      count + its rank among the matching lanes (ballot bit count), and
 //   4. writes its offsets entry and its tiles.
 // No global atomics, no workspace; the result is the unique stable order.
 #include "gq_device.hpp"
@@ -26,90 +34,125 @@ namespace gq {
 
 constexpr int kSortThreads = 1024;
 constexpr int kSortWaves = kSortThreads / kWave;
-constexpr int kChunkIds = 32768;                          // ids staged in LDS per pass
+constexpr int kChunkIds = 32768;                          // ids per pass
 constexpr int kPerLane = kChunkIds / kSortThreads;        // 32
+constexpr int kWaveIds = kChunkIds / kSortWaves;          // 2048 contiguous ids per wave
+constexpr int kHistCounters = 8192;                       // LDS counters over all copies
 constexpr int kPastEnd = INT32_MIN;                       // slots beyond the last pair
 
-// Block-wide sum of v (all threads get the result).
-__device__ __forceinline__ int block_sum(int v, int* red) {
-  const int lane = threadIdx.x & (kWave - 1), w = threadIdx.x / kWave;
-  v = wave_sum(v);
-  __syncthreads();
-  if (lane == 0) red[w] = v;
-  __syncthreads();
-  int s = 0;
+// The lane's 32 ids of chunk c0 (kPastEnd past P), all loads issued first:
+// unconditional where the wave's 2048 ids are all in range, clamped
+// addresses then a select on the last partial range, none past P.
+__device__ __forceinline__ void load_ids(const int32_t* __restrict__ ids, int32_t P, int64_t c0,
+                                         int (&v)[kPerLane]) {
+  const int lane = threadIdx.x & (kWave - 1), wave = threadIdx.x / kWave;
+  const int64_t wbase = c0 + (int64_t)wave * kWaveIds;
+  if (wbase + kWaveIds <= P) {
+    const int32_t* p = ids + wbase + lane;
 #pragma unroll
-  for (int i = 0; i < kSortWaves; ++i) s += red[i];
-  return s;
+    for (int j = 0; j < kPerLane; ++j) v[j] = p[j * kWave];
+  } else if (wbase < P) {
+#pragma unroll
+    for (int j = 0; j < kPerLane; ++j) {
+      const int64_t idx = wbase + (int64_t)j * kWave + lane;
+      const int x = ids[idx < P ? idx : P - 1];
+      v[j] = idx < P ? x : kPastEnd;
+    }
+  } else {
+#pragma unroll
+    for (int j = 0; j < kPerLane; ++j) v[j] = kPastEnd;
+  }
 }
 
-// Stage ids [c0, c0 + kChunkIds) in LDS (kPastEnd past P); loads issued first.
-__device__ __forceinline__ void stage_ids(const int32_t* __restrict__ ids, int32_t P, int64_t c0,
-                                          int* s_ids) {
-  int v[kPerLane];
-#pragma unroll
-  for (int j = 0; j < kPerLane; ++j) {
-    const int64_t idx = c0 + (int64_t)j * kSortThreads + threadIdx.x;
-    v[j] = idx < P ? ids[idx] : kPastEnd;
-  }
-#pragma unroll
-  for (int j = 0; j < kPerLane; ++j) s_ids[j * kSortThreads + threadIdx.x] = v[j];
+// Sum over the wave with DPP lane moves (total on lane 63), read back into a
+// scalar register: a fixed order, no LDS traffic.
+__device__ __forceinline__ int wave_total(int v) {
+  v += __builtin_amdgcn_update_dpp(0, v, 0xB1, 0xF, 0xF, false);   // quad_perm [1,0,3,2]
+  v += __builtin_amdgcn_update_dpp(0, v, 0x4E, 0xF, 0xF, false);   // quad_perm [2,3,0,1]
+  v += __builtin_amdgcn_update_dpp(0, v, 0x141, 0xF, 0xF, false);  // row_half_mirror
+  v += __builtin_amdgcn_update_dpp(0, v, 0x140, 0xF, 0xF, false);  // row_mirror
+  v += __builtin_amdgcn_update_dpp(0, v, 0x142, 0xA, 0xF, false);  // row_bcast:15
+  v += __builtin_amdgcn_update_dpp(0, v, 0x143, 0x8, 0xF, false);  // row_bcast:31
+  return __builtin_amdgcn_readlane(v, kWave - 1);
 }
 
 __global__ __launch_bounds__(kSortThreads) void route_sort_kernel(
     const int32_t* __restrict__ ids, int32_t P, int32_t E, int32_t tile_m,
     int32_t* __restrict__ offsets, int32_t* __restrict__ sorted_pairs,
     int32_t* __restrict__ tiles, int32_t max_tiles, int32_t* __restrict__ num_tiles) {
-  __shared__ int s_ids[kChunkIds];                        // 128 KB
+  __shared__ int hist_c[kHistCounters + kWave];           // [E + 1][C] copies (row E: ids
+                                                          // outside [0, E)), 32 KB
   __shared__ int hist[1024];
-  __shared__ int red[kSortWaves];
   __shared__ int wcount[kSortWaves];
   const int b = blockIdx.x;
   const int tid = threadIdx.x, lane = tid & (kWave - 1), wave = tid / kWave;
   const unsigned uE = (unsigned)E;
   const int n_chunks = (P + kChunkIds - 1) / kChunkIds;
+  // copies: the largest power of two <= 64 with C * E <= kHistCounters
+  int C = 64;
+  while (C > 1 && C * E > kHistCounters) C >>= 1;
+  const int cl = lane & (C - 1);
 
-  for (int e = tid; e < E; e += kSortThreads) hist[e] = 0;
+  auto hit = [&](int x) { return (b < E) ? (x == b) : (x != kPastEnd && (unsigned)x >= uE); };
+  for (int i = tid; i < C * (E + 1); i += kSortThreads) hist_c[i] = 0;
+  int v[kPerLane];
   for (int ch = 0; ch < n_chunks; ++ch) {
-    __syncthreads();                                       // s_ids free, hist zeroed
-    stage_ids(ids, P, (int64_t)ch * kChunkIds, s_ids);
-    __syncthreads();
-#pragma unroll 8
-    for (int j = 0; j < kPerLane; ++j) {
-      const int v = s_ids[j * kSortThreads + tid];
-      if ((unsigned)v < uE) atomicAdd(&hist[v], 1);
+    load_ids(ids, P, (int64_t)ch * kChunkIds, v);
+    if (ch == 0) __syncthreads();                          // copies zeroed
+#pragma unroll
+    for (int j = 0; j < kPerLane; ++j)
+      atomicAdd(&hist_c[((unsigned)v[j] < uE ? v[j] : E) * C + cl], 1);
+    if (ch == 0) {                     // the wave's matches in chunk 0, for the compaction
+      int mine = 0;
+#pragma unroll
+      for (int j = 0; j < kPerLane; ++j) mine += __popcll(__ballot(hit(v[j])));
+      if (lane == 0) wcount[wave] = mine;
     }
   }
   __syncthreads();
+  // Sum the copies: G lanes per expert (G the largest power of two with
+  // G * E <= 1024, so a group lies inside one wave), each over copies
+  // part, part + G, ... (rotated by e so neighbouring experts start in
+  // different banks), then a butterfly over the group.
+  {
+    int G = kWave;
+    while (G > 1 && G * E > kSortThreads) G >>= 1;
+    const int e = tid / G, part = tid & (G - 1);
+    int s = 0;
+    if (e < E)
+      for (int k = part; k < C; k += G) s += hist_c[e * C + ((k + e) & (C - 1))];
+    for (int off = G >> 1; off > 0; off >>= 1) s += __shfl_xor(s, off, kWave);
+    if (e < E && part == 0) hist[e] = s;
+  }
+  __syncthreads();
 
-  // Segment start / tile base of expert b, and the grand totals.
-  const int c = (tid < E) ? hist[tid] : 0;
-  const int t = (c + tile_m - 1) / tile_m;
-  const int seg_start = block_sum(tid < b ? c : 0, red);
-  const int tile_base = block_sum(tid < b ? t : 0, red);
-  const int valid_total = block_sum(c, red);
-  const int tile_total = block_sum(t, red);
+  // Segment start / tile base of expert b, and the grand totals: every wave
+  // forms them from the histogram on its own.
+  int seg_start = 0, tile_base = 0, valid_total = 0, tile_total = 0;
+  for (int e = lane; e < E; e += kWave) {
+    const int c = hist[e], t = (c + tile_m - 1) / tile_m;
+    seg_start += e < b ? c : 0;
+    tile_base += e < b ? t : 0;
+    valid_total += c;
+    tile_total += t;
+  }
+  seg_start = wave_total(seg_start);
+  tile_base = wave_total(tile_base);
+  valid_total = wave_total(valid_total);
+  tile_total = wave_total(tile_total);
 
-  // Stable compaction of this workgroup's pairs (see the file comment).
+  // Stable compaction of this workgroup's pairs (see the file comment).  One
+  // chunk: the ids are still in registers.
   int cursor = (b < E) ? seg_start : valid_total;
   for (int ch = 0; ch < n_chunks; ++ch) {
-    if (n_chunks > 1) {                                    // one chunk: still staged
-      __syncthreads();
-      stage_ids(ids, P, (int64_t)ch * kChunkIds, s_ids);
-      __syncthreads();
-    }
-    const int wbase = wave * (kChunkIds / kSortWaves);     // the wave's 2048 ids
-    uint64_t bal[kPerLane];                                // the wave's matches, kept for pass 2
-    int mine = 0;
+    if (n_chunks > 1) load_ids(ids, P, (int64_t)ch * kChunkIds, v);
+    if (ch > 0) {                      // chunk 0's counts came with the histogram
+      int mine = 0;
 #pragma unroll
-    for (int j = 0; j < kPerLane; ++j) {
-      const int v = s_ids[wbase + j * kWave + lane];
-      const bool hit = (b < E) ? (v == b) : (v != kPastEnd && (unsigned)v >= uE);
-      bal[j] = __ballot(hit);
-      mine += __popcll(bal[j]);
+      for (int j = 0; j < kPerLane; ++j) mine += __popcll(__ballot(hit(v[j])));
+      if (lane == 0) wcount[wave] = mine;
+      __syncthreads();
     }
-    if (lane == 0) wcount[wave] = mine;
-    __syncthreads();
     int before = 0, total = 0;
 #pragma unroll
     for (int i = 0; i < kSortWaves; ++i) {
@@ -118,16 +161,24 @@ __global__ __launch_bounds__(kSortThreads) void route_sort_kernel(
       total += n;
     }
     int pos = cursor + before;
-    const int64_t pbase = (int64_t)ch * kChunkIds + wbase;
+    const int64_t pbase = (int64_t)ch * kChunkIds + (int64_t)wave * kWaveIds;
+    // The ballots are taken again rather than kept (64 scalar registers);
+    // the empty asm keeps the compiler from reusing the first ones.
+#pragma unroll
+    for (int j = 0; j < kPerLane; ++j) asm volatile("" : "+v"(v[j]));
 #pragma unroll
     for (int j = 0; j < kPerLane; ++j) {
-      const uint64_t m = bal[j];
-      if ((m >> lane) & 1ull)
-        sorted_pairs[pos + __popcll(m & ((1ull << lane) - 1ull))] = (int)(pbase + j * kWave + lane);
+      const uint64_t m = __ballot(hit(v[j]));
+      if (m == 0ull) continue;                             // uniform: most rows match nothing
+      if ((m >> lane) & 1ull) {
+        const int rank = __builtin_amdgcn_mbcnt_hi((uint32_t)(m >> 32),
+                                                   __builtin_amdgcn_mbcnt_lo((uint32_t)m, 0u));
+        sorted_pairs[pos + rank] = (int)(pbase + j * kWave + lane);
+      }
       pos += __popcll(m);
     }
     cursor += total;
-    __syncthreads();                                       // wcount reused
+    if (ch + 1 < n_chunks) __syncthreads();               // wcount reused
   }
 
   if (b < E) {
