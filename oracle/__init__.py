@@ -47,4 +47,5 @@ from .grouped import (  # noqa: F401
     compare_slices,
     REL_L2_TOL,
 )
-from .moe import silu, swiglu, gate_up_swiglu, combine, down_combine  # noqa: F401
+from .moe import (silu, swiglu, gate_up_swiglu, combine, down_combine, OSS_ALPHA,  # noqa: F401
+                  OSS_LIMIT, swiglu_oss, gate_up_swiglu_oss)

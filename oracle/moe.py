@@ -20,6 +20,19 @@ Readings taken where the pages are silent:
 * the combine is the router-weighted sum over a token's slots; weights
   None means an unweighted sum (the router weight was already applied per
   pair).
+
+The pages also run gpt-oss's MXFP4 experts ("Receipts-driven engineering",
+"The numbers": the gpt-oss-120b MXFP4 serving row; the MXFP4 inference
+record, summary) without defining that model's expert activation.  Reading
+taken: gpt-oss's published expert MLP, whose fused gate_up weight
+interleaves the two projections (row 2j: gate j, row 2j + 1: up j) and whose
+activation clamps both and shifts the linear term,
+
+    act(g, u) = gc * sigmoid(alpha * gc) * (uc + 1),
+    gc = min(g, limit),  uc = min(max(u, -limit), limit),
+
+with alpha = 1.702 and limit = 7 (``swiglu_oss``).  The model's projection
+biases are not part of the products the pages define and are left out.
 """
 
 import numpy as np
@@ -27,7 +40,11 @@ import numpy as np
 from .bf16 import bf16_to_f32
 from .grouped import grouped_gemm
 
-__all__ = ["silu", "swiglu", "gate_up_swiglu", "combine", "down_combine"]
+__all__ = ["silu", "swiglu", "gate_up_swiglu", "combine", "down_combine", "OSS_ALPHA",
+           "OSS_LIMIT", "swiglu_oss", "gate_up_swiglu_oss"]
+
+OSS_ALPHA = 1.702
+OSS_LIMIT = 7.0
 
 
 def silu(z):
@@ -44,6 +61,23 @@ def swiglu(h):
         raise ValueError("gate_up width must be even")
     i = two_i // 2
     return silu(h[:, :i]) * h[:, i:]
+
+
+def swiglu_oss(h, alpha=OSS_ALPHA, limit=OSS_LIMIT):
+    """[P, 2I] gate_up products, gate and up interleaved (columns 2j, 2j+1)
+    -> [P, I]: the clamped, shifted gated unit of the module docstring."""
+    h = np.asarray(h, dtype=np.float64)
+    if h.shape[1] % 2:
+        raise ValueError("gate_up width must be even")
+    gate = np.minimum(h[:, 0::2], limit)
+    up = np.clip(h[:, 1::2], -limit, limit)
+    return gate / (1.0 + np.exp(-alpha * gate)) * (up + 1.0)
+
+
+def gate_up_swiglu_oss(x_bits, weights, topk_ids, num_experts, alpha=OSS_ALPHA,
+                       limit=OSS_LIMIT):
+    """gpt-oss activation of every routed pair's gate_up product: float64 [P, I]."""
+    return swiglu_oss(grouped_gemm(x_bits, weights, topk_ids, num_experts), alpha, limit)
 
 
 def gate_up_swiglu(x_bits, weights, topk_ids, num_experts):

@@ -87,3 +87,79 @@ def test_down_combine_brute_force():
                                                    for i in range(I))
     np.testing.assert_allclose(oracle.down_combine(act, W, ids, E, w), want, rtol=1e-12,
                                atol=1e-12)
+
+
+# ---- gpt-oss activation (interleaved gate/up, clamped, shifted) ----
+
+def _oss(g, u, **kw):
+    """act(g, u) through the oracle's [P, 2I] interface (one pair per row)."""
+    g, u = np.broadcast_arrays(np.asarray(g, np.float64), np.asarray(u, np.float64))
+    h = np.stack([g.ravel(), u.ravel()], axis=1)
+    return oracle.swiglu_oss(h, **kw).ravel().reshape(g.shape)
+
+
+def test_oss_gate_odd_part():
+    """sigmoid(t) + sigmoid(-t) = 1 makes act(g, u) - act(-g, u) = g (u + 1)
+    for |g| <= limit (a flipped sign, a dropped shift or alpha applied
+    outside the sigmoid breaks it)."""
+    g = np.linspace(-6.9, 6.9, 47)[:, None]
+    u = np.linspace(-6.5, 6.5, 11)[None, :]
+    np.testing.assert_allclose(_oss(g, u) - _oss(-g, u), g * (u + 1.0), rtol=0, atol=1e-13)
+
+
+def test_oss_zeros_and_shift():
+    u = np.linspace(-10, 10, 21)
+    assert not _oss(0.0, u).any()                          # gated part vanishes at g = 0
+    g = np.linspace(-9, 9, 19)
+    assert not _oss(g, -1.0).any()                         # the +1 shift cancels u = -1
+
+
+def test_oss_clamps():
+    g = np.linspace(-3, 3, 13)
+    np.testing.assert_array_equal(_oss(g, 50.0), _oss(g, 7.0))       # up clamped above
+    np.testing.assert_array_equal(_oss(g, -50.0), _oss(g, -7.0))     # and below
+    u = np.linspace(-3, 3, 13)
+    np.testing.assert_array_equal(_oss(100.0, u), _oss(7.0, u))      # gate clamped above only
+    # no lower clamp on the gate: a very negative gate drives the unit to 0
+    # from below, unlike a clamp at -7 (which would give about -7e-6 * (u+1))
+    assert np.all(np.abs(_oss(-30.0, u)) < 1e-20)
+    assert np.all(np.abs(_oss(-7.0, u + 4.0)) > 1e-6)
+
+
+def test_oss_alpha_against_silu():
+    """g * sigmoid(alpha g) = silu(alpha g) / alpha, checked against the
+    pinned silu at alpha = 1 and 2 with no clamping in reach."""
+    g = np.linspace(-5, 5, 41)[:, None]
+    u = np.array([[-0.5, 0.0, 2.0]])
+    for a in (1.0, 2.0):
+        want = oracle.silu(a * g) / a * (u + 1.0)
+        np.testing.assert_allclose(_oss(g, u, alpha=a, limit=1e9), want, rtol=1e-14, atol=1e-15)
+    # slope of the gated part at 0 is sigmoid(0) = 1/2, whatever alpha
+    eps = 1e-6
+    slope = (_oss(eps, 0.0) - _oss(-eps, 0.0)) / (2 * eps)
+    assert slope == pytest.approx(0.5, rel=1e-9)
+
+
+def test_oss_interleaved_layout():
+    """Gate rows are the even rows of the fused weight: zero even rows give
+    act = 0; zero odd rows give act = gate * sigmoid(alpha gate) exactly as
+    computed from the even-row product.  The split-halves layout fails both."""
+    g = np.random.default_rng(4)
+    E, I, H = 2, 4, 64
+    x = wl.draw_bf16(g, (3, H))
+    ids = np.array([[0, 1], [1, 0], [1, 1]])
+    W = (g.standard_normal((E, 2 * I, H)) * 0.2).astype(np.float32)
+    W_gate0 = W.copy()
+    W_gate0[:, 0::2] = 0
+    assert not oracle.gate_up_swiglu_oss(x, W_gate0, ids, E).any()
+    W_up0 = W.copy()
+    W_up0[:, 1::2] = 0
+    act = oracle.gate_up_swiglu_oss(x, W_up0, ids, E)
+    xf = oracle.bf16_to_f32(x).astype(np.float64)
+    gate = np.stack([xf[p // 2] @ W[ids.reshape(-1)[p], 0::2].astype(np.float64).T
+                     for p in range(6)])
+    assert np.abs(gate).max() < 7.0                        # no clamping in reach
+    np.testing.assert_allclose(act, oracle.silu(oracle.OSS_ALPHA * gate) / oracle.OSS_ALPHA,
+                               rtol=1e-12, atol=1e-12)
+    with pytest.raises(ValueError):
+        oracle.swiglu_oss(np.zeros((2, 5)))
