@@ -22,11 +22,15 @@ __all__ = [
     "gq_nf4_grouped_gemv", "gq_mxfp4_grouped_gemv", "gq_nf4_grouped_gemm",
     "gq_mxfp4_grouped_gemm", "gq_nf4_grouped_dgrad", "gq_mxfp4_grouped_dgrad",
     "gq_nf4_grouped_gemv_swiglu", "gq_nf4_grouped_gemm_swiglu", "gq_nf4_grouped_gemv_down_combine",
-    "gq_moe_combine", "gq_act_split_e4m3", "gq_mxfp4_grouped_gemm_scaled", "Route",
+    "gq_moe_combine", "gq_act_split_e4m3", "gq_mxfp4_grouped_gemm_scaled",
+    "gq_mxfp4_grouped_gemv_swiglu", "gq_mxfp4_grouped_gemm_scaled_swiglu", "OSS_ALPHA",
+    "OSS_LIMIT", "Route",
 ]
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
 TILE_M = 256                       # the tile height the grouped GEMM kernels use
+OSS_ALPHA = 1.702                  # gpt-oss gated unit: sigmoid slope
+OSS_LIMIT = 7.0                    # gpt-oss gated unit: clamp
 
 EXPORTED_SYMBOLS = (
     "gq_status_string", "gq_route_max_tiles", "gq_route_sort", "gq_nf4_decode",
@@ -34,9 +38,10 @@ EXPORTED_SYMBOLS = (
     "gq_mxfp4_grouped_gemm", "gq_nf4_grouped_dgrad", "gq_mxfp4_grouped_dgrad",
     "gq_nf4_grouped_gemv_swiglu", "gq_nf4_grouped_gemm_swiglu", "gq_nf4_grouped_gemv_down_combine",
     "gq_moe_combine", "gq_act_split_e4m3", "gq_mxfp4_grouped_gemm_scaled",
+    "gq_mxfp4_grouped_gemv_swiglu", "gq_mxfp4_grouped_gemm_scaled_swiglu",
 )
 
-_i32, _i64, _p = ctypes.c_int32, ctypes.c_int64, ctypes.c_void_p
+_i32, _i64, _p, _f32 = ctypes.c_int32, ctypes.c_int64, ctypes.c_void_p, ctypes.c_float
 _SIGNATURES = {
     "gq_status_string": (ctypes.c_char_p, [ctypes.c_int]),
     "gq_route_max_tiles": (_i32, [_i32, _i32, _i32, _i32]),
@@ -65,6 +70,11 @@ _SIGNATURES = {
     "gq_act_split_e4m3": (ctypes.c_int, [_p, _i32, _i32, _i64, _p, _p, _p]),
     "gq_mxfp4_grouped_gemm_scaled": (ctypes.c_int, [_p, _p, _i32, _i32, _p, _p, _i32, _i32, _i32,
                                                     _p, _p, _p, _p, _p, _i32, _i32, _p, _p]),
+    "gq_mxfp4_grouped_gemv_swiglu": (ctypes.c_int, [_p, _i32, _i32, _i64, _p, _p, _i32, _i32, _p,
+                                                    _i32, _f32, _f32, _p, _p]),
+    "gq_mxfp4_grouped_gemm_scaled_swiglu": (ctypes.c_int, [_p, _p, _i32, _i32, _p, _p, _i32,
+                                                           _i32, _i32, _f32, _f32, _p, _p, _p,
+                                                           _p, _i32, _i32, _p, _p]),
 }
 
 _lib = None
@@ -285,6 +295,27 @@ def gq_mxfp4_grouped_gemv(x, blocks, scales, topk_ids, pair_scale=None, out=None
     return out
 
 
+def gq_mxfp4_grouped_gemv_swiglu(x, blocks, scales, topk_ids, alpha=OSS_ALPHA, limit=OSS_LIMIT,
+                                 out=None):
+    """Decode gate_up GEMV on MXFP4 experts with gpt-oss's gated unit fused:
+    blocks [E, 2I, K] with gate row 2j and up row 2j + 1; returns bf16
+    [rows*topk, I] = gc * sigmoid(alpha gc) * (uc + 1) (gc = min(gate, limit),
+    uc = up clipped to [-limit, limit])."""
+    lib = load_library()
+    rows, K, xs = _x_args(x)
+    E, N2, Kw = _mx_bank(blocks, scales)
+    if Kw != K or N2 % 2:
+        raise ValueError("x and blocks disagree on K, or the gate_up width is odd")
+    _dev(topk_ids, "topk_ids", torch.int32, 2)
+    P = _gemv_pairs(topk_ids, rows)
+    out = _out(out, P, N2 // 2, x.device)
+    st = lib.gq_mxfp4_grouped_gemv_swiglu(_ptr(x), rows, K, xs, _ptr(blocks), _ptr(scales), E, N2,
+                                          _ptr(topk_ids), topk_ids.shape[1], float(alpha),
+                                          float(limit), _ptr(out), _stream(x))
+    _check(st, "gq_mxfp4_grouped_gemv_swiglu")
+    return out
+
+
 def _route_ptrs(route):
     return (_ptr(route.expert_offsets), _ptr(route.sorted_pairs), _ptr(route.tiles),
             _ptr(route.num_tiles), route.max_tiles, route.tile_m)
@@ -474,4 +505,32 @@ def gq_mxfp4_grouped_gemm_scaled(x_split, blocks, scales, route, pair_scale=None
                                           _ptr(_scale(pair_scale, P)), *_route_ptrs(route),
                                           _ptr(out), _stream(xq))
     _check(st, "gq_mxfp4_grouped_gemm_scaled")
+    return out
+
+
+def gq_mxfp4_grouped_gemm_scaled_swiglu(x_split, blocks, scales, route, alpha=OSS_ALPHA,
+                                        limit=OSS_LIMIT, out=None):
+    """Prefill gate_up GEMM on the block-scaled fp4 instruction with gpt-oss's
+    gated unit in the epilogue: blocks [E, 2I, K] (gate row 2j, up row
+    2j + 1); returns bf16 [rows*topk, I]."""
+    lib = load_library()
+    xq, xsc = x_split
+    _dev(xq, "x_split codes", torch.uint8, 2)
+    _dev(xsc, "x_split scales", torch.uint8, 2)
+    E, N2, K = _mx_bank(blocks, scales)
+    if N2 % 2:
+        raise ValueError("the gate_up width is odd")
+    rows = xq.shape[0]
+    cshape, sshape = split_sizes(rows, K)
+    if tuple(xq.shape) != cshape or tuple(xsc.shape) != sshape:
+        raise ValueError("x_split does not match the weights' K")
+    if route.rows != rows or route.num_experts != E:
+        raise ValueError("x_split and route disagree")
+    P = rows * route.topk
+    out = _out(out, P, N2 // 2, xq.device)
+    st = lib.gq_mxfp4_grouped_gemm_scaled_swiglu(_ptr(xq), _ptr(xsc), rows, K, _ptr(blocks),
+                                                 _ptr(scales), E, N2, route.topk, float(alpha),
+                                                 float(limit), *_route_ptrs(route), _ptr(out),
+                                                 _stream(xq))
+    _check(st, "gq_mxfp4_grouped_gemm_scaled_swiglu")
     return out

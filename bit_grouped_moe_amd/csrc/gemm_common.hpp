@@ -42,6 +42,7 @@ struct GemmArgs {
   int n_col_tiles;             // ceil(Nout / output columns per tile)
   int n_logical;               // max_tiles * n_col_tiles
   uint16_t* out;               // [P, Nout]
+  float act_alpha, act_limit;  // gpt-oss gated unit (kernels with the activation epilogue)
 };
 
 typedef __attribute__((address_space(3))) void lds_void_t;
@@ -176,6 +177,34 @@ __device__ __forceinline__ void store_wide_rows(const f32x16 (&acc)[kSub][2], in
       }
     }
   }
+}
+
+// gpt-oss gated unit of one (gate, up) pair: the gate clamped above at
+// `limit`, the up value clipped to [-limit, limit],
+//   act = gc * sigmoid(alpha * gc) * (uc + 1),  float32.
+__device__ __forceinline__ float oss_act(float gate, float up, float alpha, float limit) {
+  const float gc = fminf(gate, limit);
+  const float uc = fminf(fmaxf(up, -limit), limit);
+  return gc / (1.0f + expf(-alpha * gc)) * (uc + 1.0f);
+}
+
+// Activation epilogue of one transposed accumulator block whose 32 columns
+// are 16 interleaved (gate, up) weight-row pairs: lane (lr, lh) holds its
+// row at columns 8q + 4 lh + [0, 4), i.e. the pairs of output columns
+// 4q + 2 lh and 4q + 2 lh + 1.  Two v_permlane32_swap exchanges give lane
+// half h the output columns 8h + [0, 8), written as one 16-byte piece.
+__device__ __forceinline__ void store_block_act(const float (&v)[16], uint16_t* orow, int lh,
+                                                float alpha, float limit) {
+  uint32_t o[4];                                           // output columns 4q + 2 lh + [0, 2)
+#pragma unroll
+  for (int q = 0; q < 4; ++q)
+    o[q] = pack_bf16x2(oss_act(v[4 * q], v[4 * q + 1], alpha, limit),
+                       oss_act(v[4 * q + 2], v[4 * q + 3], alpha, limit));
+  // half 0: own o0 | partner o0 | own o1 | partner o1 = columns 0..7;
+  // half 1: partner o2 | own o2 | partner o3 | own o3 = columns 8..15
+  const auto a = __builtin_amdgcn_permlane32_swap(o[0], o[2], false, false);
+  const auto b = __builtin_amdgcn_permlane32_swap(o[1], o[3], false, false);
+  *reinterpret_cast<u32x4*>(orow + 8 * lh) = u32x4{a[0], a[1], b[0], b[1]};
 }
 
 // Host: argument checks shared by the grouped GEMM entry points.

@@ -161,7 +161,7 @@ __device__ __forceinline__ void step_barrier() {
   asm volatile("" ::: "memory");
 }
 
-template <int kSub>
+template <int kSub, bool kAct>
 __device__ __forceinline__ void mx8_columns(const GemmArgs& g, const TileInfo& t, int tid,
                                             uint8_t* A0, uint8_t* A1, uint32_t* S0, uint32_t* S1,
                                             int* pair_s, int* row_s, float* scale_s) {
@@ -169,7 +169,10 @@ __device__ __forceinline__ void mx8_columns(const GemmArgs& g, const TileInfo& t
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6), lane = tid & 63;
   const int lr = lane & 31, lh = lane >> 5;
   const int valid = t.valid;
-  const int jcol = t.n0 + 64 * wave + lr;
+  // weight rows of the tile: t.n0 counts output columns, two weight rows
+  // (gate, up) per output column with the activation epilogue
+  const int wn0 = kAct ? 2 * t.n0 : t.n0;
+  const int jcol = wn0 + 64 * wave + lr;
   // K tail (K % 64 == 32): lane half 1 has no weights in the last step; it
   // re-reads half 0 (in bounds) against the zero activations of the pad.
   auto load = [&](int ks) {
@@ -319,9 +322,31 @@ __device__ __forceinline__ void mx8_columns(const GemmArgs& g, const TileInfo& t
   else if (allcols && nrows == I5::value) run_loop(I5{});
   else run_loop(std::integral_constant<int, -1>{});
 
-  store_wide_rows<kSub>(acc, nrows, valid, pair_s, scale_s, g, t.n0, wave, lr, lh);
+  if constexpr (kAct) {
+#pragma unroll
+    for (int i = 0; i < kSub; ++i) {
+      if (i >= nrows) continue;
+      const int m = 32 * i + lr;
+      const int p = pair_s[m];
+#pragma unroll
+      for (int cb = 0; cb < 2; ++cb) {
+        const int col = t.n0 + 32 * wave + 16 * cb;         // output column (Nout % 16 == 0)
+        if (m < valid && col < g.Nout) {
+          float v[16];
+#pragma unroll
+          for (int r = 0; r < 16; ++r) v[r] = acc[i][cb][r];
+          store_block_act(v, g.out + (int64_t)p * g.Nout + col, lh, g.act_alpha, g.act_limit);
+        }
+      }
+    }
+  } else {
+    store_wide_rows<kSub>(acc, nrows, valid, pair_s, scale_s, g, t.n0, wave, lr, lh);
+  }
 }
 
+// kAct: gate_up product with the gpt-oss gated unit applied in the epilogue
+// (weight rows 2j, 2j + 1 -> output column j of an [P, N/2] result).
+template <bool kAct>
 __global__ __launch_bounds__(kGemmThreads, 1) void grouped_gemm_mx8_kernel(GemmArgs g) {
   // separate arrays: an LDS-direct load into one buffer does not alias reads
   // of the other
@@ -334,9 +359,11 @@ __global__ __launch_bounds__(kGemmThreads, 1) void grouped_gemm_mx8_kernel(GemmA
   __shared__ float scale_s[kTM];                           // its pair weight (1 if none)
   const int tid = threadIdx.x;
   TileInfo t;
-  if (!tile_head<kXN>(g, tid, t)) return;
-  if (t.valid <= kMx8Rows) mx8_columns<4>(g, t, tid, A0, A1, S0, S1, pair_s, row_s, scale_s);
-  else mx8_columns<8>(g, t, tid, A0, A1, S0, S1, pair_s, row_s, scale_s);
+  if (!tile_head<kAct ? kXN / 2 : kXN>(g, tid, t)) return;
+  if (t.valid <= kMx8Rows)
+    mx8_columns<4, kAct>(g, t, tid, A0, A1, S0, S1, pair_s, row_s, scale_s);
+  else
+    mx8_columns<8, kAct>(g, t, tid, A0, A1, S0, S1, pair_s, row_s, scale_s);
 }
 
 static inline int64_t split_kp(int64_t K) { return (K + kTK - 1) / kTK * kTK; }
@@ -359,17 +386,20 @@ extern "C" int gq_act_split_e4m3(const uint16_t* x, int32_t rows, int32_t K, int
   return launch_status();
 }
 
-extern "C" int gq_mxfp4_grouped_gemm_scaled(const uint8_t* x_codes, const uint8_t* x_scales,
-                                            int32_t rows, int32_t K, const uint8_t* blocks,
-                                            const uint8_t* scales, int32_t num_experts, int32_t N,
-                                            int32_t topk, const float* pair_scale,
-                                            const int32_t* expert_offsets,
-                                            const int32_t* sorted_pairs, const int32_t* tiles,
-                                            const int32_t* num_tiles, int32_t max_tiles,
-                                            int32_t tile_m, uint16_t* out, hipStream_t stream) {
-  using namespace gq;
+namespace gq {
+
+template <bool kAct>
+static int mx8_entry(const uint8_t* x_codes, const uint8_t* x_scales, int32_t rows, int32_t K,
+                     const uint8_t* blocks, const uint8_t* scales, int32_t num_experts, int32_t N,
+                     int32_t topk, const float* pair_scale, float alpha, float limit,
+                     const int32_t* expert_offsets, const int32_t* sorted_pairs,
+                     const int32_t* tiles, const int32_t* num_tiles, int32_t max_tiles,
+                     int32_t tile_m, uint16_t* out, hipStream_t stream) {
   if (rows < 0 || topk < 1 || num_experts < 1 || N < 1 || N % 32 || K <= 0 || K % 32)
     return kInvalid;
+  if (kAct && !(limit >= 0.f && limit < 3.4e38f && alpha == alpha && alpha > -3.4e38f &&
+                alpha < 3.4e38f))
+    return kInvalid;                                       // finite alpha, limit >= 0
   if (tile_m != kTM) return kNotSupported;
   const int64_t P = (int64_t)rows * topk;
   if (P >= INT32_MAX) return kNotSupported;
@@ -392,17 +422,44 @@ extern "C" int gq_mxfp4_grouped_gemm_scaled(const uint8_t* x_codes, const uint8_
   g.xs = x_scales;
   g.xs_stride = Kp / 16;
   g.codes = blocks; g.scl = scales;
-  g.Nw = N; g.Kw = K; g.Kc = K; g.Nout = N;
+  g.Nw = N; g.Kw = K; g.Kc = K; g.Nout = kAct ? N / 2 : N;
   g.E = num_experts; g.topk = topk; g.P = (int)P; g.pair_scale = pair_scale;
   g.offsets = expert_offsets; g.sorted_pairs = sorted_pairs; g.tiles = tiles;
   g.num_tiles = num_tiles; g.out = out;
-  g.n_col_tiles = (N + kXN - 1) / kXN;
+  g.act_alpha = alpha; g.act_limit = limit;
+  g.n_col_tiles = (N + kXN - 1) / kXN;                     // 256 weight rows per tile
   const int64_t n_logical = (int64_t)max_tiles * g.n_col_tiles;
   const int64_t group = 8LL * g.n_col_tiles;
   const int64_t grid = ((n_logical + group - 1) / group) * group;
   if (grid > INT32_MAX) return kNotSupported;
   g.n_logical = (int)n_logical;
-  hipLaunchKernelGGL(grouped_gemm_mx8_kernel, dim3((unsigned)grid), dim3(kGemmThreads), 0, stream,
-                     g);
+  hipLaunchKernelGGL(grouped_gemm_mx8_kernel<kAct>, dim3((unsigned)grid), dim3(kGemmThreads), 0,
+                     stream, g);
   return launch_status();
+}
+
+}  // namespace gq
+
+extern "C" int gq_mxfp4_grouped_gemm_scaled(const uint8_t* x_codes, const uint8_t* x_scales,
+                                            int32_t rows, int32_t K, const uint8_t* blocks,
+                                            const uint8_t* scales, int32_t num_experts, int32_t N,
+                                            int32_t topk, const float* pair_scale,
+                                            const int32_t* expert_offsets,
+                                            const int32_t* sorted_pairs, const int32_t* tiles,
+                                            const int32_t* num_tiles, int32_t max_tiles,
+                                            int32_t tile_m, uint16_t* out, hipStream_t stream) {
+  return gq::mx8_entry<false>(x_codes, x_scales, rows, K, blocks, scales, num_experts, N, topk,
+                              pair_scale, 0.f, 0.f, expert_offsets, sorted_pairs, tiles,
+                              num_tiles, max_tiles, tile_m, out, stream);
+}
+
+extern "C" int gq_mxfp4_grouped_gemm_scaled_swiglu(
+    const uint8_t* x_codes, const uint8_t* x_scales, int32_t rows, int32_t K,
+    const uint8_t* blocks, const uint8_t* scales, int32_t num_experts, int32_t N, int32_t topk,
+    float alpha, float limit, const int32_t* expert_offsets, const int32_t* sorted_pairs,
+    const int32_t* tiles, const int32_t* num_tiles, int32_t max_tiles, int32_t tile_m,
+    uint16_t* act, hipStream_t stream) {
+  return gq::mx8_entry<true>(x_codes, x_scales, rows, K, blocks, scales, num_experts, N, topk,
+                             nullptr, alpha, limit, expert_offsets, sorted_pairs, tiles,
+                             num_tiles, max_tiles, tile_m, act, stream);
 }

@@ -80,12 +80,17 @@ __device__ __forceinline__ float segment_dot(const float* lut, u32x4 c, float am
 // into SGPRs (every kernel here is compiled with kernel-argument preload),
 // so the expert-id load issues without waiting for a kernel-argument load;
 // the segment layout is derived from K rather than passed.
-template <bool kMx, int kIter, bool kWaveRows, bool kGlu>
+// kAct: 0 plain product; 1 SwiGLU with gate rows [0, N/2) and up rows
+// [N/2, N); 2 the gpt-oss gated unit with gate row 2j and up row 2j + 1
+// (alpha, limit).  With an activation a workgroup takes output columns
+// [n0, n0 + R/2) and the gate and up rows of each.
+template <bool kMx, int kIter, bool kWaveRows, int kAct>
 __global__ __launch_bounds__(kGemvMaxThreads) void grouped_gemv_kernel(
     const int32_t* __restrict__ ids, const uint16_t* __restrict__ x,
     const uint8_t* __restrict__ codes, const void* __restrict__ scl, int K, int N, int E,
     int x_stride, int topk, int P, const float* __restrict__ pair_scale,
-    uint16_t* __restrict__ out) {
+    uint16_t* __restrict__ out, float alpha, float limit) {
+  constexpr bool kGlu = kAct != 0;
   __shared__ float lut[16];
   __shared__ float red[kWaveRows ? 1 : kIter * (kGemvMaxThreads + 32)];
 
@@ -106,8 +111,6 @@ __global__ __launch_bounds__(kGemvMaxThreads) void grouped_gemv_kernel(
   const int lane = tid & (kWave - 1);
   const int p0 = blockIdx.y;
   const int R = G * kIter;                          // weight rows per workgroup
-  // kGlu: the weight holds gate rows [0, N/2) then up rows [N/2, N); a
-  // workgroup takes output columns [n0, n0 + R/2) and both halves' rows.
   constexpr int kHalf = kIter / 2;
   const int Nout = kGlu ? N / 2 : N;                // output columns per pair
   const int Rout = kGlu ? R / 2 : R;
@@ -117,9 +120,12 @@ __global__ __launch_bounds__(kGemvMaxThreads) void grouped_gemv_kernel(
   const bool active = kWaveRows ? s < S : tid < S * G;
   // weight row of row slot gg, iteration i (clamped into the matrix)
   auto wrow = [&](int gg, int i) -> int {
-    if constexpr (kGlu) {
+    if constexpr (kAct == 1) {
       const int j = min(n0 + gg + G * (i % kHalf), Nout - 1);
       return i < kHalf ? j : Nout + j;
+    } else if constexpr (kAct == 2) {
+      const int j = min(n0 + gg + G * (i % kHalf), Nout - 1);
+      return 2 * j + (i < kHalf ? 0 : 1);
     } else {
       return min(n0 + gg + G * i, N - 1);
     }
@@ -179,6 +185,15 @@ __global__ __launch_bounds__(kGemvMaxThreads) void grouped_gemv_kernel(
   // ---- the rows of one pair: kWaveRows -> row i's total on the last lane of
   // its segment group; otherwise thread r < R holds row r's total ----
   float vals[kWaveRows ? kIter : 1];
+  auto act_pair = [&](float gate, float up) {
+    if constexpr (kAct == 2) {
+      const float gc = fminf(gate, limit);
+      const float uc = fminf(fmaxf(up, -limit), limit);
+      return gc / (1.0f + expf(-alpha * gc)) * (uc + 1.0f);
+    } else {
+      return silu_f32(gate) * up;
+    }
+  };
   auto compute_pair = [&]() {
     float xf[32];
 #pragma unroll
@@ -196,7 +211,7 @@ __global__ __launch_bounds__(kGemvMaxThreads) void grouped_gemv_kernel(
       }
       if constexpr (kGlu) {
 #pragma unroll
-        for (int i = 0; i < kHalf; ++i) vals[i] = silu_f32(vals[i]) * vals[i + kHalf];
+        for (int i = 0; i < kHalf; ++i) vals[i] = act_pair(vals[i], vals[i + kHalf]);
       }
     } else {
       constexpr int kStride = kGemvMaxThreads + 32;            // pad: spreads banks
@@ -245,7 +260,7 @@ __global__ __launch_bounds__(kGemvMaxThreads) void grouped_gemv_kernel(
       if constexpr (kGlu) {                  // gate row r pairs with up row r + R/2
         if (tid < R) red[tid] = vals[0];
         lds_barrier();
-        vals[0] = tid < Rout ? silu_f32(red[tid]) * red[tid + Rout] : 0.f;
+        vals[0] = tid < Rout ? act_pair(red[tid], red[tid + Rout]) : 0.f;
         lds_barrier();
       }
     }
@@ -298,17 +313,19 @@ __global__ __launch_bounds__(kGemvMaxThreads) void grouped_gemv_kernel(
   }
 }
 
-template <bool kMx, int kIter, bool kGlu>
+template <bool kMx, int kIter, int kAct>
 static void launch_gemv_iter(dim3 grid, int NT, bool wave_rows, hipStream_t stream,
                              const uint16_t* x, int x_stride, int K, const uint8_t* codes,
                              const void* scl, int N, int E, const int32_t* ids, int topk, int P,
-                             const float* pair_scale, uint16_t* out) {
+                             const float* pair_scale, uint16_t* out, float alpha, float limit) {
   if (wave_rows)
-    hipLaunchKernelGGL((grouped_gemv_kernel<kMx, kIter, true, kGlu>), grid, dim3(NT), 0, stream,
-                       ids, x, codes, scl, K, N, E, x_stride, topk, P, pair_scale, out);
+    hipLaunchKernelGGL((grouped_gemv_kernel<kMx, kIter, true, kAct>), grid, dim3(NT), 0, stream,
+                       ids, x, codes, scl, K, N, E, x_stride, topk, P, pair_scale, out, alpha,
+                       limit);
   else
-    hipLaunchKernelGGL((grouped_gemv_kernel<kMx, kIter, false, kGlu>), grid, dim3(NT), 0, stream,
-                       ids, x, codes, scl, K, N, E, x_stride, topk, P, pair_scale, out);
+    hipLaunchKernelGGL((grouped_gemv_kernel<kMx, kIter, false, kAct>), grid, dim3(NT), 0, stream,
+                       ids, x, codes, scl, K, N, E, x_stride, topk, P, pair_scale, out, alpha,
+                       limit);
 }
 
 // Segment lanes: S segments of 32 weights per row.  S <= 64: a row's
@@ -324,15 +341,18 @@ static void segment_layout(int K, int& S, int& W, int& G, int& NT) {
   NT = S > kWave ? ((S * G + kWave - 1) / kWave) * kWave : kGemvMaxThreads;
 }
 
-template <bool kMx, bool kGlu>
+template <bool kMx, int kAct>
 static int launch_gemv(const uint16_t* x, int32_t rows, int32_t K, int64_t x_stride,
                        const uint8_t* codes, const void* scl, int32_t E, int32_t N,
                        const int32_t* ids, int32_t topk, const float* pair_scale, uint16_t* out,
-                       hipStream_t stream) {
+                       hipStream_t stream, float alpha = 0.f, float limit = 0.f) {
   if (!x || !codes || !scl || !ids || !out) return kInvalid;
   if (rows < 1 || topk < 1 || E < 1 || N < 1 || K <= 0) return kInvalid;
   if (K % (kMx ? 32 : 64)) return kInvalid;
-  if (kGlu && N % 2) return kInvalid;
+  if (kAct != 0 && N % 2) return kInvalid;
+  if (kAct == 2 && !(limit >= 0.f && limit < 3.4e38f && alpha == alpha && alpha > -3.4e38f &&
+                     alpha < 3.4e38f))
+    return kInvalid;                                       // finite alpha, limit >= 0
   if (x_stride < K || x_stride % 8) return kInvalid;
   if (!aligned16(x) || !aligned16(codes) || !aligned4(ids) || !aligned4(out)) return kInvalid;
   if (!kMx && !aligned4(scl)) return kInvalid;
@@ -355,16 +375,16 @@ static int launch_gemv(const uint16_t* x, int32_t rows, int32_t K, int64_t x_str
   const dim3 grid((N + R - 1) / R, (unsigned)P);
   switch (iter) {
     case 8:
-      launch_gemv_iter<kMx, 8, kGlu>(grid, NT, S <= kWave, stream, x, (int)x_stride, K, codes, scl,
-                                     N, E, ids, topk, (int)P, pair_scale, out);
+      launch_gemv_iter<kMx, 8, kAct>(grid, NT, S <= kWave, stream, x, (int)x_stride, K, codes, scl,
+                                     N, E, ids, topk, (int)P, pair_scale, out, alpha, limit);
       break;
     case 4:
-      launch_gemv_iter<kMx, 4, kGlu>(grid, NT, S <= kWave, stream, x, (int)x_stride, K, codes, scl,
-                                     N, E, ids, topk, (int)P, pair_scale, out);
+      launch_gemv_iter<kMx, 4, kAct>(grid, NT, S <= kWave, stream, x, (int)x_stride, K, codes, scl,
+                                     N, E, ids, topk, (int)P, pair_scale, out, alpha, limit);
       break;
     default:
-      launch_gemv_iter<kMx, 2, kGlu>(grid, NT, S <= kWave, stream, x, (int)x_stride, K, codes, scl,
-                                     N, E, ids, topk, (int)P, pair_scale, out);
+      launch_gemv_iter<kMx, 2, kAct>(grid, NT, S <= kWave, stream, x, (int)x_stride, K, codes, scl,
+                                     N, E, ids, topk, (int)P, pair_scale, out, alpha, limit);
       break;
   }
   return launch_status();
@@ -554,7 +574,7 @@ extern "C" int gq_nf4_grouped_gemv(const uint16_t* x, int32_t rows, int32_t K, i
                                    const uint8_t* codes, const float* absmax, int32_t num_experts,
                                    int32_t N, const int32_t* topk_ids, int32_t topk,
                                    const float* pair_scale, uint16_t* out, hipStream_t stream) {
-  return gq::launch_gemv<false, false>(x, rows, K, x_stride, codes, absmax, num_experts, N,
+  return gq::launch_gemv<false, 0>(x, rows, K, x_stride, codes, absmax, num_experts, N,
                                        topk_ids, topk, pair_scale, out, stream);
 }
 
@@ -563,7 +583,7 @@ extern "C" int gq_nf4_grouped_gemv_swiglu(const uint16_t* x, int32_t rows, int32
                                           const float* absmax, int32_t num_experts, int32_t N,
                                           const int32_t* topk_ids, int32_t topk, uint16_t* act,
                                           hipStream_t stream) {
-  return gq::launch_gemv<false, true>(x, rows, K, x_stride, codes, absmax, num_experts, N,
+  return gq::launch_gemv<false, 1>(x, rows, K, x_stride, codes, absmax, num_experts, N,
                                       topk_ids, topk, nullptr, act, stream);
 }
 
@@ -598,6 +618,15 @@ extern "C" int gq_mxfp4_grouped_gemv(const uint16_t* x, int32_t rows, int32_t K,
                                      int32_t num_experts, int32_t N, const int32_t* topk_ids,
                                      int32_t topk, const float* pair_scale, uint16_t* out,
                                      hipStream_t stream) {
-  return gq::launch_gemv<true, false>(x, rows, K, x_stride, blocks, scales, num_experts, N,
-                                      topk_ids, topk, pair_scale, out, stream);
+  return gq::launch_gemv<true, 0>(x, rows, K, x_stride, blocks, scales, num_experts, N,
+                                  topk_ids, topk, pair_scale, out, stream);
+}
+
+extern "C" int gq_mxfp4_grouped_gemv_swiglu(const uint16_t* x, int32_t rows, int32_t K,
+                                            int64_t x_stride, const uint8_t* blocks,
+                                            const uint8_t* scales, int32_t num_experts, int32_t N,
+                                            const int32_t* topk_ids, int32_t topk, float alpha,
+                                            float limit, uint16_t* act, hipStream_t stream) {
+  return gq::launch_gemv<true, 2>(x, rows, K, x_stride, blocks, scales, num_experts, N,
+                                  topk_ids, topk, nullptr, act, stream, alpha, limit);
 }

@@ -233,6 +233,22 @@ int gq_mxfp4_grouped_gemm(const uint16_t* x, int32_t rows, int32_t K, int64_t x_
  *   max_tiles below the bound.
  * NotSupported: tile_m != 256, rows*topk >= 2^31, rows*2*Kp >= 2^31, grid
  *   beyond 2^31 blocks.  rows == 0 enqueues nothing.
+ *
+ * gq_mxfp4_grouped_gemm_scaled_swiglu: the gate_up product of gpt-oss's
+ * experts with their gated unit applied in the epilogue.  The pages run
+ * gpt-oss MXFP4 experts ("Receipts-driven engineering", "The numbers") but
+ * do not define the activation; the reading of this library is gpt-oss's
+ * published expert MLP, whose fused gate_up weight interleaves gate row j
+ * (row 2j) and up row j (row 2j + 1):
+ *
+ *   g = sum_k split(x)[p/topk, k] * W[2j, k],  u = ... W[2j + 1, k]
+ *   act[p, j] = bf16( gc * sigmoid(alpha * gc) * (uc + 1) ),
+ *   gc = min(g, limit),  uc = min(max(u, -limit), limit)
+ *
+ * in float32 (gpt-oss: alpha = 1.702, limit = 7).  blocks/scales [E, N, K]
+ * with N = 2I; act uint16 bf16 [rows*topk, I], rows of dropped pairs zero.
+ * No pair_scale.  Errors as gq_mxfp4_grouped_gemm_scaled, plus
+ * InvalidValue for a non-finite alpha or limit, or limit < 0.
  */
 int gq_act_split_e4m3(const uint16_t* x, int32_t rows, int32_t K, int64_t x_stride,
                       uint8_t* codes, uint8_t* scales, hipStream_t stream);
@@ -243,6 +259,14 @@ int gq_mxfp4_grouped_gemm_scaled(const uint8_t* x_codes, const uint8_t* x_scales
                                  const int32_t* sorted_pairs, const int32_t* tiles,
                                  const int32_t* num_tiles, int32_t max_tiles, int32_t tile_m,
                                  uint16_t* out, hipStream_t stream);
+int gq_mxfp4_grouped_gemm_scaled_swiglu(const uint8_t* x_codes, const uint8_t* x_scales,
+                                        int32_t rows, int32_t K, const uint8_t* blocks,
+                                        const uint8_t* scales, int32_t num_experts, int32_t N,
+                                        int32_t topk, float alpha, float limit,
+                                        const int32_t* expert_offsets,
+                                        const int32_t* sorted_pairs, const int32_t* tiles,
+                                        const int32_t* num_tiles, int32_t max_tiles,
+                                        int32_t tile_m, uint16_t* act, hipStream_t stream);
 
 /* ------------------------------------------------------------------------
  * NF4 input gradient.  [P1] "Which entry point?" (grouped NF4 backward);
@@ -305,6 +329,15 @@ int gq_mxfp4_grouped_dgrad(const uint16_t* dy, int32_t P, int32_t N, int64_t dy_
  *   Arguments, grouping and errors as gq_nf4_grouped_gemv / _gemm without
  *   pair_scale; InvalidValue also for N odd (GEMV) or N % 64 (GEMM).
  *
+ * gq_mxfp4_grouped_gemv_swiglu: the decode gate_up GEMV of gpt-oss's
+ * experts with their gated unit (the gq_mxfp4_grouped_gemm_scaled_swiglu
+ * reading: gate row 2j, up row 2j + 1, act = gc * sigmoid(alpha * gc) *
+ * (uc + 1), gc = min(g, limit), uc = min(max(u, -limit), limit)), on the
+ * exact float32 products of gq_mxfp4_grouped_gemv.  blocks/scales
+ * [E, N, K] with N = 2I; act uint16 bf16 [rows*topk, I].  Errors as
+ * gq_mxfp4_grouped_gemv without pair_scale, plus InvalidValue for N odd, a
+ * non-finite alpha or limit, or limit < 0.
+ *
  * gq_nf4_grouped_gemv_down_combine (decode, rows*topk <= 64):
  *   y[t, n] = bf16( sum_s w[t, s] * sum_i act[t*topk + s, i] * W_{ids[t, s]}[n, i] )
  *   act   uint16 bf16 [rows*topk, I], row stride act_stride elements
@@ -334,6 +367,11 @@ int gq_nf4_grouped_gemm_swiglu(const uint16_t* x, int32_t rows, int32_t K, int64
                                const int32_t* sorted_pairs, const int32_t* tiles,
                                const int32_t* num_tiles, int32_t max_tiles, int32_t tile_m,
                                uint16_t* act, hipStream_t stream);
+int gq_mxfp4_grouped_gemv_swiglu(const uint16_t* x, int32_t rows, int32_t K, int64_t x_stride,
+                                 const uint8_t* blocks, const uint8_t* scales,
+                                 int32_t num_experts, int32_t N, const int32_t* topk_ids,
+                                 int32_t topk, float alpha, float limit, uint16_t* act,
+                                 hipStream_t stream);
 int gq_nf4_grouped_gemv_down_combine(const uint16_t* act, int32_t rows, int32_t I,
                                      int64_t act_stride, const uint8_t* codes,
                                      const float* absmax, int32_t num_experts, int32_t H,

@@ -253,3 +253,42 @@ def test_scaled_mxfp4_entry_points_reject(lib):
     assert call(a1=F2) == INVALID
     assert call(a2=1 << 20, a14=(1 << 22) // 256 + 33 + 1) == NOT_SUPPORTED
     assert call(a2=0) == 0
+
+
+def test_gpt_oss_activation_entry_points_reject(lib):
+    """Host-side checks of the two entry points with the gpt-oss gated unit:
+    the activation parameters, the gate_up width, and what the plain entry
+    points already reject.  No kernel is launched."""
+    nan, inf = float("nan"), float("inf")
+    # GEMV: x, rows, K, stride, blocks, scales, E, N, ids, topk, alpha, limit, act
+    g = [F, 1, 2880, 2880, F, F, 32, 5760, F, 4, 1.702, 7.0, F, None]
+
+    def gemv(**kw):
+        a = list(g)
+        for i, v in kw.items():
+            a[int(i[1:])] = v
+        return lib.gq_mxfp4_grouped_gemv_swiglu(*a)
+    assert gemv(a7=5761) == INVALID                        # odd gate_up width
+    assert gemv(a11=-1.0) == INVALID
+    assert gemv(a11=inf) == INVALID
+    assert gemv(a10=nan) == INVALID
+    assert gemv(a2=2870) == INVALID                        # K % 32
+    assert gemv(a0=NULL) == INVALID
+    assert gemv(a1=300) == NOT_SUPPORTED                   # > 256 pairs
+    # scaled GEMM: codes, scales, rows, K, blocks, scales, E, N, topk, alpha,
+    # limit, offsets, sorted, tiles, num_tiles, max_tiles, tile_m, act
+    m = [F, F, 2048, 2880, F, F, 32, 5760, 4, 1.702, 7.0, F, F, F, F, 32 + 33 + 1, 256, F, None]
+
+    def gemm(**kw):
+        a = list(m)
+        for i, v in kw.items():
+            a[int(i[1:])] = v
+        return lib.gq_mxfp4_grouped_gemm_scaled_swiglu(*a)
+    assert gemm(a7=5750) == INVALID                        # N % 32
+    assert gemm(a10=-0.5) == INVALID
+    assert gemm(a9=inf) == INVALID
+    assert gemm(a10=nan) == INVALID
+    assert gemm(a16=128) == NOT_SUPPORTED
+    assert gemm(a15=60) == INVALID
+    assert gemm(a17=NULL) == INVALID
+    assert gemm(a2=0) == 0

@@ -1,0 +1,199 @@
+"""gpt-oss's gated unit fused into the MXFP4 gate_up products, on the GPU
+against the float64 oracle (oracle.gate_up_swiglu_oss): the decode GEMV
+(in-wave and LDS-reduced rows) and the prefill GEMM on the block-scaled fp4
+instruction.  Activations are also drawn 8x larger so that many gate and up
+values pass the clamps; one-hot probes, whose products are exact, pin the
+unit itself to one bf16 ulp; ragged tiles, tile edges, dropped pairs and
+the gpt-oss-20b shapes (sampled experts)."""
+
+import numpy as np
+import pytest
+import torch
+
+import bit_grouped_moe_amd as gq
+import oracle
+import workloads as wl
+from tests.gpu_common import (LazyDecoded, assert_rows, assert_slices, bf16_bits,
+                              bf16_to_host_f32, device, packed_mx_bank, say, to_dev, to_dev_bf16)
+
+pytestmark = pytest.mark.gpu
+
+
+def _ref(x, W, ids, E):
+    return oracle.gate_up_swiglu_oss(x, W, ids, E)
+
+
+def _clamp_share(x, W, ids, E):
+    """Share of gate values above the clamp in the reference products (the
+    tests with scaled activations need the clamps in play)."""
+    h = oracle.grouped_gemm(x, W, np.where(ids >= E, -1, ids), E)
+    return float(np.mean(h[:, 0::2] > oracle.OSS_LIMIT))
+
+
+def _gemm_act(x_bits, blocks, scales, ids, E, dev):
+    route = gq.gq_route_sort(to_dev(ids.astype(np.int32), dev), E)
+    split = gq.gq_act_split_e4m3(to_dev_bf16(x_bits, dev))
+    out = gq.gq_mxfp4_grouped_gemm_scaled_swiglu(split, blocks, scales, route)
+    torch.cuda.synchronize()
+    return out
+
+
+# ---- decode GEMV ---------------------------------------------------------------
+@pytest.mark.parametrize("K,rows,xstd", [(96, 1, 1.0), (96, 3, 8.0), (2880, 2, 1.0),
+                                         (2880, 3, 8.0), (1024, 2, 8.0)])
+def test_gemv_swiglu_oss_small(K, rows, xstd):
+    """K = 96 and 1024: a row's segments inside one wave; K = 2880: rows
+    reduced through LDS.  A dropped slot gives a zero row."""
+    dev = device()
+    g = np.random.default_rng(K * 10 + rows)
+    E, I, topk = 4, 80, 2
+    blocks, scales = packed_mx_bank(g, E, 2 * I, K)
+    W = LazyDecoded("mx", blocks, scales)
+    x = wl.draw_bf16(g, (rows, K), std=xstd)
+    ids = wl.route_uniform(g, rows, E, topk)
+    if rows > 1:
+        ids[1, 0] = -1
+    say("gemv swiglu oss", K, rows, xstd)
+    act = gq.gq_mxfp4_grouped_gemv_swiglu(to_dev_bf16(x, dev), to_dev(blocks, dev),
+                                          to_dev(scales, dev), to_dev(ids, dev))
+    torch.cuda.synchronize()
+    got, ref = bf16_to_host_f32(act), _ref(x, W, ids, E)
+    if xstd > 1 and K >= 1024:
+        assert _clamp_share(x, W, ids, E) > 0.05
+    assert_slices(got, ref, ids, E)
+    assert_rows(got, ref)
+
+
+def test_gemv_swiglu_oss_gptoss():
+    """gpt-oss-20b decode: one token, top-4 of 32 experts, gate_up
+    [5760, 2880] (gate row 2j, up row 2j + 1)."""
+    dev = device()
+    E, topk = wl.GPTOSS["E"], wl.GPTOSS["topk"]
+    N2, K = wl.GPTOSS["gate_up"]
+    blocks, scales = wl.random_mxfp4_bank(E, N2, K, dev, seed=4300)
+    g = wl.rng(wl.CFG_GPTOSS, 60)
+    x = wl.draw_bf16(g, (1, K), std=4.0)
+    ids = wl.route_uniform(g, 1, E, topk)
+    say("gemv swiglu oss gpt-oss")
+    act = gq.gq_mxfp4_grouped_gemv_swiglu(to_dev_bf16(x, dev), blocks, scales, to_dev(ids, dev))
+    torch.cuda.synchronize()
+    W = LazyDecoded("mx", blocks.cpu().numpy(), scales.cpu().numpy())
+    got, ref = bf16_to_host_f32(act), _ref(x, W, ids, E)
+    assert_slices(got, ref, ids, E)
+    assert_rows(got, ref)
+
+
+# ---- prefill GEMM on the block-scaled instruction --------------------------------
+@pytest.mark.parametrize("N2,K,xstd", [(288, 1056, 1.0), (288, 1056, 8.0), (544, 2880, 8.0),
+                                       (256, 64, 1.0)])
+def test_gemm_scaled_swiglu_oss_ragged(N2, K, xstd):
+    """Skewed routing over several 256-row tiles, I = 144 and 272 ending
+    inside a 128-output tile, K = 1056 with a half-filled last step,
+    dropped and out-of-range ids."""
+    dev = device()
+    g = np.random.default_rng(N2 + 5 * K + int(xstd))
+    E, M, topk = 6, 700, 2
+    blocks, scales = packed_mx_bank(g, E, N2, K)
+    W = LazyDecoded("mx", blocks, scales)
+    ids = wl.route_zipf(g, M, E, topk, s=2.5)
+    ids[g.random(ids.shape) < 0.02] = -1
+    ids[:, 1][ids[:, 1] == 4] = E
+    x = wl.draw_bf16(g, (M, K), std=xstd)
+    say("mx8 swiglu ragged", N2, K, xstd)
+    got = bf16_to_host_f32(_gemm_act(x, to_dev(blocks, dev), to_dev(scales, dev), ids, E, dev))
+    ref = _ref(x, W, np.where(ids >= E, -1, ids), E)
+    if xstd > 1:
+        assert _clamp_share(x, W, ids, E) > 0.05
+    assert got.shape == (M * topk, N2 // 2)
+    assert_slices(got, ref, ids, E)
+    assert_rows(got, ref)
+    assert not got[(ids.reshape(-1) < 0) | (ids.reshape(-1) >= E)].any()
+
+
+def test_gemm_scaled_swiglu_oss_tile_edges():
+    """Segments of 128/129 (4 vs 8 sub-tiles), 161, 224, 256/257, 1, 33 rows,
+    an empty expert and dropped pairs, in flatten mode."""
+    dev = device()
+    g = np.random.default_rng(77)
+    sizes = [128, 129, 161, 224, 256, 257, 1, 33, 0]
+    E, N2, K = len(sizes), 320, 2880
+    ids = np.concatenate([np.full(n, e, dtype=np.int32) for e, n in enumerate(sizes)]
+                         + [np.full(5, -1, dtype=np.int32)])
+    ids = g.permutation(ids).reshape(-1, 1)
+    blocks, scales = packed_mx_bank(g, E, N2, K)
+    W = LazyDecoded("mx", blocks, scales)
+    x = wl.draw_bf16(g, (ids.shape[0], K), std=4.0)
+    say("mx8 swiglu tile edges")
+    got = bf16_to_host_f32(_gemm_act(x, to_dev(blocks, dev), to_dev(scales, dev), ids, E, dev))
+    ref = _ref(x, W, ids, E)
+    assert_slices(got, ref, ids, E)
+    assert_rows(got, ref)
+    assert not got[ids.reshape(-1) < 0].any()
+
+
+def _ulp_close(a_bits, b_bits):
+    """bf16 patterns equal or one ulp apart (same sign; +-0 equal)."""
+    a = np.asarray(a_bits, np.int64)
+    b = np.asarray(b_bits, np.int64)
+    a = np.where(a == 0x8000, 0, a)
+    b = np.where(b == 0x8000, 0, b)
+    same_sign = (a >> 15) == (b >> 15)
+    return bool(np.all((a == b) | (same_sign & (np.abs(a - b) <= 1))))
+
+
+@pytest.mark.parametrize("path", ["gemv", "gemm"])
+def test_one_hot_probe(path):
+    """x = c * e_k makes each gate and up value an exact multiple of one
+    decoded weight (c = 1, 256, 2048: inside and far beyond the clamps), so
+    the only rounding left is the unit's float32 arithmetic and the bf16
+    output: every output within one bf16 ulp of the float64 oracle."""
+    dev = device()
+    g = np.random.default_rng(19)
+    E, I, K = 2, 96, 1056
+    blocks, scales = packed_mx_bank(g, E, 2 * I, K)
+    W = LazyDecoded("mx", blocks, scales)
+    ks = np.array([0, 31, 32, 517, K - 1])
+    cs = np.array([0x3F80, 0x4380, 0x4500], dtype=np.uint16)      # 1, 256, 2048
+    x = np.zeros((len(ks) * len(cs), K), dtype=np.uint16)
+    for i, (k, c) in enumerate([(k, c) for k in ks for c in cs]):
+        x[i, k] = c
+    ids = np.stack([np.zeros(len(x)), np.ones(len(x))], axis=1).astype(np.int32)
+    say("oss one-hot", path)
+    if path == "gemv":
+        outs = []
+        for r0 in range(0, len(x), 8):                   # <= 8 rows per GEMV call
+            a = gq.gq_mxfp4_grouped_gemv_swiglu(to_dev_bf16(x[r0:r0 + 8], dev),
+                                                to_dev(blocks, dev), to_dev(scales, dev),
+                                                to_dev(ids[r0:r0 + 8], dev))
+            outs.append(bf16_bits(a))
+        torch.cuda.synchronize()
+        got = np.concatenate(outs)
+    else:
+        got = bf16_bits(_gemm_act(x, to_dev(blocks, dev), to_dev(scales, dev), ids, E, dev))
+    ref = _ref(x, W, ids, E)
+    assert np.mean(np.abs(oracle.grouped_gemm(x, W, ids, E)[:, 0::2]) > 7) > 0.2
+    want = oracle.f32_to_bf16_rne(ref.astype(np.float32))
+    assert _ulp_close(got, want)
+
+
+def test_gemm_scaled_swiglu_oss_gptoss_full():
+    """gpt-oss-20b prefill gate_up at M = 2048, top-4 of 32 experts, with
+    29 dropped pairs; three sampled experts checked per slice and per row."""
+    dev = device()
+    E, topk = wl.GPTOSS["E"], wl.GPTOSS["topk"]
+    N2, K = wl.GPTOSS["gate_up"]
+    M = 2048
+    blocks, scales = wl.random_mxfp4_bank(E, N2, K, dev, seed=4400)
+    ids = wl.route_uniform(wl.rng(wl.CFG_GPTOSS, wl.S_ROUTE), M, E, topk).copy()
+    drop = np.random.default_rng(44).choice(ids.size, 29, replace=False)
+    ids.reshape(-1)[drop] = -1
+    x = wl.draw_bf16(wl.rng(wl.CFG_GPTOSS, wl.S_X), (M, K), std=4.0)
+    say("mx8 swiglu gpt-oss full")
+    got = bf16_to_host_f32(_gemm_act(x, blocks, scales, ids, E, dev))
+    W = LazyDecoded("mx", blocks.cpu().numpy(), scales.cpu().numpy())
+    check = [0, 13, 31]
+    ref = _ref(x, W, np.where(np.isin(ids, check), ids, -1), E)
+    assert_slices(got, ref, ids, E, experts=check)
+    rows = np.nonzero(np.isin(ids.reshape(-1), check))[0]
+    assert_rows(got[rows], ref[rows], what="sampled experts")
+    assert not got[drop].any()
