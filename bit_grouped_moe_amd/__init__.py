@@ -23,8 +23,8 @@ __all__ = [
     "gq_mxfp4_grouped_gemm", "gq_nf4_grouped_dgrad", "gq_mxfp4_grouped_dgrad",
     "gq_nf4_grouped_gemv_swiglu", "gq_nf4_grouped_gemm_swiglu", "gq_nf4_grouped_gemv_down_combine",
     "gq_moe_combine", "gq_act_split_e4m3", "gq_mxfp4_grouped_gemm_scaled",
-    "gq_mxfp4_grouped_gemv_swiglu", "gq_mxfp4_grouped_gemm_scaled_swiglu", "OSS_ALPHA",
-    "OSS_LIMIT", "Route",
+    "gq_mxfp4_grouped_gemv_swiglu", "gq_mxfp4_grouped_gemm_scaled_swiglu",
+    "gq_mxfp4_grouped_gemv_down_combine", "OSS_ALPHA", "OSS_LIMIT", "Route",
 ]
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
@@ -39,6 +39,7 @@ EXPORTED_SYMBOLS = (
     "gq_nf4_grouped_gemv_swiglu", "gq_nf4_grouped_gemm_swiglu", "gq_nf4_grouped_gemv_down_combine",
     "gq_moe_combine", "gq_act_split_e4m3", "gq_mxfp4_grouped_gemm_scaled",
     "gq_mxfp4_grouped_gemv_swiglu", "gq_mxfp4_grouped_gemm_scaled_swiglu",
+    "gq_mxfp4_grouped_gemv_down_combine",
 )
 
 _i32, _i64, _p, _f32 = ctypes.c_int32, ctypes.c_int64, ctypes.c_void_p, ctypes.c_float
@@ -70,6 +71,8 @@ _SIGNATURES = {
     "gq_act_split_e4m3": (ctypes.c_int, [_p, _i32, _i32, _i64, _p, _p, _p]),
     "gq_mxfp4_grouped_gemm_scaled": (ctypes.c_int, [_p, _p, _i32, _i32, _p, _p, _i32, _i32, _i32,
                                                     _p, _p, _p, _p, _p, _i32, _i32, _p, _p]),
+    "gq_mxfp4_grouped_gemv_down_combine": (ctypes.c_int, [_p, _i32, _i32, _i64, _p, _p, _i32,
+                                                          _i32, _p, _i32, _p, _p, _p]),
     "gq_mxfp4_grouped_gemv_swiglu": (ctypes.c_int, [_p, _i32, _i32, _i64, _p, _p, _i32, _i32, _p,
                                                     _i32, _f32, _f32, _p, _p]),
     "gq_mxfp4_grouped_gemm_scaled_swiglu": (ctypes.c_int, [_p, _p, _i32, _i32, _p, _p, _i32,
@@ -439,6 +442,27 @@ def gq_nf4_grouped_gemv_down_combine(act, codes, absmax, topk_ids, topk_weights=
                                               _ptr(_weights(topk_weights, rows, topk)), _ptr(out),
                                               _stream(act))
     _check(st, "gq_nf4_grouped_gemv_down_combine")
+    return out
+
+
+def gq_mxfp4_grouped_gemv_down_combine(act, blocks, scales, topk_ids, topk_weights=None,
+                                       out=None):
+    """Decode down GEMV on MXFP4 experts with the router-weighted combine fused:
+    act bf16 [rows*topk, I] (row p is pair p's input), blocks [E, H, I];
+    returns bf16 [rows, H]."""
+    lib = load_library()
+    P, I, a_s = _x_args(act, "act")
+    E, H, Iw = _mx_bank(blocks, scales)
+    _dev(topk_ids, "topk_ids", torch.int32, 2)
+    rows, topk = topk_ids.shape
+    if Iw != I or rows * topk != P:
+        raise ValueError("act, blocks and topk_ids disagree")
+    out = _out(out, rows, H, act.device)
+    st = lib.gq_mxfp4_grouped_gemv_down_combine(_ptr(act), rows, I, a_s, _ptr(blocks),
+                                                _ptr(scales), E, H, _ptr(topk_ids), topk,
+                                                _ptr(_weights(topk_weights, rows, topk)),
+                                                _ptr(out), _stream(act))
+    _check(st, "gq_mxfp4_grouped_gemv_down_combine")
     return out
 
 

@@ -406,7 +406,9 @@ constexpr int kCombineMaxPairs = 64;
 constexpr int kCombineMaxWaves = 16;
 constexpr int kCombineMaxYs = 1024;
 
-template <bool kMx, int kR, int kPPW>
+// kSeg = 2 (rows of 65..128 segments, I <= 4096): a row takes the whole
+// wave and lane s also takes segment s + 64.
+template <bool kMx, int kR, int kPPW, int kSeg>
 __global__ __launch_bounds__(kWave * kCombineMaxWaves) void gemv_down_combine_kernel(
     const int32_t* __restrict__ ids, const uint16_t* __restrict__ act,
     const uint8_t* __restrict__ codes, const void* __restrict__ scl, int I, int H, int E,
@@ -417,45 +419,59 @@ __global__ __launch_bounds__(kWave * kCombineMaxWaves) void gemv_down_combine_ke
   // layout derived from I and P as on the host (arguments ordered as in
   // grouped_gemv_kernel)
   const int S = I >> 5;
-  const int W = S > 1 ? 1 << (32 - __builtin_clz(S - 1)) : 1;
+  const int W = kSeg == 2 ? kWave : (S > 1 ? 1 << (32 - __builtin_clz(S - 1)) : 1);
   const int NWv = min(P, kCombineMaxWaves);
   const int tid = threadIdx.x, lane = tid & (kWave - 1), wave = tid / kWave;
   const int slots = kWave / W;                             // lane groups per wave
   const int Rb = slots * kR;                               // rows per workgroup
   const int n0 = blockIdx.x * Rb;
   const int g = lane / W, s = lane - g * W;
-  const bool active = s < S;
-  const int s_cl = active ? s : 0;
+  bool active[kSeg];
+  int s_cl[kSeg];
+#pragma unroll
+  for (int j = 0; j < kSeg; ++j) {
+    active[j] = s + kWave * j < S;
+    s_cl[j] = active[j] ? s + kWave * j : 0;
+  }
   const size_t row_bytes = (size_t)I / 2;
 
   // ---- round trip 1: the wave's experts (scalar) and activation slices ----
   int pp[kPPW], ee[kPPW];
-  u32x4 xr[kPPW][4];
+  u32x4 xr[kPPW][kSeg][4];
 #pragma unroll
   for (int q = 0; q < kPPW; ++q) {
     pp[q] = min(wave + NWv * q, P - 1);                    // surplus pairs repeat the last
     ee[q] = ids[pp[q]];
-    const u32x4* ap = reinterpret_cast<const u32x4*>(act + (int64_t)pp[q] * a_stride + s_cl * 32);
 #pragma unroll
-    for (int v = 0; v < 4; ++v) xr[q][v] = ap[v];
+    for (int j = 0; j < kSeg; ++j) {
+      const u32x4* ap =
+          reinterpret_cast<const u32x4*>(act + (int64_t)pp[q] * a_stride + s_cl[j] * 32);
+#pragma unroll
+      for (int v = 0; v < 4; ++v) xr[q][j][v] = ap[v];
+    }
   }
   // ---- round trip 2: weight segments (dropped pairs read expert 0) ----
-  u32x4 cw[kPPW][kR];
-  float am[kPPW][kR];
-  uint32_t sb[kPPW][kR];
+  u32x4 cw[kPPW][kR][kSeg];
+  float am[kPPW][kR][kSeg];
+  uint32_t sb[kPPW][kR][kSeg];
 #pragma unroll
   for (int q = 0; q < kPPW; ++q) {
     const int e = (unsigned)ee[q] < (unsigned)E ? ee[q] : 0;
 #pragma unroll
     for (int i = 0; i < kR; ++i) {
       const size_t row = (size_t)e * H + min(n0 + g * kR + i, H - 1);
-      cw[q][i] = *reinterpret_cast<const u32x4*>(codes + row * row_bytes + (size_t)s_cl * 16);
-      if constexpr (kMx) {
-        sb[q][i] = (uint32_t)static_cast<const uint8_t*>(scl)[row * (size_t)(I / 32) + s_cl];
-        am[q][i] = 0.f;
-      } else {
-        am[q][i] = static_cast<const float*>(scl)[row * (size_t)(I / 64) + s_cl / 2];
-        sb[q][i] = 0u;
+#pragma unroll
+      for (int j = 0; j < kSeg; ++j) {
+        cw[q][i][j] =
+            *reinterpret_cast<const u32x4*>(codes + row * row_bytes + (size_t)s_cl[j] * 16);
+        if constexpr (kMx) {
+          sb[q][i][j] =
+              (uint32_t)static_cast<const uint8_t*>(scl)[row * (size_t)(I / 32) + s_cl[j]];
+          am[q][i][j] = 0.f;
+        } else {
+          am[q][i][j] = static_cast<const float*>(scl)[row * (size_t)(I / 64) + s_cl[j] / 2];
+          sb[q][i][j] = 0u;
+        }
       }
     }
   }
@@ -465,19 +481,27 @@ __global__ __launch_bounds__(kWave * kCombineMaxWaves) void gemv_down_combine_ke
   }
 #pragma unroll
   for (int q = 0; q < kPPW; ++q) {
-    float xf[32];
+    float part[kR];
 #pragma unroll
-    for (int v = 0; v < 4; ++v)
+    for (int i = 0; i < kR; ++i) part[i] = 0.f;
 #pragma unroll
-      for (int cc = 0; cc < 4; ++cc) {
-        xf[8 * v + 2 * cc] = bf16lo_to_f32(xr[q][v][cc]);
-        xf[8 * v + 2 * cc + 1] = bf16hi_to_f32(xr[q][v][cc]);
-      }
+    for (int j = 0; j < kSeg; ++j) {
+      float xf[32];
+#pragma unroll
+      for (int v = 0; v < 4; ++v)
+#pragma unroll
+        for (int cc = 0; cc < 4; ++cc) {
+          xf[8 * v + 2 * cc] = bf16lo_to_f32(xr[q][j][v][cc]);
+          xf[8 * v + 2 * cc + 1] = bf16hi_to_f32(xr[q][j][v][cc]);
+        }
+#pragma unroll
+      for (int i = 0; i < kR; ++i)
+        if (active[j]) part[i] += segment_dot<kMx>(lut, cw[q][i][j], am[q][i][j], sb[q][i][j], xf);
+    }
     const int p = wave + NWv * q;
 #pragma unroll
     for (int i = 0; i < kR; ++i) {
-      const float part = active ? segment_dot<kMx>(lut, cw[q][i], am[q][i], sb[q][i], xf) : 0.f;
-      const float tot = group_sum_last(part, W);
+      const float tot = group_sum_last(part[i], W);
       if (s == W - 1 && p < P) ys[p * Rb + g * kR + i] = (unsigned)ee[q] < (unsigned)E ? tot : 0.f;
     }
   }
@@ -498,11 +522,11 @@ __global__ __launch_bounds__(kWave * kCombineMaxWaves) void gemv_down_combine_ke
   }
 }
 
-template <bool kMx, int kR, int kPPW>
+template <bool kMx, int kR, int kPPW, int kSeg>
 static void launch_dc(dim3 grid, int NWv, hipStream_t stream, const uint16_t* act, int a_stride,
                       int I, const uint8_t* codes, const void* scl, int H, int E,
                       const int32_t* ids, int topk, int P, const float* tw, uint16_t* y) {
-  hipLaunchKernelGGL((gemv_down_combine_kernel<kMx, kR, kPPW>), grid, dim3(kWave * NWv), 0,
+  hipLaunchKernelGGL((gemv_down_combine_kernel<kMx, kR, kPPW, kSeg>), grid, dim3(kWave * NWv), 0,
                      stream, ids, act, codes, scl, I, H, E, a_stride, topk, P, tw, y);
 }
 
@@ -518,26 +542,37 @@ static int launch_down_combine(const uint16_t* act, int32_t rows, int32_t I, int
   if (!kMx && !aligned4(scl)) return kInvalid;
   if (tw && !aligned4(tw)) return kInvalid;
   const int64_t P = (int64_t)rows * topk;
-  if (P > kCombineMaxPairs || I > 32 * kWave || H >= (1 << 24)) return kNotSupported;
+  if (P > kCombineMaxPairs || I > 64 * kWave || H >= (1 << 24)) return kNotSupported;
   if (a_stride > INT32_MAX) return kNotSupported;
-  int S, W, G, NT;
-  segment_layout(I, S, W, G, NT);
   const int NWv = (int)std::min<int64_t>(P, kCombineMaxWaves);
   const int ppw = (int)((P + NWv - 1) / NWv);               // 1..4
+  const bool two_seg = I > 32 * kWave;                      // 65..128 segments per row
+  if (two_seg && ppw > 2) return kNotSupported;              // registers: <= 32 pairs
+  int S, W, G, NT;
+  segment_layout(I, S, W, G, NT);
+  if (two_seg) W = kWave;
   // rows per lane group: 2 for one pair per wave (as the GEMV), 1 otherwise
   const int kr = ppw == 1 ? 2 : 1;
   const int Rb = (kWave / W) * kr;
   if (P * Rb > kCombineMaxYs) return kNotSupported;
   const dim3 grid((H + Rb - 1) / Rb);
-  if (ppw == 1)
-    launch_dc<kMx, 2, 1>(grid, NWv, stream, act, (int)a_stride, I, codes, scl, H, E, ids, topk,
-                         (int)P, tw, y);
-  else if (ppw == 2)
-    launch_dc<kMx, 1, 2>(grid, NWv, stream, act, (int)a_stride, I, codes, scl, H, E, ids, topk,
-                         (int)P, tw, y);
-  else
-    launch_dc<kMx, 1, 4>(grid, NWv, stream, act, (int)a_stride, I, codes, scl, H, E, ids, topk,
-                         (int)P, tw, y);
+  if (two_seg) {
+    if (ppw == 1)
+      launch_dc<kMx, 2, 1, 2>(grid, NWv, stream, act, (int)a_stride, I, codes, scl, H, E, ids,
+                              topk, (int)P, tw, y);
+    else
+      launch_dc<kMx, 1, 2, 2>(grid, NWv, stream, act, (int)a_stride, I, codes, scl, H, E, ids,
+                              topk, (int)P, tw, y);
+  } else if (ppw == 1) {
+    launch_dc<kMx, 2, 1, 1>(grid, NWv, stream, act, (int)a_stride, I, codes, scl, H, E, ids,
+                            topk, (int)P, tw, y);
+  } else if (ppw == 2) {
+    launch_dc<kMx, 1, 2, 1>(grid, NWv, stream, act, (int)a_stride, I, codes, scl, H, E, ids,
+                            topk, (int)P, tw, y);
+  } else {
+    launch_dc<kMx, 1, 4, 1>(grid, NWv, stream, act, (int)a_stride, I, codes, scl, H, E, ids,
+                            topk, (int)P, tw, y);
+  }
   return launch_status();
 }
 
@@ -595,6 +630,16 @@ extern "C" int gq_nf4_grouped_gemv_down_combine(const uint16_t* act, int32_t row
                                                 hipStream_t stream) {
   return gq::launch_down_combine<false>(act, rows, I, act_stride, codes, absmax, num_experts, H,
                                         topk_ids, topk, topk_weights, y, stream);
+}
+
+extern "C" int gq_mxfp4_grouped_gemv_down_combine(const uint16_t* act, int32_t rows, int32_t I,
+                                                  int64_t act_stride, const uint8_t* blocks,
+                                                  const uint8_t* scales, int32_t num_experts,
+                                                  int32_t H, const int32_t* topk_ids,
+                                                  int32_t topk, const float* topk_weights,
+                                                  uint16_t* y, hipStream_t stream) {
+  return gq::launch_down_combine<true>(act, rows, I, act_stride, blocks, scales, num_experts, H,
+                                       topk_ids, topk, topk_weights, y, stream);
 }
 
 extern "C" int gq_moe_combine(const uint16_t* y_pairs, int32_t rows, int32_t topk, int32_t H,

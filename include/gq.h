@@ -346,8 +346,12 @@ int gq_mxfp4_grouped_dgrad(const uint16_t* dy, int32_t P, int32_t N, int64_t dy_
  *   outside [0, E) contributes 0.
  *   InvalidValue: null pointer (topk_weights may be NULL), rows < 1,
  *     topk < 1, E < 1, H < 1, I not a positive multiple of 64, bad stride
- *     or alignment.  NotSupported: rows*topk > 64, I > 2048, H >= 2^24,
- *     act_stride > 2^31 - 1.
+ *     or alignment.  NotSupported: rows*topk > 64, I > 4096, I > 2048 with
+ *     rows*topk > 32, H >= 2^24, act_stride > 2^31 - 1.
+ *
+ * gq_mxfp4_grouped_gemv_down_combine: the same on MXFP4 experts
+ *   (blocks/scales [E, H, I], I a positive multiple of 32), float32 exact
+ *   decode as gq_mxfp4_grouped_gemv; same errors with I % 32 for I % 64.
  *
  * gq_moe_combine (prefill):
  *   y[t, :] = bf16( sum_s w[t, s] * y_pairs[t*topk + s, :] )
@@ -378,6 +382,12 @@ int gq_nf4_grouped_gemv_down_combine(const uint16_t* act, int32_t rows, int32_t 
                                      const int32_t* topk_ids, int32_t topk,
                                      const float* topk_weights, uint16_t* y,
                                      hipStream_t stream);
+int gq_mxfp4_grouped_gemv_down_combine(const uint16_t* act, int32_t rows, int32_t I,
+                                       int64_t act_stride, const uint8_t* blocks,
+                                       const uint8_t* scales, int32_t num_experts, int32_t H,
+                                       const int32_t* topk_ids, int32_t topk,
+                                       const float* topk_weights, uint16_t* y,
+                                       hipStream_t stream);
 int gq_moe_combine(const uint16_t* y_pairs, int32_t rows, int32_t topk, int32_t H,
                    int64_t stride, const float* topk_weights, uint16_t* y, hipStream_t stream);
 

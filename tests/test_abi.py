@@ -205,8 +205,20 @@ def test_epilogue_entry_points_reject(lib):
                                                 None) == INVALID
     assert lib.gq_nf4_grouped_gemv_down_combine(F, 9, 768, 768, F, F, 128, 2048, F, 8, NULL, F,
                                                 None) == NOT_SUPPORTED
-    assert lib.gq_nf4_grouped_gemv_down_combine(F, 1, 4096, 4096, F, F, 128, 2048, F, 8, NULL, F,
+    assert lib.gq_nf4_grouped_gemv_down_combine(F, 1, 4160, 4160, F, F, 128, 2048, F, 8, NULL, F,
                                                 None) == NOT_SUPPORTED
+    # two segments per lane (I > 2048) hold at most 32 pairs
+    assert lib.gq_nf4_grouped_gemv_down_combine(F, 5, 4096, 4096, F, F, 128, 2048, F, 8, NULL, F,
+                                                None) == NOT_SUPPORTED
+    # MXFP4: I % 32, pairs, I limit, pair cap with two segments per lane
+    assert lib.gq_mxfp4_grouped_gemv_down_combine(F, 1, 2870, 2880, F, F, 32, 2880, F, 4, NULL,
+                                                  F, None) == INVALID
+    assert lib.gq_mxfp4_grouped_gemv_down_combine(F, 17, 2880, 2880, F, F, 32, 2880, F, 4, NULL,
+                                                  F, None) == NOT_SUPPORTED
+    assert lib.gq_mxfp4_grouped_gemv_down_combine(F, 9, 2880, 2880, F, F, 32, 2880, F, 4, NULL,
+                                                  F, None) == NOT_SUPPORTED
+    assert lib.gq_mxfp4_grouped_gemv_down_combine(F, 1, 4128, 4128, F, F, 32, 2880, F, 4, NULL,
+                                                  F, None) == NOT_SUPPORTED
     assert lib.gq_nf4_grouped_gemv_down_combine(F, 1, 768, 768, F, F, 128, 2048, F, 8, F2, F,
                                                 None) == INVALID          # misaligned weights
     assert lib.gq_nf4_grouped_gemv_down_combine(F, 1, 768, 1 << 31, F, F, 128, 2048, F, 8, NULL,

@@ -125,9 +125,11 @@ def test_swiglu_matches_unfused_path():
 # ---- down projection + combine ------------------------------------------------
 @pytest.mark.parametrize("rows,topk,I,weighted", [(1, 2, 128, True), (3, 2, 128, False),
                                                  (4, 4, 192, True), (2, 8, 2048, True),
-                                                 (5, 8, 768, False), (8, 8, 2048, True)])
+                                                 (5, 8, 768, False), (8, 8, 2048, True),
+                                                 (1, 8, 4096, True), (4, 8, 3072, False)])
 def test_down_combine_small(rows, topk, I, weighted):
-    """One to four pairs per wave, lane groups of 4..64 lanes, up to 64 pairs."""
+    """One to four pairs per wave, lane groups of 4..64 lanes, up to 64 pairs;
+    I = 3072 and 4096: two segments per lane (one and two pairs per wave)."""
     dev = device()
     g = wl.rng(wl.CFG_TINY, 700 + rows * 10 + topk + I)
     E, H = 9, 200

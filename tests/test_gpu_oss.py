@@ -4,7 +4,8 @@ against the float64 oracle (oracle.gate_up_swiglu_oss): the decode GEMV
 instruction.  Activations are also drawn 8x larger so that many gate and up
 values pass the clamps; one-hot probes, whose products are exact, pin the
 unit itself to one bf16 ulp; ragged tiles, tile edges, dropped pairs and
-the gpt-oss-20b shapes (sampled experts)."""
+the gpt-oss-20b shapes (sampled experts).  Then the MXFP4 decode down GEMV
+with the router-weighted combine fused, and whole gpt-oss decode layers."""
 
 import numpy as np
 import pytest
@@ -197,3 +198,58 @@ def test_gemm_scaled_swiglu_oss_gptoss_full():
     rows = np.nonzero(np.isin(ids.reshape(-1), check))[0]
     assert_rows(got[rows], ref[rows], what="sampled experts")
     assert not got[drop].any()
+
+
+# ---- decode down projection with the router-weighted combine -------------------
+@pytest.mark.parametrize("rows,topk,I,weighted", [(1, 4, 96, True), (3, 2, 2880, False),
+                                                 (1, 4, 2880, True), (8, 4, 2880, True),
+                                                 (2, 8, 4096, True), (16, 4, 1024, True)])
+def test_down_combine_mx_small(rows, topk, I, weighted):
+    """MXFP4 down GEMV + combine: in-wave rows (I <= 2048) and two segments
+    per lane (I = 2880, 4096), one and two pairs per wave, a dropped slot."""
+    dev = device()
+    g = np.random.default_rng(rows * 100 + topk * 10 + I)
+    E, H = 9, 200
+    blocks, scales = packed_mx_bank(g, E, H, I)
+    act = wl.draw_bf16(g, (rows * topk, I))
+    ids = wl.route_uniform(g, rows, E, topk)
+    if rows > 2:
+        ids[2, 1] = -1
+    w = wl.router_weights(g, rows, topk) if weighted else None
+    say("mx down combine", rows, topk, I, weighted)
+    y = gq.gq_mxfp4_grouped_gemv_down_combine(to_dev_bf16(act, dev), to_dev(blocks, dev),
+                                              to_dev(scales, dev), to_dev(ids, dev),
+                                              None if w is None else to_dev(w, dev))
+    torch.cuda.synchronize()
+    ref = oracle.down_combine(act, LazyDecoded("mx", blocks, scales), ids, E, w)
+    assert_rows(bf16_to_host_f32(y), ref)
+
+
+@pytest.mark.parametrize("M", [1, 4, 8])
+def test_decode_layer_gptoss(M):
+    """One gpt-oss-20b decode MoE layer: gate_up GEMV with the gated unit,
+    then down GEMV + router-weighted combine; each launch against the oracle
+    on its own input, and the float64 chain end to end."""
+    dev = device()
+    E, topk = wl.GPTOSS["E"], wl.GPTOSS["topk"]
+    (N2, K), (H, I) = wl.GPTOSS["gate_up"], wl.GPTOSS["down"]
+    bg, sg = wl.random_mxfp4_bank(E, N2, K, dev, seed=4500 + M)
+    bd, sd = wl.random_mxfp4_bank(E, H, I, dev, seed=4600 + M)
+    g = wl.rng(wl.CFG_GPTOSS, 70 + M)
+    x = wl.draw_bf16(g, (M, K), std=4.0)
+    ids = wl.route_uniform(g, M, E, topk)
+    w = wl.router_weights(g, M, topk)
+    say("decode layer gpt-oss", M)
+    t_ids = to_dev(ids, dev)
+    act = gq.gq_mxfp4_grouped_gemv_swiglu(to_dev_bf16(x, dev), bg, sg, t_ids)
+    y = gq.gq_mxfp4_grouped_gemv_down_combine(act, bd, sd, t_ids, to_dev(w, dev))
+    torch.cuda.synchronize()
+    Wg = LazyDecoded("mx", bg.cpu().numpy(), sg.cpu().numpy())
+    Wd = LazyDecoded("mx", bd.cpu().numpy(), sd.cpu().numpy())
+    assert_rows(bf16_to_host_f32(act), _ref(x, Wg, ids, E), what="gate_up")
+    act_bits = bf16_bits(act)
+    assert_rows(bf16_to_host_f32(y), oracle.down_combine(act_bits, Wd, ids, E, w), what="down")
+    act64 = _ref(x, Wg, ids, E)
+    y64 = oracle.combine(np.stack([act64[p] @ Wd(ids.reshape(-1)[p]).astype(np.float64).T
+                                   for p in range(M * topk)]), topk, w)
+    assert_rows(bf16_to_host_f32(y), y64, tol=8e-3, what="end to end")
