@@ -448,6 +448,98 @@ def prefill_layer_nf4(dev, steps, warmup):
             "combine_gbs": (P * Nd * 2 + M * Nd * 2) / (tc.avg_us() * 1e-6) / 1e9}
 
 
+def decode_layer_mx(dev, steps, warmup, M=1):
+    """gpt-oss-20b MXFP4 MoE layer, decode: gate_up GEMV with the gpt-oss
+    gated unit + down GEMV with the router-weighted combine fused (two
+    launches per step, graph-replayed, cold bank copy per step)."""
+    E, topk = wl.GPTOSS["E"], wl.GPTOSS["topk"]
+    (Ng, Kg), (Nd, Kd) = wl.GPTOSS["gate_up"], wl.GPTOSS["down"]
+    copies = 8                                     # 8 x 332 MB of banks > the last-level cache
+    banks_g = [wl.random_mxfp4_bank(E, Ng, Kg, dev, seed=60 + c) for c in range(copies)]
+    banks_d = [wl.random_mxfp4_bank(E, Nd, Kd, dev, seed=600 + c) for c in range(copies)]
+    g = wl.rng(wl.CFG_GPTOSS, 72)
+    ids = [wl.route_uniform(g, M, E, topk) for _ in range(steps + warmup)]
+    t_ids = [torch.from_numpy(i).to(dev) for i in ids]
+    tw = torch.from_numpy(wl.router_weights(g, M, topk)).to(dev)
+    x = bf16_dev(wl.draw_bf16(wl.rng(wl.CFG_GPTOSS, 73), (M, Kg)), dev)
+    act = torch.empty((M * topk, Ng // 2), dtype=torch.bfloat16, device=dev)
+    y = torch.empty((M, Nd), dtype=torch.bfloat16, device=dev)
+
+    def step(i):
+        b, s_ = banks_g[i % copies]
+        gq.gq_mxfp4_grouped_gemv_swiglu(x, b, s_, t_ids[i], out=act)
+        b, s_ = banks_d[i % copies]
+        gq.gq_mxfp4_grouped_gemv_down_combine(act, b, s_, t_ids[i], tw, out=y)
+
+    for i in range(steps, steps + warmup):
+        step(i)
+    gr = capture(step, steps)
+    gr.replay()
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    gr.replay()
+    torch.cuda.synchronize()
+    dt = time.perf_counter() - t0
+    total = 0
+    for i in range(steps):
+        d = len(set(ids[i].reshape(-1).tolist()))
+        total += d * (mx_expert_bytes(Ng, Kg) + mx_expert_bytes(Nd, Kd)) + M * Kg * 2 + M * Nd * 2
+    return {"workload": f"gpt-oss-20b mxfp4 moe layer decode M={M}: gate_up gemv with the "
+                        f"gpt-oss gated unit + down gemv with router-weighted combine (2 launches)",
+            "ms_per_step": 1e3 * dt / steps, "gbs": total / dt / 1e9,
+            "bytes_per_step": total / steps, "frac_hbm": total / dt / 1e9 / HBM_PEAK_GBS}
+
+
+def prefill_layer_mx(dev, steps, warmup):
+    """gpt-oss-20b MXFP4 MoE layer, prefill (M=2048 uniform top-4) on the
+    block-scaled fp4 instruction: route sort + split + gate_up GEMM with the
+    gated unit + split + down GEMM (router weight as pair scale) + combine."""
+    cfgd, M, cfg = wl.GPTOSS, 2048, wl.CFG_GPTOSS
+    E, topk = cfgd["E"], cfgd["topk"]
+    (Ng, Kg), (Nd, Kd) = cfgd["gate_up"], cfgd["down"]
+    P = M * topk
+    route = wl.route_uniform(wl.rng(cfg, wl.S_ROUTE), M, E, topk)
+    a_g, b_g = wl.random_mxfp4_bank(E, Ng, Kg, dev, seed=32)
+    a_d, b_d = wl.random_mxfp4_bank(E, Nd, Kd, dev, seed=302)
+    ids = torch.from_numpy(route).to(dev)
+    sc = torch.from_numpy(wl.router_weights(wl.rng(cfg, wl.S_LOGITS), M, topk)).to(dev)
+    x = bf16_dev(wl.draw_bf16(wl.rng(cfg, wl.S_X), (M, Kg)), dev)
+    act = torch.empty((P, Ng // 2), dtype=torch.bfloat16, device=dev)
+    yp = torch.empty((P, Nd), dtype=torch.bfloat16, device=dev)
+    y = torch.empty((M, Nd), dtype=torch.bfloat16, device=dev)
+    cs, ss = gq.split_sizes(M, Kg)
+    sx = (torch.empty(cs, dtype=torch.uint8, device=dev), torch.empty(ss, dtype=torch.uint8, device=dev))
+    cs, ss = gq.split_sizes(P, Kd)
+    sa = (torch.empty(cs, dtype=torch.uint8, device=dev), torch.empty(ss, dtype=torch.uint8, device=dev))
+    tg, td, tc = Timer(), Timer(), Timer()
+
+    def run(timed):
+        r = gq.gq_route_sort(ids, E)
+        rd = r._replace(rows=P, topk=1)
+        gq.gq_act_split_e4m3(x, *sx)
+        ev = tg.start() if timed else None
+        gq.gq_mxfp4_grouped_gemm_scaled_swiglu(sx, a_g, b_g, r, out=act)
+        if timed:
+            tg.stop(ev)
+        gq.gq_act_split_e4m3(act, *sa)
+        ev = td.start() if timed else None
+        gq.gq_mxfp4_grouped_gemm_scaled(sa, a_d, b_d, rd, pair_scale=sc, out=yp)
+        if timed:
+            td.stop(ev)
+            ev = tc.start()
+        gq.gq_moe_combine(yp, topk, out=y)
+        if timed:
+            tc.stop(ev)
+
+    dt = eager_steps(run, steps, warmup) * steps
+    flops = 2.0 * P * (Ng * Kg + Nd * Kd)
+    return {"workload": "gpt-oss-20b mxfp4 moe layer prefill M=2048 top-4 on the block-scaled "
+                        "fp4 instruction: route sort + split + gate_up gemm with the gated unit "
+                        "+ split + down gemm (router-weight scale) + combine",
+            "ms_per_step": 1e3 * dt / steps, "tflops": flops * steps / dt / 1e12,
+            "gate_up_act_us": tg.avg_us(), "down_us": td.avg_us(), "combine_us": tc.avg_us()}
+
+
 def prefill(dev, steps, warmup, fmt):
     """NF4 Qwen3 (M=4096 Zipf top-8) or MXFP4 gpt-oss (M=2048 uniform top-4):
     route sort + gate_up GEMM + down GEMM per step (eager; kernels are long)."""
@@ -716,7 +808,8 @@ def r4(d):
 
 
 LEGS = ("decode", "decode_m4", "mx_decode", "controls", "prefill", "mx_prefill",
-        "mx_prefill_scaled", "layer_decode", "layer_prefill", "dgrad", "mx_dgrad", "mfma")
+        "mx_prefill_scaled", "layer_decode", "layer_prefill", "mx_layer_decode",
+        "mx_layer_prefill", "dgrad", "mx_dgrad", "mfma")
 
 
 def run_legs(dev, args, legs):
@@ -743,6 +836,10 @@ def run_legs(dev, args, legs):
             out[leg] = decode_layer_nf4(dev, st, wu)
         elif leg == "layer_prefill":
             out[leg] = prefill_layer_nf4(dev, ps, pw)
+        elif leg == "mx_layer_decode":
+            out[leg] = decode_layer_mx(dev, st, wu)
+        elif leg == "mx_layer_prefill":
+            out[leg] = prefill_layer_mx(dev, ps, pw)
         elif leg == "dgrad":
             out[leg] = dgrad(dev, ps, pw)
         elif leg == "mx_dgrad":
@@ -834,6 +931,11 @@ def main():
         log("[bench] nf4 moe layer prefill M=4096")
         extra["nf4_moe_layer_prefill_m4096"] = prefill_layer_nf4(dev, args.prefill_steps,
                                                                  args.prefill_warmup)
+        log("[bench] mxfp4 moe layer decode M=1")
+        extra["mxfp4_moe_layer_decode_m1"] = decode_layer_mx(dev, args.steps, args.warmup)
+        log("[bench] mxfp4 moe layer prefill M=2048")
+        extra["mxfp4_moe_layer_prefill_m2048"] = prefill_layer_mx(dev, args.prefill_steps,
+                                                                  args.prefill_warmup)
         log("[bench] nf4 dgrad")
         extra["nf4_dgrad_m2048"] = dgrad(dev, args.prefill_steps, args.prefill_warmup)
         log("[bench] mxfp4 dgrad")
