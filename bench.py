@@ -540,6 +540,88 @@ def prefill_layer_mx(dev, steps, warmup):
             "gate_up_act_us": tg.avg_us(), "down_us": td.avg_us(), "combine_us": tc.avg_us()}
 
 
+def host_stream(dev, steps, warmup, M=1):
+    """Qwen3 NF4 decode (M=1, top-8 of 128) with both expert banks in pinned
+    host memory: the GEMVs read the routed experts' bytes over the host link
+    (graph-replayed, new routing every step).  Controls on the same link:
+    a pinned -> device copy of the same byte count (the link ceiling), and
+    the copy-then-compute path (the routed experts copied to a device
+    staging bank, then the device GEMVs; eager, routing known on the host)."""
+    E, topk = wl.QWEN["E"], wl.QWEN["topk"]
+    (Ng, Kg), (Nd, Kd) = wl.QWEN["gate_up"], wl.QWEN["down"]
+    cg, ag = (t.cpu().pin_memory() for t in wl.random_nf4_bank(E, Ng, Kg, dev, seed=80))
+    cd, ad = (t.cpu().pin_memory() for t in wl.random_nf4_bank(E, Nd, Kd, dev, seed=81))
+    torch.cuda.synchronize()
+    g = wl.rng(wl.CFG_QWEN_DECODE, 82)
+    ids = [wl.route_uniform(g, M, E, topk) for _ in range(steps + warmup)]
+    ids_g = [torch.from_numpy(i).to(dev) for i in ids]
+    ids_d = [torch.from_numpy(i.reshape(-1, 1).copy()).to(dev) for i in ids]
+    x = bf16_dev(wl.draw_bf16(wl.rng(wl.CFG_QWEN_DECODE, 83), (M, Kg)), dev)
+    xd = bf16_dev(wl.draw_bf16(wl.rng(wl.CFG_QWEN_DECODE, 84), (M * topk, Kd)), dev)
+    out_g = torch.empty((M * topk, Ng), dtype=torch.bfloat16, device=dev)
+    out_d = torch.empty((M * topk, Nd), dtype=torch.bfloat16, device=dev)
+
+    def step(i):
+        gq.gq_nf4_grouped_gemv_host(x, cg, ag, ids_g[i], out=out_g)
+        gq.gq_nf4_grouped_gemv_host(xd, cd, ad, ids_d[i], out=out_d)
+
+    for i in range(steps, steps + warmup):
+        step(i)
+    gr = capture(step, steps)
+    gr.replay()
+    torch.cuda.synchronize()
+    ms = event_ms(gr.replay) / steps
+    d = [len(set(i.reshape(-1).tolist())) for i in ids[:steps]]
+    step_bytes = float(np.mean([n * (nf4_expert_bytes(Ng, Kg) + nf4_expert_bytes(Nd, Kd))
+                                for n in d])) + M * Kg * 2 + M * topk * (Kd + Ng + Nd) * 2
+    # link ceiling: pinned -> device copies of the same byte count, and of 256 MB
+    link = {}
+    for nb in (int(step_bytes), 256 << 20):
+        src = torch.empty(nb, dtype=torch.uint8, pin_memory=True)
+        src.fill_(1)
+        dst = torch.empty(nb, dtype=torch.uint8, device=dev)
+        dst.copy_(src, non_blocking=True)
+        reps = 20 if nb < (64 << 20) else 4
+        t = event_ms(lambda: [dst.copy_(src, non_blocking=True) for _ in range(reps)]) / reps
+        link[nb] = nb / (t * 1e-3) / 1e9
+        del src, dst
+    # copy-then-compute: the routed experts to a device staging bank, then the
+    # device GEMVs on it (ids remapped to staging slots)
+    sg = (torch.empty((topk * M,) + tuple(cg.shape[1:]), dtype=cg.dtype, device=dev),
+          torch.empty((topk * M,) + tuple(ag.shape[1:]), dtype=ag.dtype, device=dev))
+    sd = (torch.empty((topk * M,) + tuple(cd.shape[1:]), dtype=cd.dtype, device=dev),
+          torch.empty((topk * M,) + tuple(ad.shape[1:]), dtype=ad.dtype, device=dev))
+    slot_ids = []
+    for i in range(steps):
+        experts = sorted(set(ids[i].reshape(-1).tolist()))
+        remap = {e: j for j, e in enumerate(experts)}
+        sid = np.vectorize(remap.get)(ids[i]).astype(np.int32)
+        slot_ids.append((experts, torch.from_numpy(sid).to(dev),
+                         torch.from_numpy(sid.reshape(-1, 1).copy()).to(dev)))
+
+    def copy_compute(i):
+        experts, sid_g, sid_d = slot_ids[i]
+        for j, e in enumerate(experts):
+            sg[0][j].copy_(cg[e], non_blocking=True)
+            sg[1][j].copy_(ag[e], non_blocking=True)
+            sd[0][j].copy_(cd[e], non_blocking=True)
+            sd[1][j].copy_(ad[e], non_blocking=True)
+        gq.gq_nf4_grouped_gemv(x, sg[0][:len(experts)], sg[1][:len(experts)], sid_g, out=out_g)
+        gq.gq_nf4_grouped_gemv(xd, sd[0][:len(experts)], sd[1][:len(experts)], sid_d, out=out_d)
+
+    copy_compute(0)
+    torch.cuda.synchronize()
+    cc_ms = event_ms(lambda: [copy_compute(i) for i in range(steps)]) / steps
+    gbs = step_bytes / (ms * 1e-3) / 1e9
+    return {"workload": f"qwen3-30b-a3b nf4 decode M={M} (gate_up + down gemv) with both expert "
+                        f"banks in pinned host memory, streamed over the host link by the kernel",
+            "ms_per_step": ms, "bytes_per_step": step_bytes, "gbs": gbs,
+            "link_gbs_same_bytes": link[int(step_bytes)], "link_gbs_256mb": link[256 << 20],
+            "frac_of_link": gbs / link[int(step_bytes)],
+            "copy_then_compute_ms_per_step": cc_ms,
+            "copy_then_compute_gbs": step_bytes / (cc_ms * 1e-3) / 1e9}
+
+
 def prefill(dev, steps, warmup, fmt):
     """NF4 Qwen3 (M=4096 Zipf top-8) or MXFP4 gpt-oss (M=2048 uniform top-4):
     route sort + gate_up GEMM + down GEMM per step (eager; kernels are long)."""
@@ -809,7 +891,7 @@ def r4(d):
 
 LEGS = ("decode", "decode_m4", "mx_decode", "controls", "prefill", "mx_prefill",
         "mx_prefill_scaled", "layer_decode", "layer_prefill", "mx_layer_decode",
-        "mx_layer_prefill", "dgrad", "mx_dgrad", "mfma")
+        "mx_layer_prefill", "host_stream", "dgrad", "mx_dgrad", "mfma")
 
 
 def run_legs(dev, args, legs):
@@ -840,6 +922,8 @@ def run_legs(dev, args, legs):
             out[leg] = decode_layer_mx(dev, st, wu)
         elif leg == "mx_layer_prefill":
             out[leg] = prefill_layer_mx(dev, ps, pw)
+        elif leg == "host_stream":
+            out[leg] = host_stream(dev, min(st, 50), min(wu, 5))
         elif leg == "dgrad":
             out[leg] = dgrad(dev, ps, pw)
         elif leg == "mx_dgrad":
@@ -936,6 +1020,9 @@ def main():
         log("[bench] mxfp4 moe layer prefill M=2048")
         extra["mxfp4_moe_layer_prefill_m2048"] = prefill_layer_mx(dev, args.prefill_steps,
                                                                   args.prefill_warmup)
+        log("[bench] nf4 decode from pinned host memory")
+        extra["nf4_decode_m1_host_streamed"] = host_stream(dev, min(args.steps, 50),
+                                                           min(args.warmup, 5))
         log("[bench] nf4 dgrad")
         extra["nf4_dgrad_m2048"] = dgrad(dev, args.prefill_steps, args.prefill_warmup)
         log("[bench] mxfp4 dgrad")

@@ -24,7 +24,8 @@ __all__ = [
     "gq_nf4_grouped_gemv_swiglu", "gq_nf4_grouped_gemm_swiglu", "gq_nf4_grouped_gemv_down_combine",
     "gq_moe_combine", "gq_act_split_e4m3", "gq_mxfp4_grouped_gemm_scaled",
     "gq_mxfp4_grouped_gemv_swiglu", "gq_mxfp4_grouped_gemm_scaled_swiglu",
-    "gq_mxfp4_grouped_gemv_down_combine", "OSS_ALPHA", "OSS_LIMIT", "Route",
+    "gq_mxfp4_grouped_gemv_down_combine", "gq_nf4_grouped_gemv_host", "gq_mxfp4_grouped_gemv_host",
+    "OSS_ALPHA", "OSS_LIMIT", "Route",
 ]
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
@@ -39,7 +40,7 @@ EXPORTED_SYMBOLS = (
     "gq_nf4_grouped_gemv_swiglu", "gq_nf4_grouped_gemm_swiglu", "gq_nf4_grouped_gemv_down_combine",
     "gq_moe_combine", "gq_act_split_e4m3", "gq_mxfp4_grouped_gemm_scaled",
     "gq_mxfp4_grouped_gemv_swiglu", "gq_mxfp4_grouped_gemm_scaled_swiglu",
-    "gq_mxfp4_grouped_gemv_down_combine",
+    "gq_mxfp4_grouped_gemv_down_combine", "gq_nf4_grouped_gemv_host", "gq_mxfp4_grouped_gemv_host",
 )
 
 _i32, _i64, _p, _f32 = ctypes.c_int32, ctypes.c_int64, ctypes.c_void_p, ctypes.c_float
@@ -71,6 +72,10 @@ _SIGNATURES = {
     "gq_act_split_e4m3": (ctypes.c_int, [_p, _i32, _i32, _i64, _p, _p, _p]),
     "gq_mxfp4_grouped_gemm_scaled": (ctypes.c_int, [_p, _p, _i32, _i32, _p, _p, _i32, _i32, _i32,
                                                     _p, _p, _p, _p, _p, _i32, _i32, _p, _p]),
+    "gq_nf4_grouped_gemv_host": (ctypes.c_int, [_p, _i32, _i32, _i64, _p, _p, _i32, _i32, _p,
+                                                _i32, _p, _p, _p]),
+    "gq_mxfp4_grouped_gemv_host": (ctypes.c_int, [_p, _i32, _i32, _i64, _p, _p, _i32, _i32, _p,
+                                                  _i32, _p, _p, _p]),
     "gq_mxfp4_grouped_gemv_down_combine": (ctypes.c_int, [_p, _i32, _i32, _i64, _p, _p, _i32,
                                                           _i32, _p, _i32, _p, _p, _p]),
     "gq_mxfp4_grouped_gemv_swiglu": (ctypes.c_int, [_p, _i32, _i32, _i64, _p, _p, _i32, _i32, _p,
@@ -316,6 +321,60 @@ def gq_mxfp4_grouped_gemv_swiglu(x, blocks, scales, topk_ids, alpha=OSS_ALPHA, l
                                           _ptr(topk_ids), topk_ids.shape[1], float(alpha),
                                           float(limit), _ptr(out), _stream(x))
     _check(st, "gq_mxfp4_grouped_gemv_swiglu")
+    return out
+
+
+def _host_bank(a, b, names):
+    """Host-resident bank tensors: CPU, pinned, contiguous (the library maps
+    them to device addresses and rejects memory that is not pinned)."""
+    for t, n in zip((a, b), names):
+        if t.device.type != "cpu" or not t.is_pinned():
+            raise ValueError(f"{n} must be a pinned host tensor (pin_memory=True)")
+        if not t.is_contiguous():
+            raise ValueError(f"{n} must be contiguous")
+
+
+def gq_nf4_grouped_gemv_host(x, codes, absmax, topk_ids, pair_scale=None, out=None):
+    """Decode GEMV on NF4 experts resident in pinned host memory: codes uint8
+    [E, N, K/2] and absmax float32 [E, N, K/64] are pinned CPU tensors; the
+    kernel streams the routed experts' bytes over the host link.  x, topk_ids,
+    pair_scale and out are device tensors.  Returns bf16 [rows*topk, N]."""
+    lib = load_library()
+    rows, K, xs = _x_args(x)
+    _host_bank(codes, absmax, ("codes", "absmax"))
+    if codes.dtype != torch.uint8 or absmax.dtype != torch.float32 or codes.dim() != 3:
+        raise ValueError("codes uint8 [E, N, K/2] and absmax float32 [E, N, K/64] expected")
+    E, N, half = codes.shape
+    if half * 2 != K or tuple(absmax.shape) != (E, N, K // 64):
+        raise ValueError("x, codes and absmax disagree on the shapes")
+    _dev(topk_ids, "topk_ids", torch.int32, 2)
+    P = _gemv_pairs(topk_ids, rows)
+    out = _out(out, P, N, x.device)
+    st = lib.gq_nf4_grouped_gemv_host(_ptr(x), rows, K, xs, _ptr(codes), _ptr(absmax), E, N,
+                                      _ptr(topk_ids), topk_ids.shape[1],
+                                      _ptr(_scale(pair_scale, P)), _ptr(out), _stream(x))
+    _check(st, "gq_nf4_grouped_gemv_host")
+    return out
+
+
+def gq_mxfp4_grouped_gemv_host(x, blocks, scales, topk_ids, pair_scale=None, out=None):
+    """Decode GEMV on MXFP4 experts resident in pinned host memory (blocks
+    uint8 [E, N, K/32, 16], scales uint8 [E, N, K/32], pinned CPU tensors)."""
+    lib = load_library()
+    rows, K, xs = _x_args(x)
+    _host_bank(blocks, scales, ("blocks", "scales"))
+    if blocks.dtype != torch.uint8 or scales.dtype != torch.uint8 or blocks.dim() != 4:
+        raise ValueError("blocks uint8 [E, N, K/32, 16] and scales uint8 [E, N, K/32] expected")
+    E, N, nb, sixteen = blocks.shape
+    if sixteen != 16 or nb * 32 != K or tuple(scales.shape) != (E, N, nb):
+        raise ValueError("x, blocks and scales disagree on the shapes")
+    _dev(topk_ids, "topk_ids", torch.int32, 2)
+    P = _gemv_pairs(topk_ids, rows)
+    out = _out(out, P, N, x.device)
+    st = lib.gq_mxfp4_grouped_gemv_host(_ptr(x), rows, K, xs, _ptr(blocks), _ptr(scales), E, N,
+                                        _ptr(topk_ids), topk_ids.shape[1],
+                                        _ptr(_scale(pair_scale, P)), _ptr(out), _stream(x))
+    _check(st, "gq_mxfp4_grouped_gemv_host")
     return out
 
 

@@ -603,7 +603,51 @@ __global__ __launch_bounds__(256) void moe_combine_kernel(const uint16_t* __rest
   *reinterpret_cast<u32x4*>(y + (int64_t)t * H + c * 8) = o;
 }
 
+// Expert banks resident in pinned host memory: the device address of each
+// bank, from the runtime's mapping of the pinned allocation.  Memory the
+// runtime has not pinned and mapped is rejected here, before any launch
+// (a device read of an unmapped host address would fault).
+static int host_bank_ptrs(const void* a, const void* b, const void*& da, const void*& db) {
+  if (!a || !b) return kInvalid;
+  void* pa = nullptr;
+  void* pb = nullptr;
+  if (hipHostGetDevicePointer(&pa, const_cast<void*>(a), 0) != hipSuccess || !pa ||
+      hipHostGetDevicePointer(&pb, const_cast<void*>(b), 0) != hipSuccess || !pb) {
+    (void)hipGetLastError();                               // do not leave it for the next call
+    return kInvalid;
+  }
+  da = pa;
+  db = pb;
+  return kOk;
+}
+
 }  // namespace gq
+
+extern "C" int gq_nf4_grouped_gemv_host(const uint16_t* x, int32_t rows, int32_t K,
+                                        int64_t x_stride, const uint8_t* codes,
+                                        const float* absmax, int32_t num_experts, int32_t N,
+                                        const int32_t* topk_ids, int32_t topk,
+                                        const float* pair_scale, uint16_t* out,
+                                        hipStream_t stream) {
+  const void *dc = nullptr, *da = nullptr;
+  const int st = gq::host_bank_ptrs(codes, absmax, dc, da);
+  if (st != gq::kOk) return st;
+  return gq::launch_gemv<false, 0>(x, rows, K, x_stride, static_cast<const uint8_t*>(dc), da,
+                                   num_experts, N, topk_ids, topk, pair_scale, out, stream);
+}
+
+extern "C" int gq_mxfp4_grouped_gemv_host(const uint16_t* x, int32_t rows, int32_t K,
+                                          int64_t x_stride, const uint8_t* blocks,
+                                          const uint8_t* scales, int32_t num_experts, int32_t N,
+                                          const int32_t* topk_ids, int32_t topk,
+                                          const float* pair_scale, uint16_t* out,
+                                          hipStream_t stream) {
+  const void *db = nullptr, *ds = nullptr;
+  const int st = gq::host_bank_ptrs(blocks, scales, db, ds);
+  if (st != gq::kOk) return st;
+  return gq::launch_gemv<true, 0>(x, rows, K, x_stride, static_cast<const uint8_t*>(db), ds,
+                                  num_experts, N, topk_ids, topk, pair_scale, out, stream);
+}
 
 extern "C" int gq_nf4_grouped_gemv(const uint16_t* x, int32_t rows, int32_t K, int64_t x_stride,
                                    const uint8_t* codes, const float* absmax, int32_t num_experts,

@@ -156,6 +156,33 @@ int gq_mxfp4_grouped_gemv(const uint16_t* x, int32_t rows, int32_t K, int64_t x_
                           const float* pair_scale, uint16_t* out, hipStream_t stream);
 
 /* ------------------------------------------------------------------------
+ * Experts streamed from host memory.  [P1] page header (streaming expert
+ * weights from RAM or SSD) and section "Which entry point?" (the row for
+ * streaming experts from RAM or NVMe); [P2] "What the discipline caught" (the fused
+ * kernel as the only expert compute while experts stream over the host
+ * link, against the link's ceiling) and "The numbers" (t ~ c + bytes/link).
+ *
+ * gq_nf4_grouped_gemv_host / gq_mxfp4_grouped_gemv_host: gq_nf4_grouped_gemv
+ * / gq_mxfp4_grouped_gemv with the expert bank (codes and absmax, or blocks
+ * and scales) in pinned, device-mapped host memory (hipHostMalloc, or a
+ * pinned torch tensor), passed as HOST pointers.  The kernel reads the
+ * routed experts' bytes straight over the host link as it decodes them: no
+ * staging copy, each active expert's bytes cross the link once per launch.
+ * x, topk_ids, pair_scale and out are device pointers as before; same
+ * arithmetic, results bit-identical to the device-resident call.
+ * InvalidValue also when a bank pointer is not pinned, mapped host memory
+ * (checked before anything is enqueued).
+ */
+int gq_nf4_grouped_gemv_host(const uint16_t* x, int32_t rows, int32_t K, int64_t x_stride,
+                             const uint8_t* codes, const float* absmax, int32_t num_experts,
+                             int32_t N, const int32_t* topk_ids, int32_t topk,
+                             const float* pair_scale, uint16_t* out, hipStream_t stream);
+int gq_mxfp4_grouped_gemv_host(const uint16_t* x, int32_t rows, int32_t K, int64_t x_stride,
+                               const uint8_t* blocks, const uint8_t* scales, int32_t num_experts,
+                               int32_t N, const int32_t* topk_ids, int32_t topk,
+                               const float* pair_scale, uint16_t* out, hipStream_t stream);
+
+/* ------------------------------------------------------------------------
  * Prefill grouped GEMM.  [P1] "Which entry point?" (grouped NF4 forward,
  * native MXFP4 expert math) and header (one launch for the active experts,
  * no full-size bf16 weight copies); [P2] summary (codebook decoded in

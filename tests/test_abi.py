@@ -304,3 +304,14 @@ def test_gpt_oss_activation_entry_points_reject(lib):
     assert gemm(a15=60) == INVALID
     assert gemm(a17=NULL) == INVALID
     assert gemm(a2=0) == 0
+
+
+def test_host_bank_entry_points_reject_unpinned_memory(lib):
+    """The host-resident GEMVs map the bank pointers before anything else:
+    plain (unpinned) host memory and NULL are rejected, never launched on."""
+    buf = ctypes.create_string_buffer(1 << 16)
+    hp = ctypes.c_void_p(ctypes.addressof(buf))
+    for fn in (lib.gq_nf4_grouped_gemv_host, lib.gq_mxfp4_grouped_gemv_host):
+        assert fn(F, 1, 2048, 2048, hp, hp, 128, 1536, F, 8, NULL, F, None) == INVALID
+        assert fn(F, 1, 2048, 2048, NULL, hp, 128, 1536, F, 8, NULL, F, None) == INVALID
+        assert fn(F, 1, 2048, 2048, hp, NULL, 128, 1536, F, 8, NULL, F, None) == INVALID
