@@ -83,8 +83,10 @@ __device__ __forceinline__ float segment_dot(const float* lut, u32x4 c, float am
 // kAct: 0 plain product; 1 SwiGLU with gate rows [0, N/2) and up rows
 // [N/2, N); 2 the gpt-oss gated unit with gate row 2j and up row 2j + 1
 // (alpha, limit).  With an activation a workgroup takes output columns
-// [n0, n0 + R/2) and the gate and up rows of each.
-template <bool kMx, int kIter, bool kWaveRows, int kAct>
+// [n0, n0 + R/2) and the gate and up rows of each.  kHostBank: the same code
+// for a bank in pinned host memory (a separate instance, so that profiles
+// keep the host-link launches apart from the HBM ones).
+template <bool kMx, int kIter, bool kWaveRows, int kAct, bool kHostBank = false>
 __global__ __launch_bounds__(kGemvMaxThreads) void grouped_gemv_kernel(
     const int32_t* __restrict__ ids, const uint16_t* __restrict__ x,
     const uint8_t* __restrict__ codes, const void* __restrict__ scl, int K, int N, int E,
@@ -313,17 +315,19 @@ __global__ __launch_bounds__(kGemvMaxThreads) void grouped_gemv_kernel(
   }
 }
 
-template <bool kMx, int kIter, int kAct>
+template <bool kMx, int kIter, int kAct, bool kHostBank>
 static void launch_gemv_iter(dim3 grid, int NT, bool wave_rows, hipStream_t stream,
                              const uint16_t* x, int x_stride, int K, const uint8_t* codes,
                              const void* scl, int N, int E, const int32_t* ids, int topk, int P,
                              const float* pair_scale, uint16_t* out, float alpha, float limit) {
   if (wave_rows)
-    hipLaunchKernelGGL((grouped_gemv_kernel<kMx, kIter, true, kAct>), grid, dim3(NT), 0, stream,
+    hipLaunchKernelGGL((grouped_gemv_kernel<kMx, kIter, true, kAct, kHostBank>), grid, dim3(NT),
+                       0, stream,
                        ids, x, codes, scl, K, N, E, x_stride, topk, P, pair_scale, out, alpha,
                        limit);
   else
-    hipLaunchKernelGGL((grouped_gemv_kernel<kMx, kIter, false, kAct>), grid, dim3(NT), 0, stream,
+    hipLaunchKernelGGL((grouped_gemv_kernel<kMx, kIter, false, kAct, kHostBank>), grid, dim3(NT),
+                       0, stream,
                        ids, x, codes, scl, K, N, E, x_stride, topk, P, pair_scale, out, alpha,
                        limit);
 }
@@ -341,7 +345,7 @@ static void segment_layout(int K, int& S, int& W, int& G, int& NT) {
   NT = S > kWave ? ((S * G + kWave - 1) / kWave) * kWave : kGemvMaxThreads;
 }
 
-template <bool kMx, int kAct>
+template <bool kMx, int kAct, bool kHostBank = false>
 static int launch_gemv(const uint16_t* x, int32_t rows, int32_t K, int64_t x_stride,
                        const uint8_t* codes, const void* scl, int32_t E, int32_t N,
                        const int32_t* ids, int32_t topk, const float* pair_scale, uint16_t* out,
@@ -375,15 +379,15 @@ static int launch_gemv(const uint16_t* x, int32_t rows, int32_t K, int64_t x_str
   const dim3 grid((N + R - 1) / R, (unsigned)P);
   switch (iter) {
     case 8:
-      launch_gemv_iter<kMx, 8, kAct>(grid, NT, S <= kWave, stream, x, (int)x_stride, K, codes, scl,
+      launch_gemv_iter<kMx, 8, kAct, kHostBank>(grid, NT, S <= kWave, stream, x, (int)x_stride, K, codes, scl,
                                      N, E, ids, topk, (int)P, pair_scale, out, alpha, limit);
       break;
     case 4:
-      launch_gemv_iter<kMx, 4, kAct>(grid, NT, S <= kWave, stream, x, (int)x_stride, K, codes, scl,
+      launch_gemv_iter<kMx, 4, kAct, kHostBank>(grid, NT, S <= kWave, stream, x, (int)x_stride, K, codes, scl,
                                      N, E, ids, topk, (int)P, pair_scale, out, alpha, limit);
       break;
     default:
-      launch_gemv_iter<kMx, 2, kAct>(grid, NT, S <= kWave, stream, x, (int)x_stride, K, codes, scl,
+      launch_gemv_iter<kMx, 2, kAct, kHostBank>(grid, NT, S <= kWave, stream, x, (int)x_stride, K, codes, scl,
                                      N, E, ids, topk, (int)P, pair_scale, out, alpha, limit);
       break;
   }
@@ -632,7 +636,7 @@ extern "C" int gq_nf4_grouped_gemv_host(const uint16_t* x, int32_t rows, int32_t
   const void *dc = nullptr, *da = nullptr;
   const int st = gq::host_bank_ptrs(codes, absmax, dc, da);
   if (st != gq::kOk) return st;
-  return gq::launch_gemv<false, 0>(x, rows, K, x_stride, static_cast<const uint8_t*>(dc), da,
+  return gq::launch_gemv<false, 0, true>(x, rows, K, x_stride, static_cast<const uint8_t*>(dc), da,
                                    num_experts, N, topk_ids, topk, pair_scale, out, stream);
 }
 
@@ -645,7 +649,7 @@ extern "C" int gq_mxfp4_grouped_gemv_host(const uint16_t* x, int32_t rows, int32
   const void *db = nullptr, *ds = nullptr;
   const int st = gq::host_bank_ptrs(blocks, scales, db, ds);
   if (st != gq::kOk) return st;
-  return gq::launch_gemv<true, 0>(x, rows, K, x_stride, static_cast<const uint8_t*>(db), ds,
+  return gq::launch_gemv<true, 0, true>(x, rows, K, x_stride, static_cast<const uint8_t*>(db), ds,
                                   num_experts, N, topk_ids, topk, pair_scale, out, stream);
 }
 

@@ -13,7 +13,7 @@ import pytest
 import bench
 from bit_grouped_moe_amd import profile_summary as ps
 
-GEMV_NAME = "void gq::grouped_gemv_kernel<false, 2, true, false>(int const*)"
+GEMV_NAME = "void gq::grouped_gemv_kernel<false, 2, true, 0, false>(int const*)"
 GEMM_NAME = "void gq::grouped_gemm_fwd_kernel<0>(gq::GemmArgs)"
 COPY_NAME = "(anonymous namespace)::copy_kernel(int4 const*)"
 GEMV_GRID = ps.GATE_UP_GEMV[1]
