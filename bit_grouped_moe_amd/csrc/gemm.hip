@@ -125,7 +125,7 @@ struct DgLoad {
   u32x4 c;
   float a;      // NF4 absmax of (row t/kBlk, block t%kBlk), t < 64*kBlk
   uint32_t s;   // MXFP4 scale byte of the same
-  bool ok, aok;
+  bool aok;     // the scale block lies inside the matrix
 };
 
 template <int kMode>
@@ -135,7 +135,6 @@ __device__ __forceinline__ DgLoad dg_load(const GemmArgs& g, int e, int k0, int 
   const int r = tid >> 2, q = tid & 3;                    // row in step, 16-byte quarter
   const int n = ks * kTK + r;                             // W row (< Nw since Nw % 64 == 0)
   const int kb = k0 + q * 32;                             // first weight of this quarter
-  L.ok = kb < g.Kw;
   const size_t row = (size_t)e * g.Nw + n;
   L.c = *reinterpret_cast<const u32x4*>(g.codes + row * (size_t)(g.Kw / 2) +
                                         min(kb, g.Kw - 32) / 2);
@@ -160,7 +159,11 @@ __device__ __forceinline__ void dg_stage(const DgLoad& L, uint8_t* Cs, float* As
   using F = DgFmt<kMode>;
   // Cs: 64 rows x kCStride bytes of raw codes; As: [64 rows][kBlk] factors
   const int r = tid >> 2, q = tid & 3;
-  *reinterpret_cast<u32x4*>(Cs + r * kCStride + q * 16) = L.ok ? L.c : u32x4{0u, 0u, 0u, 0u};
+  // Quarters past the matrix width keep their (clamped, re-read) codes:
+  // their scale blocks get a zero factor below, so they decode to zeros.
+  // (A select here on the loaded codes is hoisted by the compiler to the
+  // start of the step and makes it wait for the code load just issued.)
+  *reinterpret_cast<u32x4*>(Cs + r * kCStride + q * 16) = L.c;
   if (tid < F::kBlk * kTK) {
     float f;
     if constexpr (F::kMx) f = e8m0_to_f32(L.s);
@@ -175,10 +178,11 @@ __device__ __forceinline__ void dg_stage(const DgLoad& L, uint8_t* Cs, float* As
 // r8*8 .. +8 of the column quad 4*j4 .. +3: it reads its two code bytes of
 // each of the 8 rows from LDS once per step, the rows' factors (one scale
 // block covers the quad) as 32 contiguous bytes, and writes each column's 8
-// consecutive contraction values as one 16-byte run.
+// consecutive contraction values as one 16-byte run.  Both formats take two
+// passes of two columns.
 //  * NF4: codebook values from the 16-entry LDS table; weight =
 //    float32(value * absmax), then bf16 RNE.
-//  * MXFP4, in two passes of two columns (code byte cp of each row holds
+//  * MXFP4 (code byte cp of each row holds
 //    columns 4*j4 + 2cp and + 2cp + 1, the even one in the low nibble): the
 //    hardware converter turns the byte into the two bf16 weights with the
 //    e8m0 factor applied, exactly; a byte permute then pairs rows i and
@@ -222,36 +226,40 @@ __device__ __forceinline__ void dg_decode_pair(const DgCodes& R, const float* As
   *reinterpret_cast<u32x4*>(col + kBStride) = u32x4{co[0], co[1], co[2], co[3]};
 }
 
-// NF4: all four columns of the quad per call, from the 16-entry codebook
-// table (16 distinct banks: conflict-free); code dword h holds rows 2h and
-// 2h + 1, its 8 nibbles in element order are the quad's columns of row 2h
-// then of row 2h + 1 (high nibble = even column).
+// NF4: columns 2*part and 2*part + 1 of the quad per call (part 0, 1: the
+// decode is spread over two MFMA slices), from the 16-entry codebook table
+// (16 distinct banks: conflict-free); code dword h holds rows 2h and 2h + 1,
+// its 8 nibbles in element order are the quad's columns of row 2h then of
+// row 2h + 1 (high nibble = even column).
 __device__ __forceinline__ void dg_decode_nf4(const DgCodes& R, const float* As, const float* lut,
-                                              uint16_t* Bs, int tid) {
+                                              uint16_t* Bs, int tid, int part) {
   const int j4 = tid & 31, r8 = tid >> 5;
   const f32x4* fp = reinterpret_cast<const f32x4*>(As + (j4 / 16) * kTK + r8 * 8);
   const f32x4 f0 = fp[0], f1 = fp[1];
   const float f[8] = {f0[0], f0[1], f0[2], f0[3], f1[0], f1[1], f1[2], f1[3]};
-  uint32_t c[4][4];                      // [column][row pair]
+  uint32_t c[2][4];                      // [column of the pair][row pair]
 #pragma unroll
   for (int h = 0; h < 4; ++h) {
     float q[8];
-    nf4_lookup8(lut, R.two[h], q);
+    nf4_lookup8(lut, R.two[h], q);       // the other pair's lookups are dead code
 #pragma unroll
-    for (int k = 0; k < 4; ++k) c[k][h] = pack_bf16x2(q[k] * f[2 * h], q[4 + k] * f[2 * h + 1]);
+    for (int k = 0; k < 2; ++k) {
+      const int col = 2 * part + k;
+      c[k][h] = pack_bf16x2(q[col] * f[2 * h], q[4 + col] * f[2 * h + 1]);
+    }
   }
 #pragma unroll
-  for (int k = 0; k < 4; ++k)
-    *reinterpret_cast<u32x4*>(Bs + (j4 * 4 + k) * kBStride + r8 * 8) =
+  for (int k = 0; k < 2; ++k)
+    *reinterpret_cast<u32x4*>(Bs + (j4 * 4 + 2 * part + k) * kBStride + r8 * 8) =
         u32x4{c[k][0], c[k][1], c[k][2], c[k][3]};
 }
 
-// one step's B tile: NF4 in one pass, MXFP4 in two (slices 1 and 2)
+// one step's B tile in two passes (slices 1 and 2), two columns of the quad each
 template <int kMode>
 __device__ __forceinline__ void dg_decode(const DgCodes& R, const float* As, int part,
                                           const float* lut, uint16_t* Bs, int tid) {
   if constexpr (kMode == kDgradNF4) {
-    if (part == 0) dg_decode_nf4(R, As, lut, Bs, tid);
+    dg_decode_nf4(R, As, lut, Bs, tid, part);
   } else {
     dg_decode_pair<kMode>(R, As, part, Bs, tid);
   }
@@ -301,16 +309,18 @@ __device__ __forceinline__ void grouped_gemm_body(const GemmArgs& g) {
   // forward operand (coalesced 128-byte row loads, per-wave swizzled LDS
   // area); fragment-shaped loads straight into registers make every load
   // instruction touch 32 rows and kept the address unit ~80% busy (gpt-oss
-  // dgrad gate_up 513 -> 433 us staged).  NF4: the direct loads (on the
-  // Qwen3 shapes tiles are half full, ~128 rows per expert, and the staging's
-  // extra LDS traffic costs more than the address unit saves: 220 vs 227 us).
-  constexpr bool kDirectA = kMode == kDgradNF4;
+  // dgrad gate_up 513 -> 433 us staged).  NF4: LDS-direct loads into the
+  // same area (on the Qwen3 shapes tiles are half full, ~128 rows per
+  // expert, and staging through registers costs more LDS issue than the
+  // address unit saves: 227 vs 220 us with fragment-shaped loads; LDS-direct
+  // 213 us).  For MXFP4 the LDS-direct form is not faster (434 vs 426 us).
+  constexpr bool kDmaA = kMode == kDgradNF4;
   constexpr bool kGlu = kMode == kFwdNF4Glu;
   constexpr int kTNo = kGlu ? kTN / 2 : kTN;               // output columns per tile
   __shared__ __attribute__((aligned(16))) uint16_t Bs[2][kTN * kBStride];
   __shared__ __attribute__((aligned(16))) uint8_t Cs[kDg ? 2 : 1][kDg ? kTK * kCStride : 16];
   __shared__ float As[kDg ? 2 : 1][kDg ? DgFmt<kMode>::kBlk * kTK : 1];
-  __shared__ __attribute__((aligned(16))) uint16_t Aw[kDirectA ? 1 : 4][kDirectA ? 8 : 64 * kTK];
+  __shared__ __attribute__((aligned(16))) uint16_t Aw[4][64 * kTK];
   __shared__ int pair_s[kTM];
   // dgrad rows are the pairs themselves: row_s aliases pair_s (saves 1 KB of
   // LDS, which lets two dgrad workgroups share a CU)
@@ -362,7 +372,7 @@ __device__ __forceinline__ void grouped_gemm_body(const GemmArgs& g) {
   // when read), see the note at fwd_load; a wave loads the rows of sub-tile
   // ms1 only in the variants where ms1 is active (kNa = 8 loads) and none in
   // the variant for a wave without active rows.
-  uint16_t* aw = &Aw[kDirectA ? 0 : wave][0];
+  uint16_t* aw = &Aw[wave][0];
   // The lane's row offsets are re-read from LDS at every step (registers
   // are short); element offsets fit 32 bits (host check).
   auto load_a = [&](auto na_c, int ks, u32x4 (&Ar)[8]) {
@@ -394,17 +404,48 @@ __device__ __forceinline__ void grouped_gemm_body(const GemmArgs& g) {
       }
     }
   };
-  // dgrad (one wave per SIMD, LDS already busy with the code staging) keeps
-  // the activation operand out of LDS: each lane loads its MFMA fragments
-  // (row lr, 16 bytes at k = lh*32 + sl*8) straight into registers, one step
-  // ahead.  Rows are the pairs; the contraction (N) is a multiple of 64.
-  const uint16_t* ad0 = g.x + (int64_t)row_s[ms0 * 32 + lr] * g.x_stride + lh * 32;
-  const uint16_t* ad1 = g.x + (int64_t)row_s[ms1 * 32 + lr] * g.x_stride + lh * 32;
-  auto load_a_direct = [&](auto na_c, int ks, int sl, u32x4 (&Ad)[2][4]) {
+  // NF4 dgrad: the same rows and swizzle, written by LDS-direct loads.
+  // Instruction j (j < 4: sub-tile ms0, else ms1) fills the wave's local rows
+  // r0(j) .. r0(j) + 8, r0(j) = (j / 4) * 32 + (j % 4) * 8; lane L writes
+  // slot L % 8 of row r0(j) + L / 8 and so fetches global chunk
+  // (L % 8) ^ ((row >> 1) & 7).  A step's fragments are all read into
+  // registers at its start, then the next step's rows are loaded over them
+  // (one area per wave: no barrier).  Rows are the pairs; the contraction
+  // (N) is a multiple of 64, so no K tail.  Byte offsets fit 32 bits (host
+  // check on the element offsets).
+  uint32_t voff[kDmaA ? 8 : 1];
+  if constexpr (kDmaA) {
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+      const int r = (j >> 2) * 32 + (j & 3) * 8 + (lane >> 3);
+      const int c = (lane & 7) ^ ((r >> 1) & 7);
+      voff[j] = (uint32_t)row_s[(j < 4 ? ms0 : ms1) * 32 + (j & 3) * 8 + (lane >> 3)] *
+                    (uint32_t)(g.x_stride * 2) + 16u * (uint32_t)c;
+    }
+  }
+  auto dma_a = [&](auto na_c, int ks) {
     constexpr int kNa = decltype(na_c)::value;             // 8: both sub-tiles, 4: ms0 only
-    const int koff = ks * kTK;
-    Ad[0][sl] = *reinterpret_cast<const u32x4*>(ad0 + koff + sl * 8);
-    if constexpr (kNa == 8) Ad[1][sl] = *reinterpret_cast<const u32x4*>(ad1 + koff + sl * 8);
+    const char* xb = reinterpret_cast<const char*>(g.x) + (size_t)ks * (kTK * 2);
+#pragma unroll
+    for (int j = 0; j < kNa; ++j) {
+      uint32_t vo = voff[j];
+      // opaque: otherwise the compiler keeps all offsets widened to 64 bits
+      // (16 registers) and spills
+      asm volatile("" : "+v"(vo));
+      __builtin_amdgcn_global_load_lds((glb_void_t*)(xb + vo),
+                                       (lds_void_t*)(aw + ((j >> 2) * 32 + (j & 3) * 8) * kTK),
+                                       16, 0, 0);
+    }
+  };
+  auto read_frags = [&](auto na_c, u32x4 (&F)[2][4]) {
+    constexpr int kNj = decltype(na_c)::value / 4;
+#pragma unroll
+    for (int j = 0; j < kNj; ++j)
+#pragma unroll
+      for (int sl = 0; sl < 4; ++sl) {
+        const int slot = (lh * 4 + sl) ^ ((lr >> 1) & 7);
+        F[j][sl] = *reinterpret_cast<const u32x4*>(aw + (j * 32 + lr) * kTK + slot * 8);
+      }
   };
   auto load_b_slice = [&](const uint16_t* B, int sl, bf16x8 (&b)[4]) {
 #pragma unroll
@@ -439,8 +480,8 @@ __device__ __forceinline__ void grouped_gemm_body(const GemmArgs& g) {
     }
   };
 
-  u32x4 Ar[kDirectA ? 1 : 8];                              // staged A prefetch
-  u32x4 Ad[2][kDirectA ? 4 : 1];                           // direct A fragments
+  u32x4 Ar[kDmaA ? 1 : 8];                                 // staged A prefetch
+  u32x4 Ad[2][kDmaA ? 4 : 1];                              // a step's A fragments (LDS-direct)
   FwdLoad F0{}, F1{};
   DgLoad D{};
   DgCodes R{};
@@ -458,9 +499,8 @@ __device__ __forceinline__ void grouped_gemm_body(const GemmArgs& g) {
   // activations and codes in flight ----
   auto prologue_a = [&](auto na_c) {
     if constexpr (decltype(na_c)::value > 0) {
-      if constexpr (kDirectA) {
-#pragma unroll
-        for (int sl = 0; sl < 4; ++sl) load_a_direct(na_c, 0, sl, Ad);
+      if constexpr (kDmaA) {
+        dma_a(na_c, 0);
       } else {
         load_a(na_c, 0, Ar);
         stage_a(na_c, Ar);
@@ -512,7 +552,7 @@ __device__ __forceinline__ void grouped_gemm_body(const GemmArgs& g) {
         u32x4 ac[2];
         if constexpr (kRows >= 0) {
           constexpr int kNj = kRows == 1 ? 1 : 2;          // sub-tiles with operands
-          if constexpr (kDirectA) {
+          if constexpr (kDmaA) {
             ac[0] = Ad[0][sl];
             if constexpr (kNj == 2) ac[1] = Ad[1][sl];
           } else {
@@ -531,18 +571,38 @@ __device__ __forceinline__ void grouped_gemm_body(const GemmArgs& g) {
           fwd_decode_chunk<kMode>(F_dec, sl, lut, Bn, tid);
         }
         if constexpr (kRows >= 0) mfma_slice(rows_c, ac, bc);
-        if constexpr (kDirectA && kNa > 0) load_a_direct(NaC{}, min(ks + 1, nsteps - 1), sl, Ad);
+        if constexpr (kDmaA && kNa > 0) {
+          if (sl == 0) {        // every fragment of step ks has arrived: load step ks+1 over them
+            __builtin_amdgcn_s_waitcnt(0xC07F);            // lgkmcnt(0)
+            dma_a(NaC{}, min(ks + 1, nsteps - 1));
+          }
+        }
       };
+      if constexpr (kDmaA && kNa > 0) read_frags(NaC{}, Ad);  // waits for step ks's rows
       if constexpr (kRows >= 0) load_b_slice(B, 0, b0);
       slice(0, b0, b1);
       slice(1, b1, b0);
       slice(2, b0, b1);
       slice(3, b1, b0);
-      if constexpr (!kDirectA && kNa > 0) {
+      if constexpr (!kDmaA && kNa > 0) {
         stage_a(NaC{}, Ar);                              // step ks+1 (own area: no barrier)
         load_a(NaC{}, min(ks + 2, nsteps - 1), Ar);
       }
-      lds_barrier();
+      if constexpr (kDmaA) {
+        // Barrier without a fence: a release fence would also wait for the
+        // LDS-direct loads in flight (they count as pending LDS writes) and
+        // with them for the code loads just issued.  Those loads write only
+        // this wave's own area, which only this wave reads, after the wait
+        // the compiler inserts for them; lgkmcnt(0) completes this wave's
+        // LDS writes, and the empty asm statements keep every memory access
+        // on its side of the barrier.
+        asm volatile("" ::: "memory");
+        __builtin_amdgcn_s_waitcnt(0xC07F);                // lgkmcnt(0)
+        __builtin_amdgcn_s_barrier();
+        asm volatile("" ::: "memory");
+      } else {
+        lds_barrier();
+      }
     };
     for (int ks = 0; ks < nsteps; ks += 2) {
       step(ks, F1, F0);
