@@ -49,7 +49,9 @@ constexpr int kCStride = 64;      // bytes per LDS row of raw codes (dgrad stagi
 // ---- B producers: fill Bs[col][k] (bf16, row stride kBStride) for step ks ----
 
 // Forward: B[k][col] = W[n0 + col][ks*64 + k].  Thread t decodes 32 weights:
-// col = t % 128, half h = t / 128 (k in [32h, 32h+32)).
+// col = t / 2, half h = t % 2 (k in [32h, 32h+32)), so the two halves of a
+// row's 32 code bytes are neighbouring lanes and a load instruction touches
+// 32 rows rather than 64 (down GEMM 188 -> 185 us).
 struct FwdLoad {
   u32x4 c;
   float a;      // NF4 absmax
@@ -64,7 +66,7 @@ struct FwdLoad {
 template <int kMode>
 __device__ __forceinline__ FwdLoad fwd_load(const GemmArgs& g, int e, int n0, int ks, int tid) {
   FwdLoad L;
-  const int col = tid & (kTN - 1), h = tid >> 7;
+  const int col = tid >> 1, h = tid & 1;
   const int k0 = ks * kTK + h * 32;
   int n;
   if constexpr (kMode == kFwdNF4Glu) {
@@ -94,7 +96,7 @@ __device__ __forceinline__ FwdLoad fwd_load(const GemmArgs& g, int e, int n0, in
 template <int kMode>
 __device__ __forceinline__ void fwd_decode_chunk(const FwdLoad& L, int q, const float* lut,
                                                  uint16_t* Bs, int tid) {
-  const int col = tid & (kTN - 1), h = tid >> 7;
+  const int col = tid >> 1, h = tid & 1;
   uint32_t p[4];
   // Elements outside the matrix get a zero factor (their codes are a clamped
   // re-read): one select per chunk instead of one per output dword.
