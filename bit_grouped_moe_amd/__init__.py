@@ -24,6 +24,7 @@ __all__ = [
     "gq_nf4_grouped_gemv_swiglu", "gq_nf4_grouped_gemm_swiglu", "gq_nf4_grouped_gemv_down_combine",
     "gq_moe_combine", "gq_act_split_e4m3", "gq_mxfp4_grouped_gemm_scaled",
     "gq_mxfp4_grouped_gemv_swiglu", "gq_mxfp4_grouped_gemm_scaled_swiglu",
+    "gq_mxfp4_grouped_gemm_scaled_swiglu_split",
     "gq_mxfp4_grouped_gemv_down_combine", "gq_nf4_grouped_gemv_host", "gq_mxfp4_grouped_gemv_host",
     "OSS_ALPHA", "OSS_LIMIT", "Route",
 ]
@@ -40,6 +41,7 @@ EXPORTED_SYMBOLS = (
     "gq_nf4_grouped_gemv_swiglu", "gq_nf4_grouped_gemm_swiglu", "gq_nf4_grouped_gemv_down_combine",
     "gq_moe_combine", "gq_act_split_e4m3", "gq_mxfp4_grouped_gemm_scaled",
     "gq_mxfp4_grouped_gemv_swiglu", "gq_mxfp4_grouped_gemm_scaled_swiglu",
+    "gq_mxfp4_grouped_gemm_scaled_swiglu_split",
     "gq_mxfp4_grouped_gemv_down_combine", "gq_nf4_grouped_gemv_host", "gq_mxfp4_grouped_gemv_host",
 )
 
@@ -83,6 +85,10 @@ _SIGNATURES = {
     "gq_mxfp4_grouped_gemm_scaled_swiglu": (ctypes.c_int, [_p, _p, _i32, _i32, _p, _p, _i32,
                                                            _i32, _i32, _f32, _f32, _p, _p, _p,
                                                            _p, _i32, _i32, _p, _p]),
+    "gq_mxfp4_grouped_gemm_scaled_swiglu_split": (ctypes.c_int, [_p, _p, _i32, _i32, _p, _p,
+                                                                 _i32, _i32, _i32, _f32, _f32,
+                                                                 _p, _p, _p, _p, _i32, _i32, _p,
+                                                                 _p, _p]),
 }
 
 _lib = None
@@ -617,3 +623,39 @@ def gq_mxfp4_grouped_gemm_scaled_swiglu(x_split, blocks, scales, route, alpha=OS
                                                  _stream(xq))
     _check(st, "gq_mxfp4_grouped_gemm_scaled_swiglu")
     return out
+
+
+def gq_mxfp4_grouped_gemm_scaled_swiglu_split(x_split, blocks, scales, route, alpha=OSS_ALPHA,
+                                              limit=OSS_LIMIT, out=None):
+    """gq_mxfp4_grouped_gemm_scaled_swiglu with the [rows*topk, I] result
+    written as its two-term e4m3 split (the bytes gq_act_split_e4m3 would
+    write for it); returns (codes, scales), the down product's x_split.
+    ``out``: an optional (codes, scales) pair of the split_sizes shapes."""
+    lib = load_library()
+    xq, xsc = x_split
+    _dev(xq, "x_split codes", torch.uint8, 2)
+    _dev(xsc, "x_split scales", torch.uint8, 2)
+    E, N2, K = _mx_bank(blocks, scales)
+    if N2 % 2:
+        raise ValueError("the gate_up width is odd")
+    rows = xq.shape[0]
+    cshape, sshape = split_sizes(rows, K)
+    if tuple(xq.shape) != cshape or tuple(xsc.shape) != sshape:
+        raise ValueError("x_split does not match the weights' K")
+    if route.rows != rows or route.num_experts != E:
+        raise ValueError("x_split and route disagree")
+    P = rows * route.topk
+    ocs, oss = split_sizes(P, N2 // 2)
+    if out is None:
+        out = (torch.empty(ocs, dtype=torch.uint8, device=xq.device),
+               torch.empty(oss, dtype=torch.uint8, device=xq.device))
+    oq, osc = out
+    _dev(oq, "out codes", torch.uint8, 2)
+    _dev(osc, "out scales", torch.uint8, 2)
+    if tuple(oq.shape) != ocs or tuple(osc.shape) != oss:
+        raise ValueError(f"out must be uint8 {ocs} and {oss}")
+    st = lib.gq_mxfp4_grouped_gemm_scaled_swiglu_split(
+        _ptr(xq), _ptr(xsc), rows, K, _ptr(blocks), _ptr(scales), E, N2, route.topk,
+        float(alpha), float(limit), *_route_ptrs(route), _ptr(oq), _ptr(osc), _stream(xq))
+    _check(st, "gq_mxfp4_grouped_gemm_scaled_swiglu_split")
+    return oq, osc

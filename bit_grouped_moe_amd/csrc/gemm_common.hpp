@@ -43,6 +43,8 @@ struct GemmArgs {
   int n_logical;               // max_tiles * n_col_tiles
   uint16_t* out;               // [P, Nout]
   float act_alpha, act_limit;  // gpt-oss gated unit (kernels with the activation epilogue)
+  uint8_t* out_q;              // gated unit written as its two-term e4m3 split instead of
+  uint8_t* out_s;              // bf16: codes [P, 2 Nout], scales [P, Nout / 16] (Nout % 64 == 0)
 };
 
 typedef __attribute__((address_space(3))) void lds_void_t;
@@ -61,7 +63,10 @@ struct TileInfo {
   int e, start, valid, n0;
 };
 
-template <int kTNo>
+// kSplitOut: the output is the e4m3 split (out_q, out_s); a dropped pair's
+// row gets zero codes and zero scale bytes in the tile's column range, which
+// is what the split of a zero row is.
+template <int kTNo, bool kSplitOut = false>
 __device__ __forceinline__ bool tile_head(const GemmArgs& g, int tid, TileInfo& t) {
   const int C = g.n_col_tiles;
   const int bid = blockIdx.x;
@@ -75,6 +80,24 @@ __device__ __forceinline__ bool tile_head(const GemmArgs& g, int tid, TileInfo& 
     const int dstart = g.offsets[g.E] + (tile - T) * kTM;
     if (dstart >= g.P || dstart < 0) return false;
     const int dvalid = min(kTM, g.P - dstart);
+    if constexpr (kSplitOut) {
+      // columns [n0, n0 + ncols): 2 ncols code bytes from byte 2 n0 of the
+      // row, ncols / 16 scale bytes from byte n0 / 16 (multiples of 64)
+      const int ncols = min(kTNo, g.Nout - t.n0);
+      const int per = ncols / 8 + ncols / 64;              // 16-byte code pieces + scale dwords
+      for (int idx = tid; idx < dvalid * per; idx += kGemmThreads) {
+        const int r = idx / per, c = idx % per;
+        const int p = g.sorted_pairs[dstart + r];
+        if ((unsigned)p >= (unsigned)g.P) continue;
+        if (c < ncols / 8)
+          *reinterpret_cast<u32x4*>(g.out_q + (int64_t)p * (2 * g.Nout) + 2 * t.n0 + 16 * c) =
+              u32x4{0u, 0u, 0u, 0u};
+        else
+          *reinterpret_cast<uint32_t*>(g.out_s + (int64_t)p * (g.Nout / 16) + t.n0 / 16 +
+                                       4 * (c - ncols / 8)) = 0u;
+      }
+      return false;
+    }
     for (int idx = tid; idx < dvalid * (kTNo / 8); idx += kGemmThreads) {
       const int r = idx / (kTNo / 8), c8 = idx % (kTNo / 8);
       const int col = t.n0 + c8 * 8;

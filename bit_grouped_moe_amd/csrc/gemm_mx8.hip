@@ -129,6 +129,81 @@ __global__ __launch_bounds__(256) void act_split_kernel(const uint16_t* __restri
   *reinterpret_cast<uint16_t*>(sc + r * (int64_t)(Kp / 16) + s * 4 + 2 * j) = (uint16_t)sbytes;
 }
 
+// The gated unit of one output row's 32-column block, written as its split
+// (the activation epilogue with kSplit).  The block is the two transposed
+// accumulator blocks v0, v1 (32 interleaved gate/up weight rows each) of a
+// row: after the exchanges of store_block_act, lane half h holds the bf16
+// results of block columns 8h + [0, 8) (from v0) and 16 + 8h + [0, 8) (from
+// v1); the two halves' maxima are exchanged once per term, and each lane
+// converts its 16 values exactly as act_split_kernel converts them (so the
+// bytes equal those of the bf16 output split afterwards).  qrow: the row's
+// 128 code bytes of the block's 64-K step; blk: the block's index within it.
+__device__ __forceinline__ void store_block_act_split(const float (&v0)[16], const float (&v1)[16],
+                                                      uint8_t* qrow, uint8_t* srow, int blk,
+                                                      int lh, float alpha, float limit) {
+  float y[16];                                             // this lane's 16 block values
+#pragma unroll
+  for (int cb = 0; cb < 2; ++cb) {
+    const float (&v)[16] = cb ? v1 : v0;
+    uint32_t o[4];
+#pragma unroll
+    for (int q = 0; q < 4; ++q)
+      o[q] = pack_bf16x2(oss_act(v[4 * q], v[4 * q + 1], alpha, limit),
+                         oss_act(v[4 * q + 2], v[4 * q + 3], alpha, limit));
+    const auto a = __builtin_amdgcn_permlane32_swap(o[0], o[2], false, false);
+    const auto b = __builtin_amdgcn_permlane32_swap(o[1], o[3], false, false);
+    const uint32_t w[4] = {a[0], a[1], b[0], b[1]};
+#pragma unroll
+    for (int k = 0; k < 4; ++k) {
+      y[8 * cb + 2 * k] = bf16lo_to_f32(w[k]);
+      y[8 * cb + 2 * k + 1] = bf16hi_to_f32(w[k]);
+    }
+  }
+  // the block maximum over both lane halves (lanes l and l ^ 32)
+  auto block_max = [&](const float (&u)[16]) {
+    float m = 0.f;
+#pragma unroll
+    for (int i = 0; i < 16; ++i) m = fmaxf(m, fabsf(u[i]));
+    // one element of the result is this lane's own value, the other its
+    // partner's (which is which depends on the lane half)
+    const auto x = __builtin_amdgcn_permlane32_swap(__float_as_uint(m), __float_as_uint(m),
+                                                    false, false);
+    return fmaxf(__uint_as_float(x[0]), __uint_as_float(x[1]));
+  };
+  // e4m3 codes of u * 2^-X (4 dwords, element order) and the residual
+  auto term = [&](float (&u)[16], int X, uint32_t (&q)[4]) {
+#pragma unroll
+    for (int d = 0; d < 4; ++d) {
+      int w = __builtin_amdgcn_cvt_pk_fp8_f32(__builtin_amdgcn_ldexpf(u[4 * d], -X),
+                                              __builtin_amdgcn_ldexpf(u[4 * d + 1], -X), 0,
+                                              false);
+      w = __builtin_amdgcn_cvt_pk_fp8_f32(__builtin_amdgcn_ldexpf(u[4 * d + 2], -X),
+                                          __builtin_amdgcn_ldexpf(u[4 * d + 3], -X), w, true);
+      q[d] = (uint32_t)w;
+      const f32x2 lo = __builtin_amdgcn_cvt_pk_f32_fp8(w, false);
+      const f32x2 hi = __builtin_amdgcn_cvt_pk_f32_fp8(w, true);
+      u[4 * d] -= __builtin_amdgcn_ldexpf(lo.x, X);
+      u[4 * d + 1] -= __builtin_amdgcn_ldexpf(lo.y, X);
+      u[4 * d + 2] -= __builtin_amdgcn_ldexpf(hi.x, X);
+      u[4 * d + 3] -= __builtin_amdgcn_ldexpf(hi.y, X);
+    }
+  };
+  uint32_t qh[4], ql[4];
+  const int Xh = split_exponent(block_max(y));
+  term(y, Xh, qh);                                         // y is now the exact residual
+  const int Xl = split_exponent(block_max(y));
+  term(y, Xl, ql);
+  // elements [0, 16) at byte 16 blk, [16, 32) at 32 + 16 blk; lo codes + 64
+  const int o0 = 16 * blk + 8 * lh, o1 = 32 + 16 * blk + 8 * lh;
+  *reinterpret_cast<uint2*>(qrow + o0) = uint2{qh[0], qh[1]};
+  *reinterpret_cast<uint2*>(qrow + o1) = uint2{qh[2], qh[3]};
+  *reinterpret_cast<uint2*>(qrow + 64 + o0) = uint2{ql[0], ql[1]};
+  *reinterpret_cast<uint2*>(qrow + 64 + o1) = uint2{ql[2], ql[3]};
+  if (lh == 0)
+    *reinterpret_cast<uint16_t*>(srow + 2 * blk) =
+        (uint16_t)((uint32_t)(Xh + 127) | ((uint32_t)(Xl + 127) << 8));
+}
+
 // ---- the grouped GEMM: 256 pairs x 256 columns per workgroup ----------------
 // One wave per SIMD; wave w owns the columns n0 + 64 w + [0, 64) (two
 // column blocks of 32) for every 32-row sub-tile of the tile (4 or 8
@@ -161,7 +236,7 @@ __device__ __forceinline__ void step_barrier() {
   asm volatile("" ::: "memory");
 }
 
-template <int kSub, bool kAct>
+template <int kSub, bool kAct, bool kSplit>
 __device__ __forceinline__ void mx8_columns(const GemmArgs& g, const TileInfo& t, int tid,
                                             uint8_t* A0, uint8_t* A1, uint32_t* S0, uint32_t* S1,
                                             int* pair_s, int* row_s, float* scale_s) {
@@ -322,7 +397,27 @@ __device__ __forceinline__ void mx8_columns(const GemmArgs& g, const TileInfo& t
   else if (allcols && nrows == I5::value) run_loop(I5{});
   else run_loop(std::integral_constant<int, -1>{});
 
-  if constexpr (kAct) {
+  if constexpr (kSplit) {
+    // the wave's 32 output columns are one split block of each row
+    const int col = t.n0 + 32 * wave;                      // output column (Nout % 64 == 0)
+#pragma unroll
+    for (int i = 0; i < kSub; ++i) {
+      if (i >= nrows) continue;
+      const int m = 32 * i + lr;
+      const int p = pair_s[m];
+      if (m < valid && col < g.Nout) {
+        float v0[16], v1[16];
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+          v0[r] = acc[i][0][r];
+          v1[r] = acc[i][1][r];
+        }
+        store_block_act_split(v0, v1, g.out_q + (int64_t)p * (2 * g.Nout) + 2 * (col & ~63),
+                              g.out_s + (int64_t)p * (g.Nout / 16) + (col & ~63) / 16,
+                              (col >> 5) & 1, lh, g.act_alpha, g.act_limit);
+      }
+    }
+  } else if constexpr (kAct) {
 #pragma unroll
     for (int i = 0; i < kSub; ++i) {
       if (i >= nrows) continue;
@@ -345,8 +440,9 @@ __device__ __forceinline__ void mx8_columns(const GemmArgs& g, const TileInfo& t
 }
 
 // kAct: gate_up product with the gpt-oss gated unit applied in the epilogue
-// (weight rows 2j, 2j + 1 -> output column j of an [P, N/2] result).
-template <bool kAct>
+// (weight rows 2j, 2j + 1 -> output column j of an [P, N/2] result); kSplit:
+// that result written as its two-term e4m3 split (the next product's input).
+template <bool kAct, bool kSplit = false>
 __global__ __launch_bounds__(kGemmThreads, 1) void grouped_gemm_mx8_kernel(GemmArgs g) {
   // separate arrays: an LDS-direct load into one buffer does not alias reads
   // of the other
@@ -359,11 +455,11 @@ __global__ __launch_bounds__(kGemmThreads, 1) void grouped_gemm_mx8_kernel(GemmA
   __shared__ float scale_s[kTM];                           // its pair weight (1 if none)
   const int tid = threadIdx.x;
   TileInfo t;
-  if (!tile_head<kAct ? kXN / 2 : kXN>(g, tid, t)) return;
+  if (!tile_head<kAct ? kXN / 2 : kXN, kSplit>(g, tid, t)) return;
   if (t.valid <= kMx8Rows)
-    mx8_columns<4, kAct>(g, t, tid, A0, A1, S0, S1, pair_s, row_s, scale_s);
+    mx8_columns<4, kAct, kSplit>(g, t, tid, A0, A1, S0, S1, pair_s, row_s, scale_s);
   else
-    mx8_columns<8, kAct>(g, t, tid, A0, A1, S0, S1, pair_s, row_s, scale_s);
+    mx8_columns<8, kAct, kSplit>(g, t, tid, A0, A1, S0, S1, pair_s, row_s, scale_s);
 }
 
 static inline int64_t split_kp(int64_t K) { return (K + kTK - 1) / kTK * kTK; }
@@ -388,15 +484,19 @@ extern "C" int gq_act_split_e4m3(const uint16_t* x, int32_t rows, int32_t K, int
 
 namespace gq {
 
-template <bool kAct>
+// kSplit (with kAct): the result goes to out_q / out_s as its split instead
+// of to out.
+template <bool kAct, bool kSplit = false>
 static int mx8_entry(const uint8_t* x_codes, const uint8_t* x_scales, int32_t rows, int32_t K,
                      const uint8_t* blocks, const uint8_t* scales, int32_t num_experts, int32_t N,
                      int32_t topk, const float* pair_scale, float alpha, float limit,
                      const int32_t* expert_offsets, const int32_t* sorted_pairs,
                      const int32_t* tiles, const int32_t* num_tiles, int32_t max_tiles,
-                     int32_t tile_m, uint16_t* out, hipStream_t stream) {
+                     int32_t tile_m, uint16_t* out, hipStream_t stream, uint8_t* out_q = nullptr,
+                     uint8_t* out_s = nullptr) {
   if (rows < 0 || topk < 1 || num_experts < 1 || N < 1 || N % 32 || K <= 0 || K % 32)
     return kInvalid;
+  if (kSplit && N % 128) return kNotSupported;             // whole 64-column split steps
   if (kAct && !(limit >= 0.f && limit < 3.4e38f && alpha == alpha && alpha > -3.4e38f &&
                 alpha < 3.4e38f))
     return kInvalid;                                       // finite alpha, limit >= 0
@@ -407,10 +507,12 @@ static int mx8_entry(const uint8_t* x_codes, const uint8_t* x_scales, int32_t ro
   const int64_t Kp = split_kp(K);
   if ((int64_t)rows * 2 * Kp >= INT32_MAX) return kNotSupported;   // 32-bit row offsets
   if (!x_codes || !x_scales || !blocks || !scales || !expert_offsets || !sorted_pairs || !tiles ||
-      !num_tiles || !out)
+      !num_tiles)
     return kInvalid;
-  if (!aligned16(x_codes) || !aligned4(x_scales) || !aligned16(blocks) || !aligned16(out))
+  if (kSplit ? (!out_q || !out_s || !aligned16(out_q) || !aligned4(out_s))
+             : (!out || !aligned16(out)))
     return kInvalid;
+  if (!aligned16(x_codes) || !aligned4(x_scales) || !aligned16(blocks)) return kInvalid;
   if (!aligned4(expert_offsets) || !aligned4(sorted_pairs) || !aligned4(tiles) ||
       !aligned4(num_tiles) || (pair_scale && !aligned4(pair_scale)))
     return kInvalid;
@@ -427,14 +529,15 @@ static int mx8_entry(const uint8_t* x_codes, const uint8_t* x_scales, int32_t ro
   g.offsets = expert_offsets; g.sorted_pairs = sorted_pairs; g.tiles = tiles;
   g.num_tiles = num_tiles; g.out = out;
   g.act_alpha = alpha; g.act_limit = limit;
+  g.out_q = out_q; g.out_s = out_s;
   g.n_col_tiles = (N + kXN - 1) / kXN;                     // 256 weight rows per tile
   const int64_t n_logical = (int64_t)max_tiles * g.n_col_tiles;
   const int64_t group = 8LL * g.n_col_tiles;
   const int64_t grid = ((n_logical + group - 1) / group) * group;
   if (grid > INT32_MAX) return kNotSupported;
   g.n_logical = (int)n_logical;
-  hipLaunchKernelGGL(grouped_gemm_mx8_kernel<kAct>, dim3((unsigned)grid), dim3(kGemmThreads), 0,
-                     stream, g);
+  hipLaunchKernelGGL((grouped_gemm_mx8_kernel<kAct, kSplit>), dim3((unsigned)grid),
+                     dim3(kGemmThreads), 0, stream, g);
   return launch_status();
 }
 
@@ -462,4 +565,16 @@ extern "C" int gq_mxfp4_grouped_gemm_scaled_swiglu(
   return gq::mx8_entry<true>(x_codes, x_scales, rows, K, blocks, scales, num_experts, N, topk,
                              nullptr, alpha, limit, expert_offsets, sorted_pairs, tiles,
                              num_tiles, max_tiles, tile_m, act, stream);
+}
+
+extern "C" int gq_mxfp4_grouped_gemm_scaled_swiglu_split(
+    const uint8_t* x_codes, const uint8_t* x_scales, int32_t rows, int32_t K,
+    const uint8_t* blocks, const uint8_t* scales, int32_t num_experts, int32_t N, int32_t topk,
+    float alpha, float limit, const int32_t* expert_offsets, const int32_t* sorted_pairs,
+    const int32_t* tiles, const int32_t* num_tiles, int32_t max_tiles, int32_t tile_m,
+    uint8_t* act_codes, uint8_t* act_scales, hipStream_t stream) {
+  return gq::mx8_entry<true, true>(x_codes, x_scales, rows, K, blocks, scales, num_experts, N,
+                                   topk, nullptr, alpha, limit, expert_offsets, sorted_pairs,
+                                   tiles, num_tiles, max_tiles, tile_m, nullptr, stream,
+                                   act_codes, act_scales);
 }

@@ -276,6 +276,19 @@ int gq_mxfp4_grouped_gemm(const uint16_t* x, int32_t rows, int32_t K, int64_t x_
  * with N = 2I; act uint16 bf16 [rows*topk, I], rows of dropped pairs zero.
  * No pair_scale.  Errors as gq_mxfp4_grouped_gemm_scaled, plus
  * InvalidValue for a non-finite alpha or limit, or limit < 0.
+ *
+ * gq_mxfp4_grouped_gemm_scaled_swiglu_split: the same product and gated
+ * unit, the bf16 result written as its two-term e4m3 split (the layout of
+ * gq_act_split_e4m3 for [rows*topk, I]) instead of as bf16, so that it
+ * feeds the down product directly:
+ *
+ *   act_codes, act_scales = gq_act_split_e4m3(act)   (bytes identical)
+ *
+ * act_codes uint8 [rows*topk, 2I] (16-byte aligned), act_scales uint8
+ * [rows*topk, I/16] (4-byte aligned); rows of dropped pairs get zero codes
+ * and zero scale bytes (the split of a zero row).  Errors as
+ * gq_mxfp4_grouped_gemm_scaled_swiglu; NotSupported also when N % 128 != 0
+ * (I a multiple of 64: whole 64-column split steps).
  */
 int gq_act_split_e4m3(const uint16_t* x, int32_t rows, int32_t K, int64_t x_stride,
                       uint8_t* codes, uint8_t* scales, hipStream_t stream);
@@ -294,6 +307,12 @@ int gq_mxfp4_grouped_gemm_scaled_swiglu(const uint8_t* x_codes, const uint8_t* x
                                         const int32_t* sorted_pairs, const int32_t* tiles,
                                         const int32_t* num_tiles, int32_t max_tiles,
                                         int32_t tile_m, uint16_t* act, hipStream_t stream);
+int gq_mxfp4_grouped_gemm_scaled_swiglu_split(
+    const uint8_t* x_codes, const uint8_t* x_scales, int32_t rows, int32_t K,
+    const uint8_t* blocks, const uint8_t* scales, int32_t num_experts, int32_t N, int32_t topk,
+    float alpha, float limit, const int32_t* expert_offsets, const int32_t* sorted_pairs,
+    const int32_t* tiles, const int32_t* num_tiles, int32_t max_tiles, int32_t tile_m,
+    uint8_t* act_codes, uint8_t* act_scales, hipStream_t stream);
 
 /* ------------------------------------------------------------------------
  * NF4 input gradient.  [P1] "Which entry point?" (grouped NF4 backward);

@@ -113,3 +113,27 @@ def plus_zero(bits):
     b = np.asarray(bits, dtype=np.uint16).copy()
     b[b == 0x8000] = 0
     return b
+
+
+def unpermute_split(codes, scales, K):
+    """Natural-order (hi, lo, s_hi, s_lo) from the split kernel's layout:
+    per 64-k step, 128 bytes = hi then lo (64 each); in each, bytes
+    [32h, 32h + 32) hold elements 16h + [0, 16) of k block 2s, then of
+    block 2s + 1; scales per step s_hi(2s), s_lo(2s), s_hi(2s+1), s_lo(2s+1)."""
+    rows = codes.shape[0]
+    kp = codes.shape[1] // 2
+    c = codes.reshape(rows, kp // 64, 2, 2, 2, 16)        # [row, step, term, h, block, i]
+    c = c.transpose(0, 1, 2, 4, 3, 5)                     # [row, step, term, block, h, i]
+    hi = c[:, :, 0].reshape(rows, kp)[:, :K]
+    lo = c[:, :, 1].reshape(rows, kp)[:, :K]
+    s = scales.reshape(rows, kp // 64, 2, 2)              # [row, step, block, term]
+    s_hi = s[:, :, :, 0].reshape(rows, kp // 32)[:, :K // 32]
+    s_lo = s[:, :, :, 1].reshape(rows, kp // 32)[:, :K // 32]
+    return hi, lo, s_hi, s_lo
+
+
+def same_codes(a, b):
+    """e4m3 codes equal up to the sign of zero (0x00 vs 0x80 hold the same value)."""
+    a = np.where(a == 0x80, 0, a)
+    b = np.where(b == 0x80, 0, b)
+    return np.array_equal(a, b)

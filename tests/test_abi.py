@@ -304,6 +304,23 @@ def test_gpt_oss_activation_entry_points_reject(lib):
     assert gemm(a15=60) == INVALID
     assert gemm(a17=NULL) == INVALID
     assert gemm(a2=0) == 0
+    # the same product written as the split: ..., act_codes, act_scales
+    m2 = m[:17] + [F, F, None]
+
+    def gemm_split(**kw):
+        a = list(m2)
+        for i, v in kw.items():
+            a[int(i[1:])] = v
+        return lib.gq_mxfp4_grouped_gemm_scaled_swiglu_split(*a)
+    assert gemm_split(a7=5750) == INVALID                  # N % 32
+    assert gemm_split(a7=5728) == NOT_SUPPORTED            # I = 2864: not whole 64-column steps
+    assert gemm_split(a10=nan) == INVALID
+    assert gemm_split(a17=NULL) == INVALID
+    assert gemm_split(a18=NULL) == INVALID
+    assert gemm_split(a17=ctypes.c_void_p(0x1008)) == INVALID   # codes not 16-byte aligned
+    assert gemm_split(a18=ctypes.c_void_p(0x1002)) == INVALID   # scales not 4-byte aligned
+    assert gemm_split(a16=128) == NOT_SUPPORTED
+    assert gemm_split(a2=0) == 0
 
 
 def test_host_bank_entry_points_reject_unpinned_memory(lib):

@@ -14,40 +14,16 @@ import bit_grouped_moe_amd as gq
 import oracle
 import workloads as wl
 from tests.gpu_common import (LazyDecoded, assert_rows, assert_slices, bf16_bits,
-                              bf16_to_host_f32, device, packed_mx_bank, plus_zero, say, to_dev,
-                              to_dev_bf16)
+                              bf16_to_host_f32, device, packed_mx_bank, plus_zero, same_codes, say,
+                              to_dev, to_dev_bf16, unpermute_split)
 
 pytestmark = pytest.mark.gpu
-
-
-def unpermute_split(codes, scales, K):
-    """Natural-order (hi, lo, s_hi, s_lo) from the split kernel's layout:
-    per 64-k step, 128 bytes = hi then lo (64 each); in each, bytes
-    [32h, 32h + 32) hold elements 16h + [0, 16) of k block 2s, then of
-    block 2s + 1; scales per step s_hi(2s), s_lo(2s), s_hi(2s+1), s_lo(2s+1)."""
-    rows = codes.shape[0]
-    kp = codes.shape[1] // 2
-    c = codes.reshape(rows, kp // 64, 2, 2, 2, 16)        # [row, step, term, h, block, i]
-    c = c.transpose(0, 1, 2, 4, 3, 5)                     # [row, step, term, block, h, i]
-    hi = c[:, :, 0].reshape(rows, kp)[:, :K]
-    lo = c[:, :, 1].reshape(rows, kp)[:, :K]
-    s = scales.reshape(rows, kp // 64, 2, 2)              # [row, step, block, term]
-    s_hi = s[:, :, :, 0].reshape(rows, kp // 32)[:, :K // 32]
-    s_lo = s[:, :, :, 1].reshape(rows, kp // 32)[:, :K // 32]
-    return hi, lo, s_hi, s_lo
 
 
 def _split(x_bits, dev):
     codes, scales = gq.gq_act_split_e4m3(to_dev_bf16(x_bits, dev))
     torch.cuda.synchronize()
     return codes.cpu().numpy(), scales.cpu().numpy()
-
-
-def _same_codes(a, b):
-    """e4m3 codes equal up to the sign of zero (0x00 vs 0x80 hold the same value)."""
-    a = np.where(a == 0x80, 0, a)
-    b = np.where(b == 0x80, 0, b)
-    return np.array_equal(a, b)
 
 
 @pytest.mark.parametrize("rows,K", [(7, 64), (33, 2880), (5, 544), (64, 2048), (3, 32)])
@@ -67,7 +43,7 @@ def test_split_bit_exact(rows, K):
     hi, lo, sh, sl = unpermute_split(codes, scales, K)
     rhi, rlo, rsh, rsl = oracle.act_split_e4m3(x)
     assert np.array_equal(sh, rsh) and np.array_equal(sl, rsl)
-    assert _same_codes(hi, rhi) and _same_codes(lo, rlo)
+    assert same_codes(hi, rhi) and same_codes(lo, rlo)
     kp = codes.shape[1] // 2
     if kp > K:                                            # pad block: zeros, scale 0
         c = codes.reshape(rows, kp // 64, 2, 2, 2, 16)

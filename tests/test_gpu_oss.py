@@ -15,7 +15,8 @@ import bit_grouped_moe_amd as gq
 import oracle
 import workloads as wl
 from tests.gpu_common import (LazyDecoded, assert_rows, assert_slices, bf16_bits,
-                              bf16_to_host_f32, device, packed_mx_bank, say, to_dev, to_dev_bf16)
+                              bf16_to_host_f32, device, packed_mx_bank, same_codes, say, to_dev,
+                              to_dev_bf16, unpermute_split)
 
 pytestmark = pytest.mark.gpu
 
@@ -198,6 +199,90 @@ def test_gemm_scaled_swiglu_oss_gptoss_full():
     rows = np.nonzero(np.isin(ids.reshape(-1), check))[0]
     assert_rows(got[rows], ref[rows], what="sampled experts")
     assert not got[drop].any()
+
+
+# ---- the gated unit written as the next product's e4m3 split ----------------------
+def _split_pair(x_bits, blocks, scales, ids, E, dev):
+    """(fused split, split of the bf16 result) of the same gate_up product."""
+    route = gq.gq_route_sort(to_dev(ids.astype(np.int32), dev), E)
+    xs = gq.gq_act_split_e4m3(to_dev_bf16(x_bits, dev))
+    fused = gq.gq_mxfp4_grouped_gemm_scaled_swiglu_split(xs, blocks, scales, route)
+    act = gq.gq_mxfp4_grouped_gemm_scaled_swiglu(xs, blocks, scales, route)
+    after = gq.gq_act_split_e4m3(act)
+    torch.cuda.synchronize()
+    return fused, after, act
+
+
+def _assert_same_bytes(fused, after):
+    for a, b, what in zip(fused, after, ("codes", "scales")):
+        diff = (a != b).nonzero()
+        assert diff.shape[0] == 0, (what, diff[:5].tolist())
+
+
+@pytest.mark.parametrize("N2,K,xstd", [(256, 1056, 1.0), (640, 2880, 8.0), (384, 64, 8.0)])
+def test_gemm_scaled_swiglu_split_equals_split_of_result(N2, K, xstd):
+    """The fused split's code and scale bytes equal gq_act_split_e4m3 of the
+    bf16 result, over skewed routing on several tiles, I = 128, 320 and 192
+    (a last 128-output tile half full), clamped values, dropped and
+    out-of-range ids (their rows: zero codes, zero scale bytes)."""
+    dev = device()
+    g = np.random.default_rng(3 * N2 + K + int(xstd))
+    E, M, topk = 6, 700, 2
+    blocks, scales = packed_mx_bank(g, E, N2, K)
+    ids = wl.route_zipf(g, M, E, topk, s=2.5)
+    ids[g.random(ids.shape) < 0.02] = -1
+    ids[:, 1][ids[:, 1] == 4] = E
+    x = wl.draw_bf16(g, (M, K), std=xstd)
+    say("mx8 swiglu split", N2, K, xstd)
+    fused, after, act = _split_pair(x, to_dev(blocks, dev), to_dev(scales, dev), ids, E, dev)
+    assert tuple(fused[0].shape) == (M * topk, N2) and tuple(fused[1].shape) == (M * topk, N2 // 32)
+    _assert_same_bytes(fused, after)
+    dropped = torch.from_numpy((ids.reshape(-1) < 0) | (ids.reshape(-1) >= E)).to(dev)
+    assert int(dropped.sum()) > 0
+    assert not fused[0][dropped].any() and not fused[1][dropped].any()
+    # and against the oracle's split of the bf16 result
+    hi, lo, sh, sl = unpermute_split(fused[0].cpu().numpy(), fused[1].cpu().numpy(), N2 // 2)
+    rhi, rlo, rsh, rsl = oracle.act_split_e4m3(bf16_bits(act))
+    assert np.array_equal(sh, rsh) and np.array_equal(sl, rsl)
+    assert same_codes(hi, rhi) and same_codes(lo, rlo)
+
+
+def test_gemm_scaled_swiglu_split_tile_edges():
+    """Segments of 128/129, 161, 224, 256/257, 1, 33 rows, an empty expert
+    and dropped pairs in flatten mode: bytes equal the split of the result."""
+    dev = device()
+    g = np.random.default_rng(78)
+    sizes = [128, 129, 161, 224, 256, 257, 1, 33, 0]
+    E, N2, K = len(sizes), 384, 2880
+    ids = np.concatenate([np.full(n, e, dtype=np.int32) for e, n in enumerate(sizes)]
+                         + [np.full(5, -1, dtype=np.int32)])
+    ids = g.permutation(ids).reshape(-1, 1)
+    blocks, scales = packed_mx_bank(g, E, N2, K)
+    x = wl.draw_bf16(g, (ids.shape[0], K), std=4.0)
+    say("mx8 swiglu split tile edges")
+    fused, after, _ = _split_pair(x, to_dev(blocks, dev), to_dev(scales, dev), ids, E, dev)
+    _assert_same_bytes(fused, after)
+
+
+def test_gemm_scaled_swiglu_split_gptoss_full():
+    """gpt-oss-20b gate_up at M = 2048, top-4 of 32, with dropped pairs:
+    every code and scale byte of the fused split equals the split of the
+    bf16 result (both on the device; the bf16 result is checked against the
+    oracle by test_gemm_scaled_swiglu_oss_gptoss_full)."""
+    dev = device()
+    E, topk = wl.GPTOSS["E"], wl.GPTOSS["topk"]
+    N2, K = wl.GPTOSS["gate_up"]
+    M = 2048
+    blocks, scales = wl.random_mxfp4_bank(E, N2, K, dev, seed=4401)
+    ids = wl.route_uniform(wl.rng(wl.CFG_GPTOSS, wl.S_ROUTE), M, E, topk).copy()
+    drop = np.random.default_rng(45).choice(ids.size, 29, replace=False)
+    ids.reshape(-1)[drop] = -1
+    x = wl.draw_bf16(wl.rng(wl.CFG_GPTOSS, wl.S_X), (M, K), std=4.0)
+    say("mx8 swiglu split gpt-oss full")
+    fused, after, _ = _split_pair(x, blocks, scales, ids, E, dev)
+    _assert_same_bytes(fused, after)
+    d = torch.from_numpy(drop).to(dev)
+    assert not fused[0][d].any() and not fused[1][d].any()
 
 
 # ---- decode down projection with the router-weighted combine -------------------
