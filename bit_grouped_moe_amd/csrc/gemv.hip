@@ -222,6 +222,7 @@ __global__ __launch_bounds__(kGemvMaxThreads) void grouped_gemv_kernel(
         red[i * kStride + tid] = active ? segment_dot<kMx>(lut, cw[i], am[i], sb[i], xf) : 0.f;
       lds_barrier();
       vals[0] = 0.f;
+      bool unit_done = false;                // the gated unit already applied (uniform)
       if (8 * R <= NT) {
         // eight threads per row (segments part, part + 8, ...), then an
         // 8-lane DPP sum; the total goes through LDS to thread r
@@ -243,7 +244,12 @@ __global__ __launch_bounds__(kGemvMaxThreads) void grouped_gemv_kernel(
         lds_barrier();                                         // every partial read
         if (rr < R && part == 7) red[rr] = v;
         lds_barrier();
-        if (tid < R) vals[0] = red[tid];
+        if constexpr (kGlu) {                // the row totals are in LDS already
+          vals[0] = tid < Rout ? act_pair(red[tid], red[tid + Rout]) : 0.f;
+          unit_done = true;
+        } else {
+          if (tid < R) vals[0] = red[tid];
+        }
       } else if (tid < R) {                                    // R <= NT (host check)
         const int gg = tid % G, ii = tid / G;                  // weight row wrow(gg, ii)
         const float* src = red + ii * kStride + gg * S;
@@ -260,10 +266,12 @@ __global__ __launch_bounds__(kGemvMaxThreads) void grouped_gemv_kernel(
       }
       lds_barrier();
       if constexpr (kGlu) {                  // gate row r pairs with up row r + R/2
-        if (tid < R) red[tid] = vals[0];
-        lds_barrier();
-        vals[0] = tid < Rout ? act_pair(red[tid], red[tid + Rout]) : 0.f;
-        lds_barrier();
+        if (!unit_done) {
+          if (tid < R) red[tid] = vals[0];
+          lds_barrier();
+          vals[0] = tid < Rout ? act_pair(red[tid], red[tid + Rout]) : 0.f;
+          lds_barrier();
+        }
       }
     }
   };
