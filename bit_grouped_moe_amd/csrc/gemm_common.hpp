@@ -208,7 +208,7 @@ __device__ __forceinline__ void store_wide_rows(const f32x16 (&acc)[kSub][2], in
 __device__ __forceinline__ float oss_act(float gate, float up, float alpha, float limit) {
   const float gc = fminf(gate, limit);
   const float uc = fminf(fmaxf(up, -limit), limit);
-  return gc / (1.0f + expf(-alpha * gc)) * (uc + 1.0f);
+  return gc * sigmoid_f32(alpha * gc) * (uc + 1.0f);
 }
 
 // Activation epilogue of one transposed accumulator block whose 32 columns

@@ -191,7 +191,7 @@ __global__ __launch_bounds__(kGemvMaxThreads) void grouped_gemv_kernel(
     if constexpr (kAct == 2) {
       const float gc = fminf(gate, limit);
       const float uc = fminf(fmaxf(up, -limit), limit);
-      return gc / (1.0f + expf(-alpha * gc)) * (uc + 1.0f);
+      return gc * sigmoid_f32(alpha * gc) * (uc + 1.0f);
     } else {
       return silu_f32(gate) * up;
     }

@@ -272,7 +272,9 @@ int gq_mxfp4_grouped_gemm(const uint16_t* x, int32_t rows, int32_t K, int64_t x_
  *   act[p, j] = bf16( gc * sigmoid(alpha * gc) * (uc + 1) ),
  *   gc = min(g, limit),  uc = min(max(u, -limit), limit)
  *
- * in float32 (gpt-oss: alpha = 1.702, limit = 7).  blocks/scales [E, N, K]
+ * in float32, sigmoid(z) = 1 / (1 + 2^(-z log2 e)) from the hardware
+ * exponential and reciprocal (a few float32 ulp; gpt-oss: alpha = 1.702,
+ * limit = 7).  blocks/scales [E, N, K]
  * with N = 2I; act uint16 bf16 [rows*topk, I], rows of dropped pairs zero.
  * No pair_scale.  Errors as gq_mxfp4_grouped_gemm_scaled, plus
  * InvalidValue for a non-finite alpha or limit, or limit < 0.
@@ -366,7 +368,9 @@ int gq_mxfp4_grouped_dgrad(const uint16_t* dy, int32_t P, int32_t N, int64_t dy_
  * [I, 2I) in a fused gate_up weight; SwiGLU act = silu(gate) * up with
  * silu(z) = z / (1 + exp(-z)); combine = router-weighted sum over a
  * token's slots, in slot order).  All arithmetic float32, one bf16
- * rounding per output.
+ * rounding per output; sigmoid (in silu and in gpt-oss's gated unit) is
+ * 1 / (1 + 2^(-z log2 e)) from the hardware exponential and reciprocal, a
+ * few float32 ulp from the correctly rounded value.
  *
  * gq_nf4_grouped_gemv_swiglu / gq_nf4_grouped_gemm_swiglu:
  *   act[p, j] = bf16( silu(g) * u ),  g = sum_k x[p/topk, k] * W[j, k],
