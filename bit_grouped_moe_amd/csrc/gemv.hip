@@ -427,6 +427,7 @@ __global__ __launch_bounds__(kWave * kCombineMaxWaves) void gemv_down_combine_ke
     int a_stride, int topk, int P, const float* __restrict__ tw, uint16_t* __restrict__ y) {
   __shared__ float lut[16];
   __shared__ float ys[kCombineMaxYs];                      // [P][Rb]
+  __shared__ float tws[kCombineMaxPairs];                  // router weights
 
   // layout derived from I and P as on the host (arguments ordered as in
   // grouped_gemv_kernel)
@@ -447,7 +448,11 @@ __global__ __launch_bounds__(kWave * kCombineMaxWaves) void gemv_down_combine_ke
   }
   const size_t row_bytes = (size_t)I / 2;
 
-  // ---- round trip 1: the wave's experts (scalar) and activation slices ----
+  // ---- round trip 1: the wave's experts (scalar) and activation slices; the
+  // router weight of pair tid too, kept in a register until the combine (a
+  // load there, after the arithmetic, put a memory round trip at the end of
+  // every workgroup; into LDS at once, its wait held the weight loads back)
+  const float tw_own = (tw && tid < P) ? tw[tid] : 1.f;
   int pp[kPPW], ee[kPPW];
   u32x4 xr[kPPW][kSeg][4];
 #pragma unroll
@@ -517,6 +522,7 @@ __global__ __launch_bounds__(kWave * kCombineMaxWaves) void gemv_down_combine_ke
       if (s == W - 1 && p < P) ys[p * Rb + g * kR + i] = (unsigned)ee[q] < (unsigned)E ? tot : 0.f;
     }
   }
+  if (tid < P) tws[tid] = tw_own;
   lds_barrier();
   // ---- combine: thread (t, r) sums its token's slots in order ----
   const int rows = P / topk;
@@ -527,8 +533,7 @@ __global__ __launch_bounds__(kWave * kCombineMaxWaves) void gemv_down_combine_ke
     float acc = 0.f;
     for (int sl = 0; sl < topk; ++sl) {
       const int p = t * topk + sl;
-      const float w = tw ? tw[p] : 1.f;
-      acc = __builtin_fmaf(w, ys[p * Rb + r], acc);
+      acc = __builtin_fmaf(tws[p], ys[p * Rb + r], acc);
     }
     y[(int64_t)t * H + n] = f32_to_bf16_bits(acc);
   }
