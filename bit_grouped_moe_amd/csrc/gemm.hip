@@ -703,12 +703,16 @@ __device__ __forceinline__ void fwd_columns(const GemmArgs& g, int e, int n0, in
   };
   NLoad X = load(0);
   NLoad Y = load(min(1, nsteps - 1));
+  // The pair weight of this thread's row is loaded here but put into LDS only
+  // after the main loop: written now, its dependent load would be waited for
+  // before the prologue barrier (gate_up 312 -> 307 us).
+  float psc;
   {
     int p = g.sorted_pairs[start + min(tid, valid - 1)];
     p = ((unsigned)p < (unsigned)g.P) ? p : 0;
     pair_s[tid] = p;
     row_s[tid] = p / g.topk;
-    scale_s[tid] = g.pair_scale ? g.pair_scale[p] : 1.f;
+    psc = g.pair_scale ? g.pair_scale[p] : 1.f;
   }
   if constexpr (!kMx) nf4_pairs_init(lut2, tid);
   lds_barrier();
@@ -850,6 +854,8 @@ __device__ __forceinline__ void fwd_columns(const GemmArgs& g, int e, int n0, in
   else if (allcols && nrows == I6::value) run_loop(I6{});
   else if (allcols && nrows == I5::value) run_loop(I5{});
   else run_loop(std::integral_constant<int, -1>{});
+  scale_s[tid] = psc;
+  lds_barrier();
 
   // ---- epilogue: one output row per lane ----
   if constexpr (kGlu) {
