@@ -255,12 +255,15 @@ __device__ __forceinline__ void mx8_columns(const GemmArgs& g, const TileInfo& t
     return n_load<kFwdMX8>(g, t.e, jcol, ks, full ? lh : 0);
   };
   NLoad X = load(0), Y = load(min(1, nsteps - 1));
+  // the row's pair weight goes to LDS after the main loop (as in the bf16
+  // kernel: the prologue barrier then does not wait for its dependent load)
+  float psc;
   {
     int p = g.sorted_pairs[t.start + min(tid, valid - 1)];
     p = ((unsigned)p < (unsigned)g.P) ? p : 0;
     pair_s[tid] = p;
     row_s[tid] = p / g.topk;
-    scale_s[tid] = g.pair_scale ? g.pair_scale[p] : 1.f;
+    psc = g.pair_scale ? g.pair_scale[p] : 1.f;
   }
   lds_barrier();
 
@@ -396,6 +399,8 @@ __device__ __forceinline__ void mx8_columns(const GemmArgs& g, const TileInfo& t
   else if (allcols && nrows == I6::value) run_loop(I6{});
   else if (allcols && nrows == I5::value) run_loop(I5{});
   else run_loop(std::integral_constant<int, -1>{});
+  scale_s[tid] = psc;
+  lds_barrier();
 
   if constexpr (kSplit) {
     // the wave's 32 output columns are one split block of each row
