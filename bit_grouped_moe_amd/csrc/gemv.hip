@@ -580,14 +580,16 @@ static int launch_down_combine(const uint16_t* act, int32_t rows, int32_t I, int
   int S, W, G, NT;
   segment_layout(I, S, W, G, NT);
   if (two_seg) W = kWave;
-  // rows per lane group: 2 for one pair per wave (as the GEMV), 1 otherwise
-  const int kr = ppw == 1 ? 2 : 1;
+  // rows per lane group: 2 for one pair per wave (as the GEMV; 4 when a row
+  // takes the whole wave: half the workgroups, gpt-oss decode layer 18.6 ->
+  // 17.7 us, while 8 rows ran at 31 us), 1 otherwise
+  const int kr = ppw == 1 ? (two_seg ? 4 : 2) : 1;
   const int Rb = (kWave / W) * kr;
   if (P * Rb > kCombineMaxYs) return kNotSupported;
   const dim3 grid((H + Rb - 1) / Rb);
   if (two_seg) {
     if (ppw == 1)
-      launch_dc<kMx, 2, 1, 2>(grid, NWv, stream, act, (int)a_stride, I, codes, scl, H, E, ids,
+      launch_dc<kMx, 4, 1, 2>(grid, NWv, stream, act, (int)a_stride, I, codes, scl, H, E, ids,
                               topk, (int)P, tw, y);
     else
       launch_dc<kMx, 1, 2, 2>(grid, NWv, stream, act, (int)a_stride, I, codes, scl, H, E, ids,
