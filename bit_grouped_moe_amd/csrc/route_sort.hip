@@ -76,14 +76,15 @@ __device__ __forceinline__ int wave_total(int v) {
   return __builtin_amdgcn_readlane(v, kWave - 1);
 }
 
-__global__ __launch_bounds__(kSortThreads) void route_sort_kernel(
+// One workgroup's whole share of the sort.  kDropped selects the pairs it
+// compacts at compile time (expert b's, or the dropped ones for b = E), so
+// the match test in the loops is one compare with no branch.
+template <bool kDropped>
+__device__ __forceinline__ void sort_workgroup(
     const int32_t* __restrict__ ids, int32_t P, int32_t E, int32_t tile_m,
     int32_t* __restrict__ offsets, int32_t* __restrict__ sorted_pairs,
-    int32_t* __restrict__ tiles, int32_t max_tiles, int32_t* __restrict__ num_tiles) {
-  __shared__ int hist_c[kHistCounters + kWave];           // [E + 1][C] copies (row E: ids
-                                                          // outside [0, E)), 32 KB
-  __shared__ int hist[1024];
-  __shared__ int wcount[kSortWaves];
+    int32_t* __restrict__ tiles, int32_t max_tiles, int32_t* __restrict__ num_tiles,
+    int* __restrict__ hist_c, int* __restrict__ hist, int* __restrict__ wcount) {
   const int b = blockIdx.x;
   const int tid = threadIdx.x, lane = tid & (kWave - 1), wave = tid / kWave;
   const unsigned uE = (unsigned)E;
@@ -93,7 +94,7 @@ __global__ __launch_bounds__(kSortThreads) void route_sort_kernel(
   while (C > 1 && C * E > kHistCounters) C >>= 1;
   const int cl = lane & (C - 1);
 
-  auto hit = [&](int x) { return (b < E) ? (x == b) : (x != kPastEnd && (unsigned)x >= uE); };
+  auto hit = [&](int x) { return kDropped ? (x != kPastEnd && (unsigned)x >= uE) : (x == b); };
   for (int i = tid; i < C * (E + 1); i += kSortThreads) hist_c[i] = 0;
   int v[kPerLane];
   for (int ch = 0; ch < n_chunks; ++ch) {
@@ -143,7 +144,7 @@ __global__ __launch_bounds__(kSortThreads) void route_sort_kernel(
 
   // Stable compaction of this workgroup's pairs (see the file comment).  One
   // chunk: the ids are still in registers.
-  int cursor = (b < E) ? seg_start : valid_total;
+  int cursor = kDropped ? valid_total : seg_start;
   for (int ch = 0; ch < n_chunks; ++ch) {
     if (n_chunks > 1) load_ids(ids, P, (int64_t)ch * kChunkIds, v);
     if (ch > 0) {                      // chunk 0's counts came with the histogram
@@ -168,9 +169,10 @@ __global__ __launch_bounds__(kSortThreads) void route_sort_kernel(
     for (int j = 0; j < kPerLane; ++j) asm volatile("" : "+v"(v[j]));
 #pragma unroll
     for (int j = 0; j < kPerLane; ++j) {
-      const uint64_t m = __ballot(hit(v[j]));
+      const bool h = hit(v[j]);
+      const uint64_t m = __ballot(h);
       if (m == 0ull) continue;                             // uniform: most rows match nothing
-      if ((m >> lane) & 1ull) {
+      if (h) {
         const int rank = __builtin_amdgcn_mbcnt_hi((uint32_t)(m >> 32),
                                                    __builtin_amdgcn_mbcnt_lo((uint32_t)m, 0u));
         sorted_pairs[pos + rank] = (int)(pbase + j * kWave + lane);
@@ -181,7 +183,7 @@ __global__ __launch_bounds__(kSortThreads) void route_sort_kernel(
     if (ch + 1 < n_chunks) __syncthreads();               // wcount reused
   }
 
-  if (b < E) {
+  if (!kDropped) {
     if (tid == 0) offsets[b] = seg_start;
     const int nt = (hist[b] + tile_m - 1) / tile_m;
     for (int j = tid; j < nt; j += kSortThreads) {
@@ -198,6 +200,22 @@ __global__ __launch_bounds__(kSortThreads) void route_sort_kernel(
       tiles[2 * j + 1] = -1;
     }
   }
+}
+
+__global__ __launch_bounds__(kSortThreads) void route_sort_kernel(
+    const int32_t* __restrict__ ids, int32_t P, int32_t E, int32_t tile_m,
+    int32_t* __restrict__ offsets, int32_t* __restrict__ sorted_pairs,
+    int32_t* __restrict__ tiles, int32_t max_tiles, int32_t* __restrict__ num_tiles) {
+  __shared__ int hist_c[kHistCounters + kWave];           // [E + 1][C] copies (row E: ids
+                                                          // outside [0, E)), 32 KB
+  __shared__ int hist[1024];
+  __shared__ int wcount[kSortWaves];
+  if ((int)blockIdx.x < E)
+    sort_workgroup<false>(ids, P, E, tile_m, offsets, sorted_pairs, tiles, max_tiles, num_tiles,
+                          hist_c, hist, wcount);
+  else
+    sort_workgroup<true>(ids, P, E, tile_m, offsets, sorted_pairs, tiles, max_tiles, num_tiles,
+                         hist_c, hist, wcount);
 }
 
 }  // namespace gq
