@@ -156,33 +156,56 @@ __global__ __launch_bounds__(kGemvMaxThreads) void grouped_gemv_kernel(
 #pragma unroll
     for (int v = 0; v < 4; ++v) xr[v] = xp[v];
   }
-  if ((unsigned)e >= (unsigned)E) {          // dropped pair: its slice is zero
-    for (int r = tid; r < Rout; r += NT)
-      if (n0 + r < Nout) out[(int64_t)p0 * Nout + n0 + r] = 0;
-    return;
-  }
 
   // ---- round trip 2: the weight bytes of expert e ----
-  const size_t row_bytes = (size_t)K / 2;
-  u32x4 cw[kIter];
-  float am[kIter];
-  uint32_t sb[kIter];
+  // Everything but the expert's base address is formed while the id is in
+  // flight, so that once it arrives only the scalar base remains before the
+  // loads issue (offsets from a scalar base: the loads take the base in
+  // SGPRs).  Offsets inside one expert fit 32 bits (host check: an expert's
+  // codes are < 2^31 bytes); rows < 2^24 and row bytes <= 4096 allow 24-bit
+  // multiplies.  No branch on the id before the loads: with one, the
+  // compiler sinks every address computation and the activation loads below
+  // the id wait.  A dropped pair reads expert 0 and stores zeros.  Measured
+  // under graph replay against the form with a dropped-pair return and the
+  // addresses formed after the id: one-token gate_up 6.37-6.40 -> 6.09-6.13
+  // us, down 5.20-5.24 -> 4.99 us, M=4 gate_up 15.2-15.4 -> 14.9-15.0 us.
+  //
   // Unconditional loads from clamped addresses (rows past N and idle lanes
   // re-read valid bytes whose results are never stored): a conditional load
   // would zero its registers first and stall on every older load in flight.
   // The weight bytes are read once per launch: non-temporal loads (measured
   // ~2% faster on the one-token gate_up launch than default-policy loads).
-  const int s_cl = active ? s : 0;
+  const uint32_t row_bytes = (uint32_t)K / 2;
+  const uint32_t s_cl = active ? s : 0;
+  constexpr uint32_t kScaleBytes = kMx ? 1u : 4u;             // e8m0 byte / fp32 absmax
+  const uint32_t spr = kMx ? (uint32_t)(K / 32) : (uint32_t)(K / 64);   // scales per row
+  uint32_t woff[kIter], soff[kIter];
 #pragma unroll
   for (int i = 0; i < kIter; ++i) {
-    const size_t row = (size_t)e * N + wrow(g, i);
-    cw[i] = __builtin_nontemporal_load(
-        reinterpret_cast<const u32x4*>(codes + row * row_bytes + (size_t)s_cl * 16));
+    const uint32_t r = (uint32_t)wrow(g, i);
+    woff[i] = __umul24(r, row_bytes) + s_cl * 16u;
+    soff[i] = (__umul24(r, spr) + (kMx ? s_cl : s_cl / 2)) * kScaleBytes;
+    // opaque: otherwise refolded into multiply-adds with the base after the
+    // id has arrived
+    asm volatile("" : "+v"(woff[i]), "+v"(soff[i]));
+  }
+  size_t ebytes = (size_t)N * row_bytes, escl = (size_t)N * spr * kScaleBytes;
+  asm volatile("" : "+s"(ebytes), "+s"(escl));
+  const bool dropped = (unsigned)e >= (unsigned)E;             // uniform
+  const size_t ec = dropped ? 0 : (size_t)(uint32_t)e;
+  const uint8_t* cbase = codes + ec * ebytes;
+  const uint8_t* sbase = static_cast<const uint8_t*>(scl) + ec * escl;
+  u32x4 cw[kIter];
+  float am[kIter];
+  uint32_t sb[kIter];
+#pragma unroll
+  for (int i = 0; i < kIter; ++i) {
+    cw[i] = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(cbase + woff[i]));
     if constexpr (kMx) {
-      sb[i] = (uint32_t)static_cast<const uint8_t*>(scl)[row * (size_t)(K / 32) + s_cl];
+      sb[i] = (uint32_t)sbase[soff[i]];
       am[i] = 0.f;
     } else {
-      am[i] = static_cast<const float*>(scl)[row * (size_t)(K / 64) + s_cl / 2];
+      am[i] = *reinterpret_cast<const float*>(sbase + soff[i]);
       sb[i] = 0u;
     }
   }
@@ -293,11 +316,13 @@ __global__ __launch_bounds__(kGemvMaxThreads) void grouped_gemv_kernel(
 #pragma unroll
       for (int i = 0; i < (kGlu ? kHalf : kIter); ++i) {
         const int n = n0 + g + G * i;
-        if (s == W - 1 && n < Nout) out[(int64_t)p * Nout + n] = f32_to_bf16_bits(vals[i] * sc);
+        if (s == W - 1 && n < Nout)
+          out[(int64_t)p * Nout + n] = f32_to_bf16_bits(dropped ? 0.f : vals[i] * sc);
       }
     } else {
       const int n = n0 + tid;
-      if (tid < Rout && n < Nout) out[(int64_t)p * Nout + n] = f32_to_bf16_bits(vals[0] * sc);
+      if (tid < Rout && n < Nout)
+        out[(int64_t)p * Nout + n] = f32_to_bf16_bits(dropped ? 0.f : vals[0] * sc);
     }
   };
 
@@ -312,7 +337,7 @@ __global__ __launch_bounds__(kGemvMaxThreads) void grouped_gemv_kernel(
 #pragma unroll
   for (int c = 0; c < kGemvMaxPairs / kWave; ++c) {
     const int q = lane + kWave * c;
-    match[c] = __ballot(idl[c] == e);
+    match[c] = __ballot(idl[c] == e && q < P);   // q < P: the padding (-1) may equal e
     dup |= __ballot(idl[c] == e && q < p0) != 0ull;
   }
   if (dup) return;                           // an earlier pair's workgroup serves p0
@@ -329,7 +354,7 @@ __global__ __launch_bounds__(kGemvMaxThreads) void grouped_gemv_kernel(
                                                         (active ? s : 0) * 32);
 #pragma unroll
       for (int v = 0; v < 4; ++v) xr[v] = xp[v];
-      compute_pair();
+      if (!dropped) compute_pair();          // a dropped pair stores zeros
       store_pair(p);
     }
   }
@@ -383,6 +408,7 @@ static int launch_gemv(const uint16_t* x, int32_t rows, int32_t K, int64_t x_str
   if (pair_scale && !aligned4(pair_scale)) return kInvalid;
   const int64_t P = (int64_t)rows * topk;
   if (P > kGemvMaxPairs || K > kGemvMaxK || N >= (1 << 24)) return kNotSupported;
+  if ((int64_t)N * (K / 2) >= ((int64_t)1 << 31)) return kNotSupported;   // 32-bit offsets
   if (x_stride > INT32_MAX) return kNotSupported;
   int S, W, G, NT;
   segment_layout(K, S, W, G, NT);

@@ -144,7 +144,9 @@ int gq_mxfp4_decode(const uint8_t* blocks, const uint8_t* scales, int64_t n_rows
  * InvalidValue: null pointer (pair_scale may be NULL), rows < 1,
  *   topk < 1, E < 1, N < 1, K not a positive multiple of 64 (NF4) / 32
  *   (MXFP4), bad stride or alignment.
- * NotSupported: rows*topk > 256, K > 8192, N >= 2^24, x_stride > 2^31 - 1.
+ * A pair whose id lies outside [0, E) is dropped: its output row is zero.
+ * NotSupported: rows*topk > 256, K > 8192, N >= 2^24, N*K/2 >= 2^31 (one
+ *   expert's codes), x_stride > 2^31 - 1.
  */
 int gq_nf4_grouped_gemv(const uint16_t* x, int32_t rows, int32_t K, int64_t x_stride,
                         const uint8_t* codes, const float* absmax, int32_t num_experts,

@@ -10,7 +10,7 @@ import torch
 import bit_grouped_moe_amd as gq
 import oracle
 import workloads as wl
-from tests.gpu_common import (LazyDecoded, plus_zero,
+from tests.gpu_common import (LazyDecoded, plus_zero, assert_rows,
                               assert_slices, bf16_bits, bf16_to_host_f32, device,
                               packed_mx_bank, packed_nf4_bank, say, to_dev, to_dev_bf16)
 
@@ -88,6 +88,43 @@ def test_shared_experts_dropped_and_flatten(fmt):
     out = _run(fmt, xp, bank, fl, dev)
     ref = oracle.grouped_gemm(xp, W, fl, E)
     assert_slices(bf16_to_host_f32(out), ref, fl, E)
+
+
+@pytest.mark.parametrize("fmt", ["nf4", "mx"])
+@pytest.mark.parametrize("case", ["some", "all"])
+def test_dropped_pairs_write_only_their_rows(fmt, case):
+    """Dropped ids (-1, which is also the kernel's padding of the routing
+    table past the last pair, E, INT32_MAX, -7) give exact zero rows, and no
+    store lands outside the [P, N] output: the output sits between two guard
+    bands of a sentinel, checked untouched.  Few pairs, so most lanes of the
+    routing table are padding."""
+    dev = device()
+    g = np.random.default_rng(29 if case == "some" else 31)
+    E, N, K = 5, 160, 256
+    bank = packed_nf4_bank(g, E, N, K) if fmt == "nf4" else packed_mx_bank(g, E, N, K)
+    W = LazyDecoded(fmt, *bank)
+    if case == "some":
+        ids = np.array([[2, -1], [-1, 4], [E, 2], [2**31 - 1, -7]], np.int32)
+    else:
+        ids = np.full((3, 2), -1, np.int32)
+    rows, topk = ids.shape
+    P, G = rows * topk, 4096
+    x = wl.draw_bf16(g, (rows, K))
+    sentinel = 0x7A5B
+    buf = torch.full((P * N + 2 * G,), sentinel, dtype=torch.int16, device=dev)
+    out = buf[G:G + P * N].view(torch.bfloat16).view(P, N)
+    fn = gq.gq_nf4_grouped_gemv if fmt == "nf4" else gq.gq_mxfp4_grouped_gemv
+    say("gemv dropped guard", fmt, case)
+    fn(to_dev_bf16(x, dev), to_dev(bank[0], dev), to_dev(bank[1], dev), to_dev(ids, dev),
+       out=out)
+    torch.cuda.synchronize()
+    b = buf.cpu().numpy()
+    assert np.all(b[:G] == sentinel) and np.all(b[G + P * N:] == sentinel)
+    got = bf16_to_host_f32(out)
+    ref = oracle.grouped_gemm(x, W, ids, E)
+    assert_rows(got, ref, what="dropped rows zero, kept rows")
+    dropped = ((ids < 0) | (ids >= E)).reshape(-1)
+    assert np.all(bf16_bits(out)[dropped] == 0)        # +0.0, not -0.0
 
 
 @pytest.mark.parametrize("fmt", ["nf4", "mx"])
