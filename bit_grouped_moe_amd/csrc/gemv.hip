@@ -19,8 +19,9 @@
 //    (fully coalesced).
 //  * NF4: codebook lookups from a 16-entry LDS table (conflict-free), the
 //    64-block absmax factored out of each 32-weight partial sum; MXFP4: the
-//    gfx950 e2m1 converter, the e8m0 factor applied to the partial sum with
-//    ldexp.  Both keep the decoded weight exact (float32).
+//    gfx950 e2m1 converter to bf16 pairs and bf16-pair dot products, the
+//    e8m0 factor applied to the partial sum with ldexp.  Both keep the
+//    decoded weight and its products exact (float32 sums).
 //  * partial sums are reduced in a fixed order (DPP lane moves inside a wave,
 //    LDS across waves): no atomics, bitwise reproducible.
 #include <algorithm>
@@ -35,10 +36,18 @@ constexpr int kGemvMaxThreads = 256;
 constexpr int kGemvMaxPairs = 256;
 constexpr int kGemvMaxK = 8192;     // 256 segments of 32 weights
 
-// Partial dot product of one 32-weight segment with the activation slice.
+// Partial dot product of one 32-weight segment with the activation slice
+// (xf: as float32; xr: the raw bf16 pairs).  NF4: codebook values (float32)
+// against xf.  MXFP4: the converter turns each code byte into its two
+// weights as a bf16 pair (exact: every e2m1 value is a bf16 value) and
+// v_dot2_f32_bf16 multiplies it with the matching activation pair (the
+// products are exact in float32; two per instruction, float32 sums): 25%
+// fewer VALU instructions than float32 FMAs on converted weights, and no
+// activation conversion; one-token gpt-oss gate_up 9.99 -> 9.70 us, down
+// 7.34 -> 7.01 us (graph-replayed, same-box A/B).
 template <bool kMx>
 __device__ __forceinline__ float segment_dot(const float* lut, u32x4 c, float am, uint32_t sb,
-                                             const float (&xf)[32]) {
+                                             const float (&xf)[32], const u32x4 (&xr)[4]) {
   float acc = 0.f;
 #pragma unroll
   for (int w = 0; w < 4; ++w) {
@@ -50,9 +59,11 @@ __device__ __forceinline__ float segment_dot(const float* lut, u32x4 c, float am
     if constexpr (kMx) {
 #pragma unroll
       for (int b = 0; b < 4; ++b) {
-        const f32x2 v = e2m1_pair_f32(d, b);        // element 2j: low nibble
-        acc = __builtin_fmaf(v.x, xf[8 * w + 2 * b], acc);
-        acc = __builtin_fmaf(v.y, xf[8 * w + 2 * b + 1], acc);
+        const uint32_t wv = e2m1_pair_bf16_scaled(d, b, 1.0f);   // element 2j: low half
+        // a scalar copy first: a bit_cast of a vector element reads element 0
+        const uint32_t xv = xr[w][b];
+        acc = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, wv),
+                                              __builtin_bit_cast(bf16x2, xv), acc, false);
       }
     } else {
       float q[8];
@@ -239,7 +250,7 @@ __global__ __launch_bounds__(kGemvMaxThreads) void grouped_gemv_kernel(
     if constexpr (kWaveRows) {
 #pragma unroll
       for (int i = 0; i < kIter; ++i) {
-        const float part = active ? segment_dot<kMx>(lut, cw[i], am[i], sb[i], xf) : 0.f;
+        const float part = active ? segment_dot<kMx>(lut, cw[i], am[i], sb[i], xf, xr) : 0.f;
         vals[i] = group_sum_last(part, W);                     // total on lane s == W-1
       }
       if constexpr (kGlu) {
@@ -250,7 +261,7 @@ __global__ __launch_bounds__(kGemvMaxThreads) void grouped_gemv_kernel(
       constexpr int kStride = kGemvMaxThreads + 32;            // pad: spreads banks
 #pragma unroll
       for (int i = 0; i < kIter; ++i)
-        red[i * kStride + tid] = active ? segment_dot<kMx>(lut, cw[i], am[i], sb[i], xf) : 0.f;
+        red[i * kStride + tid] = active ? segment_dot<kMx>(lut, cw[i], am[i], sb[i], xf, xr) : 0.f;
       lds_barrier();
       vals[0] = 0.f;
       bool unit_done = false;                // the gated unit already applied (uniform)
@@ -551,7 +562,8 @@ __global__ __launch_bounds__(kWave * kCombineMaxWaves) void gemv_down_combine_ke
         }
 #pragma unroll
       for (int i = 0; i < kR; ++i)
-        if (active[j]) part[i] += segment_dot<kMx>(lut, cw[q][i][j], am[q][i][j], sb[q][i][j], xf);
+        if (active[j])
+          part[i] += segment_dot<kMx>(lut, cw[q][i][j], am[q][i][j], sb[q][i][j], xf, xr[q][j]);
     }
     const int p = wave + NWv * q;
 #pragma unroll

@@ -137,7 +137,8 @@ int gq_mxfp4_decode(const uint8_t* blocks, const uint8_t* scales, int64_t n_rows
  * it; no sort is needed (the kernel reads topk_ids directly).  Arithmetic,
  * float32 throughout with no bf16 rounding of the weights: each group of 32
  * consecutive k is summed as sum(codebook_value * x) (NF4) or
- * sum(e2m1_value * x) (MXFP4), then multiplied once by the group's factor
+ * sum(e2m1_value * x) (MXFP4; exact products, two per bf16-pair dot
+ * instruction, float32 sums), then multiplied once by the group's factor
  * (the NF4 absmax of its 64-block; the MXFP4 2^(s-127), exact); the group
  * partials are added in a fixed order.  A one-hot x therefore returns
  * bf16(float32(value * factor)), the decoded weight, bit for bit.
