@@ -193,6 +193,17 @@ struct DgCodes {
   uint32_t two[4];   // bytes j4*2, j4*2+1 of rows r8*8 + 2i (low half) and + 2i+1 (high half)
 };
 
+// The dgrad B tile stores column col at LDS row dg_brow(col), a permutation
+// inside each group of four rows.  The decode writes columns 4 apart in one
+// instruction (a thread owns a column quad) and the MFMA operand reads take 32
+// consecutive columns; with 72-element rows the plain order put four lanes of
+// every 16-byte write group on the same banks.  XOR-ing the row's low two
+// bits with bit 4 and with bits 3 ^ 5 keeps both access groups on distinct
+// banks (checked for 64 banks x 16 lanes and 32 banks x 8 lanes per cycle).
+__device__ __forceinline__ int dg_brow(int col) {
+  return col ^ ((col >> 4) & 1) ^ ((((col >> 3) ^ (col >> 5)) & 1) << 1);
+}
+
 template <int kMode>
 __device__ __forceinline__ void dg_read_codes(const uint8_t* Cs, const float* As, int tid,
                                               DgCodes& R) {
@@ -223,9 +234,10 @@ __device__ __forceinline__ void dg_decode_pair(const DgCodes& R, const float* As
     ce[h] = __builtin_amdgcn_perm(r1, r0, 0x05040100u);     // low halves: even column
     co[h] = __builtin_amdgcn_perm(r1, r0, 0x07060302u);     // high halves: odd column
   }
-  uint16_t* col = Bs + (j4 * 4 + 2 * cp) * kBStride + r8 * 8;
-  *reinterpret_cast<u32x4*>(col) = u32x4{ce[0], ce[1], ce[2], ce[3]};
-  *reinterpret_cast<u32x4*>(col + kBStride) = u32x4{co[0], co[1], co[2], co[3]};
+  const int c0 = j4 * 4 + 2 * cp;
+  *reinterpret_cast<u32x4*>(Bs + dg_brow(c0) * kBStride + r8 * 8) = u32x4{ce[0], ce[1], ce[2], ce[3]};
+  *reinterpret_cast<u32x4*>(Bs + dg_brow(c0 + 1) * kBStride + r8 * 8) =
+      u32x4{co[0], co[1], co[2], co[3]};
 }
 
 // NF4: columns 2*part and 2*part + 1 of the quad per call (part 0, 1: the
@@ -252,7 +264,7 @@ __device__ __forceinline__ void dg_decode_nf4(const DgCodes& R, const float* As,
   }
 #pragma unroll
   for (int k = 0; k < 2; ++k)
-    *reinterpret_cast<u32x4*>(Bs + (j4 * 4 + 2 * part + k) * kBStride + r8 * 8) =
+    *reinterpret_cast<u32x4*>(Bs + dg_brow(j4 * 4 + 2 * part + k) * kBStride + r8 * 8) =
         u32x4{c[k][0], c[k][1], c[k][2], c[k][3]};
 }
 
@@ -451,9 +463,11 @@ __device__ __forceinline__ void grouped_gemm_body(const GemmArgs& g) {
   };
   auto load_b_slice = [&](const uint16_t* B, int sl, bf16x8 (&b)[4]) {
 #pragma unroll
-    for (int c = 0; c < 4; ++c)
+    for (int c = 0; c < 4; ++c) {
+      const int row = kDg ? dg_brow(c * 32 + lr) : c * 32 + lr;
       b[c] = as_bf16x8(
-          *reinterpret_cast<const u32x4*>(B + (c * 32 + lr) * kBStride + lh * 32 + sl * 8));
+          *reinterpret_cast<const u32x4*>(B + row * kBStride + lh * 32 + sl * 8));
+    }
   };
   // kRows = number of active 32-row sub-tiles of this wave (1 or 2) with all
   // 128 columns valid: unguarded MFMAs.  kRows == 0: generic guarded path.
