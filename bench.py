@@ -680,6 +680,90 @@ def prefill(dev, steps, warmup, fmt):
     }
 
 
+def dequant_baseline(dev, steps, warmup):
+    """The pages' comparator, dequantize-then-GEMM (bit_grouped_moe_amd.dequant_baseline):
+    the Qwen3 NF4 decode step (M=1: gate_up + down, own routing, cold bank
+    copy per step, graph-replayed) and the Qwen3 NF4 prefill step (M=4096
+    Zipf top-8: gate_up + down, one captured step replayed), each the same
+    workload as the fused legs; the routing is grouped on the host outside
+    the timed region."""
+    from bit_grouped_moe_amd.dequant_baseline import DequantGemm
+    E, topk = wl.QWEN["E"], wl.QWEN["topk"]
+    (Ng, Kg), (Nd, Kd) = wl.QWEN["gate_up"], wl.QWEN["down"]
+    res = {}
+    # ---- decode M=1 (same banks, routing and inputs as decode_nf4) ----
+    banks_g = [wl.random_nf4_bank(E, Ng, Kg, dev, seed=10 + c) for c in range(COPIES)]
+    banks_d = [wl.random_nf4_bank(E, Nd, Kd, dev, seed=100 + c) for c in range(COPIES)]
+    g = wl.rng(wl.CFG_QWEN_DECODE, wl.S_ROUTE)
+    ids = [wl.route_uniform(g, 1, E, topk) for _ in range(steps + warmup)]
+    x = bf16_dev(wl.draw_bf16(wl.rng(wl.CFG_QWEN_DECODE, wl.S_X), (1, Kg)), dev)
+    xd = bf16_dev(wl.draw_bf16(wl.rng(wl.CFG_QWEN_DECODE, wl.S_DOWN_IN), (topk, Kd)), dev)
+    wg = torch.empty((topk, Ng, Kg), dtype=torch.bfloat16, device=dev)
+    wd = torch.empty((topk, Nd, Kd), dtype=torch.bfloat16, device=dev)
+    dg = [DequantGemm(c, a, wbuf=wg) for c, a in banks_g]
+    dd = [DequantGemm(c, a, wbuf=wd) for c, a in banks_d]
+    plans = [(dg[0].plan(i, gather=True), dd[0].plan(i.reshape(-1, 1), gather=False))
+             for i in ids]
+    out_g = torch.empty((topk, Ng), dtype=torch.bfloat16, device=dev)
+    out_d = torch.empty((topk, Nd), dtype=torch.bfloat16, device=dev)
+
+    def step(i):
+        pg, pd = plans[i]
+        dg[i % COPIES].run(x, pg, out_g)
+        dd[i % COPIES].run(xd, pd, out_d)
+
+    for i in range(steps, steps + warmup):
+        step(i)
+    gr = capture(step, steps)
+    gr.replay()
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    gr.replay()
+    torch.cuda.synchronize()
+    res["decode_m1_ms_per_step"] = 1e3 * (time.perf_counter() - t0) / steps
+    del gr, banks_g, banks_d, dg, dd, wg, wd
+    torch.cuda.empty_cache()
+    # ---- prefill M=4096 Zipf (same banks, routing and inputs as prefill("nf4")) ----
+    cfg, M = wl.CFG_QWEN_PREFILL, 4096
+    P = M * topk
+    route = wl.route_zipf(wl.rng(cfg, wl.S_ROUTE), M, E, topk)
+    cg, ag = wl.random_nf4_bank(E, Ng, Kg, dev, seed=30)
+    cd, ad = wl.random_nf4_bank(E, Nd, Kd, dev, seed=300)
+    x = bf16_dev(wl.draw_bf16(wl.rng(cfg, wl.S_X), (M, Kg)), dev)
+    xd = bf16_dev(wl.draw_bf16(wl.rng(cfg, wl.S_DOWN_IN), (P, Kd)), dev)
+    pg_ = DequantGemm(cg, ag)
+    pd_ = DequantGemm(cd, ad)
+    plan_g = pg_.plan(route, gather=True)
+    plan_d = pd_.plan(route.reshape(-1, 1), gather=False)
+    out_g = torch.empty((P, Ng), dtype=torch.bfloat16, device=dev)
+    out_d = torch.empty((P, Nd), dtype=torch.bfloat16, device=dev)
+
+    def pstep(_):
+        pg_.run(x, plan_g, out_g)
+        pd_.run(xd, plan_d, out_d)
+
+    def dec_only(_):
+        pg_.decode(plan_g)
+        pd_.decode(plan_d)
+
+    for _ in range(3):
+        pstep(0)
+    reps = max(3, min(steps, 10))
+    gp = capture(pstep, 1)
+    gd = capture(dec_only, 1)
+    gp.replay()
+    gd.replay()
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for _ in range(reps):
+        gp.replay()
+    torch.cuda.synchronize()
+    res["prefill_m4096_ms_per_step"] = 1e3 * (time.perf_counter() - t0) / reps
+    res["prefill_m4096_dequant_ms"] = event_ms(gd.replay)
+    res["prefill_m4096_bf16_copy_bytes"] = E * (Ng * Kg + Nd * Kd) * 2
+    return res
+
+
 def prefill_mx_scaled(dev, steps, warmup):
     """gpt-oss MXFP4 prefill (M=2048 uniform top-4) on the block-scaled fp4
     matrix instruction: route sort + activation split + gate_up GEMM +
@@ -891,7 +975,7 @@ def r4(d):
 
 LEGS = ("decode", "decode_m4", "mx_decode", "controls", "prefill", "mx_prefill",
         "mx_prefill_scaled", "layer_decode", "layer_prefill", "mx_layer_decode",
-        "mx_layer_prefill", "host_stream", "dgrad", "mx_dgrad", "mfma")
+        "mx_layer_prefill", "host_stream", "dequant", "dgrad", "mx_dgrad", "mfma")
 
 
 def run_legs(dev, args, legs):
@@ -924,6 +1008,8 @@ def run_legs(dev, args, legs):
             out[leg] = prefill_layer_mx(dev, ps, pw)
         elif leg == "host_stream":
             out[leg] = host_stream(dev, min(st, 50), min(wu, 5))
+        elif leg == "dequant":
+            out[leg] = dequant_baseline(dev, st, wu)
         elif leg == "dgrad":
             out[leg] = dgrad(dev, ps, pw)
         elif leg == "mx_dgrad":
@@ -1023,6 +1109,15 @@ def main():
         log("[bench] nf4 decode from pinned host memory")
         extra["nf4_decode_m1_host_streamed"] = host_stream(dev, min(args.steps, 50),
                                                            min(args.warmup, 5))
+        log("[bench] dequantize-then-GEMM comparator")
+        dq = dequant_baseline(dev, args.steps, args.warmup)
+        dq["workload"] = ("qwen3-30b-a3b nf4, dequantize-then-GEMM (decode to a bf16 copy, then "
+                          "hipBLASLt per expert): decode M=1 and prefill M=4096 Zipf, the same "
+                          "workloads as the headline and prefill legs")
+        dq["fused_speedup_decode_m1"] = dq["decode_m1_ms_per_step"] / dec["ms_per_step"]
+        dq["fused_speedup_prefill_m4096"] = dq["prefill_m4096_ms_per_step"] / pre["ms_per_step"]
+        extra["dequant_then_gemm"] = dq
+        log("[bench]", r4(dq))
         log("[bench] nf4 dgrad")
         extra["nf4_dgrad_m2048"] = dgrad(dev, args.prefill_steps, args.prefill_warmup)
         log("[bench] mxfp4 dgrad")
