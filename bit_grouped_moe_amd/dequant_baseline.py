@@ -27,9 +27,9 @@ class DequantGemm:
     ``plan(ids, gather)`` groups the pairs of ``ids`` int32 [rows, topk]
     (numpy) by expert; ``run(x, groups, out)`` decodes every planned expert
     into the bf16 buffer and multiplies x's rows by it (gather: pair p reads
-    row p // topk of x; otherwise row p), writing out [rows*topk, N].  Pairs whose id lies outside [0, E)
-    are left zero.  Every launch goes to torch's current stream, so a step
-    can be captured in a graph."""
+    row p // topk of x; otherwise row p), writing out [rows*topk, N].
+    Pairs whose id lies outside [0, E) are left zero.  Every launch goes to
+    torch's current stream, so a step can be captured in a graph."""
 
     def __init__(self, codes, absmax, max_experts=None, wbuf=None):
         self.codes, self.absmax = codes, absmax
