@@ -17,8 +17,9 @@
 //    float registers; several rows per thread, all loads issued up front.
 //    Consecutive threads read consecutive 16-byte pieces of contiguous rows
 //    (fully coalesced).
-//  * NF4: codebook lookups from a 16-entry LDS table (conflict-free), the
-//    64-block absmax factored out of each 32-weight partial sum; MXFP4: the
+//  * NF4: codebook value pairs from a 256-entry LDS table indexed by the
+//    code byte, the 64-block absmax factored out of each 32-weight partial
+//    sum; MXFP4: the
 //    gfx950 e2m1 converter to bf16 pairs and bf16-pair dot products, the
 //    e8m0 factor applied to the partial sum with ldexp.  Both keep the
 //    decoded weight and its products exact (float32 sums).
@@ -45,8 +46,22 @@ constexpr int kGemvMaxK = 8192;     // 256 segments of 32 weights
 // fewer VALU instructions than float32 FMAs on converted weights, and no
 // activation conversion; one-token gpt-oss gate_up 9.99 -> 9.70 us, down
 // 7.34 -> 7.01 us (graph-replayed, same-box A/B).
+//
+// NF4 values come from a 256-entry table of codebook value pairs indexed by
+// the code byte (one 8-byte LDS read per two weights, the table at LDS
+// address 0 so its byte offset is one shift).  Against the 16-entry table
+// (one 4-byte read per weight) this halves the LDS reads at the end of each
+// workgroup, where the decode follows the last weight bytes; same-box A/B
+// over three alternations, graph-replayed: one-token gate_up 6.05-6.08 ->
+// 5.92-5.97 us, down 4.97-5.05 -> 4.78-4.81 us, decode step 11.1 -> 10.7-10.8
+// us, M = 4 down 10.8 -> 10.4 us.
+using LutT = f32x2;
+constexpr int kLutN = 256;
+__device__ __forceinline__ void lut_init(LutT* lut, int tid, int nt) {
+  for (int t = tid; t < kLutN; t += nt) nf4_pairs_init(lut, t);
+}
 template <bool kMx>
-__device__ __forceinline__ float segment_dot(const float* lut, u32x4 c, float am, uint32_t sb,
+__device__ __forceinline__ float segment_dot(const LutT* lut, u32x4 c, float am, uint32_t sb,
                                              const float (&xf)[32], const u32x4 (&xr)[4]) {
   float acc = 0.f;
 #pragma unroll
@@ -67,7 +82,7 @@ __device__ __forceinline__ float segment_dot(const float* lut, u32x4 c, float am
       }
     } else {
       float q[8];
-      nf4_lookup8(lut, d, q);                       // element 2j: high nibble
+      nf4_pairs8(lut, d, q);                        // element 2j: high nibble
 #pragma unroll
       for (int j = 0; j < 8; ++j) acc = __builtin_fmaf(q[j], xf[8 * w + j], acc);
     }
@@ -104,7 +119,7 @@ __global__ __launch_bounds__(kGemvMaxThreads) void grouped_gemv_kernel(
     int x_stride, int topk, int P, const float* __restrict__ pair_scale,
     uint16_t* __restrict__ out, float alpha, float limit) {
   constexpr bool kGlu = kAct != 0;
-  __shared__ float lut[16];
+  __shared__ __attribute__((aligned(4096))) LutT lut[kLutN];
   __shared__ float red[kWaveRows ? 1 : kIter * (kGemvMaxThreads + 32)];
 
   // segment layout (the host's segment_layout, derived from K)
@@ -222,7 +237,7 @@ __global__ __launch_bounds__(kGemvMaxThreads) void grouped_gemv_kernel(
   }
 
   if constexpr (!kMx) {
-    nf4_lut_init(lut, tid);
+    lut_init(lut, tid, blockDim.x);
     lds_barrier();
   }
 
@@ -474,7 +489,7 @@ __global__ __launch_bounds__(kWave * kCombineMaxWaves) void gemv_down_combine_ke
     const int32_t* __restrict__ ids, const uint16_t* __restrict__ act,
     const uint8_t* __restrict__ codes, const void* __restrict__ scl, int I, int H, int E,
     int a_stride, int topk, int P, const float* __restrict__ tw, uint16_t* __restrict__ y) {
-  __shared__ float lut[16];
+  __shared__ __attribute__((aligned(4096))) LutT lut[kLutN];
   __shared__ float ys[kCombineMaxYs];                      // [P][Rb]
   __shared__ float tws[kCombineMaxPairs];                  // router weights
 
@@ -547,7 +562,7 @@ __global__ __launch_bounds__(kWave * kCombineMaxWaves) void gemv_down_combine_ke
     }
   }
   if constexpr (!kMx) {
-    nf4_lut_init(lut, tid);
+    lut_init(lut, tid, blockDim.x);
     lds_barrier();
   }
 #pragma unroll
