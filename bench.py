@@ -147,7 +147,9 @@ def decode_nf4(dev, steps, warmup, M=1):
     g = wl.rng(wl.CFG_QWEN_DECODE, wl.S_ROUTE)
     ids = [wl.route_uniform(g, M, E, topk) for _ in range(steps + warmup)]
     ids_g = [torch.from_numpy(i).to(dev) for i in ids]
-    ids_d = [torch.from_numpy(i.reshape(-1, 1).copy()).to(dev) for i in ids]
+    # the down product reads the same routing tensor, flattened (a view), as
+    # in a real layer where both projections consume one router output
+    ids_d = [t.view(-1, 1) for t in ids_g]
     x = bf16_dev(wl.draw_bf16(wl.rng(wl.CFG_QWEN_DECODE, wl.S_X), (M, Kg)), dev)
     xd = bf16_dev(wl.draw_bf16(wl.rng(wl.CFG_QWEN_DECODE, wl.S_DOWN_IN), (M * topk, Kd)), dev)
     out_g = torch.empty((M * topk, Ng), dtype=torch.bfloat16, device=dev)
@@ -322,7 +324,9 @@ def decode_mx(dev, steps, warmup):
     g = wl.rng(wl.CFG_GPTOSS, wl.S_ROUTE)
     ids = [wl.route_uniform(g, 1, E, topk) for _ in range(steps + warmup)]
     ids_g = [torch.from_numpy(i).to(dev) for i in ids]
-    ids_d = [torch.from_numpy(i.reshape(-1, 1).copy()).to(dev) for i in ids]
+    # the down product reads the same routing tensor, flattened (a view), as
+    # in a real layer where both projections consume one router output
+    ids_d = [t.view(-1, 1) for t in ids_g]
     x = bf16_dev(wl.draw_bf16(wl.rng(wl.CFG_GPTOSS, wl.S_X), (1, Kg)), dev)
     xd = bf16_dev(wl.draw_bf16(wl.rng(wl.CFG_GPTOSS, wl.S_DOWN_IN), (topk, Kd)), dev)
     out_g = torch.empty((topk, Ng), dtype=torch.bfloat16, device=dev)
@@ -555,7 +559,9 @@ def host_stream(dev, steps, warmup, M=1):
     g = wl.rng(wl.CFG_QWEN_DECODE, 82)
     ids = [wl.route_uniform(g, M, E, topk) for _ in range(steps + warmup)]
     ids_g = [torch.from_numpy(i).to(dev) for i in ids]
-    ids_d = [torch.from_numpy(i.reshape(-1, 1).copy()).to(dev) for i in ids]
+    # the down product reads the same routing tensor, flattened (a view), as
+    # in a real layer where both projections consume one router output
+    ids_d = [t.view(-1, 1) for t in ids_g]
     x = bf16_dev(wl.draw_bf16(wl.rng(wl.CFG_QWEN_DECODE, 83), (M, Kg)), dev)
     xd = bf16_dev(wl.draw_bf16(wl.rng(wl.CFG_QWEN_DECODE, 84), (M * topk, Kd)), dev)
     out_g = torch.empty((M * topk, Ng), dtype=torch.bfloat16, device=dev)
